@@ -1,0 +1,143 @@
+"""Pins for the oracle's routing (readings R-score, R-cand, R-group, R-topk).
+
+Checked against: the linearity identity (a summary score equals the mean raw
+logit over the chunk's tokens, computed without ever forming a summary),
+exhaustive k-subset enumeration on tiny inputs, and the planted-chunk recall
+that the planted workload is built to guarantee.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import hga_inputs as hi
+from oracle import hga_oracle as ora
+
+
+def _summaries(w):
+    B, H, T, d = w.k_cache.shape
+    gs = np.zeros((B, H, T // 8, d), np.float32)
+    cs = np.zeros((B, H, T // 64, d), np.float32)
+    ora.build_summaries(w.k_cache, 0, w.t_hist + w.seg_len, w.dtype, gs, cs)
+    return gs, cs
+
+
+def test_chunk_scores_equal_mean_logit_over_chunk_tokens():
+    w = hi.random_layer(seed=5, batch=1, n_q_heads=4, n_kv_heads=2, head_dim=32, t_hist=512,
+                        seg_len=256, top_chunks=3, top_groups=10, dtype="f32")
+    gs, cs = _summaries(w)
+    G = w.group_size
+    for kvh in range(2):
+        for j in range(4):
+            J = w.t_hist // 64 + j
+            rows = ora.block_rows(w.q, 0, kvh, j, G)
+            sig = ora.block_scores(rows, cs[0, kvh, :J])
+            kk = w.k_cache[0, kvh].astype(np.float64)
+            brute = np.array([max(float(np.mean(kk[64 * c:64 * c + 64] @ r)) for r in rows) for c in range(J)])
+            assert np.max(np.abs(sig - brute)) <= 1e-5 * (1 + np.max(np.abs(brute)))
+            gsig = ora.block_scores(rows, gs[0, kvh, :8 * J])
+            gbrute = np.array([max(float(np.mean(kk[8 * g:8 * g + 8] @ r)) for r in rows) for g in range(8 * J)])
+            assert np.max(np.abs(gsig - gbrute)) <= 1e-5 * (1 + np.max(np.abs(gbrute)))
+
+
+def _brute_topk(scores, ids, k):
+    """The unique k-subset whose members all beat all non-members under
+    (score desc, id asc), found by enumerating every subset."""
+    k = min(k, len(ids))
+    found = []
+    for sub in itertools.combinations(range(len(ids)), k):
+        inside = set(sub)
+        ok = all((scores[x] > scores[y]) or (scores[x] == scores[y] and ids[x] < ids[y])
+                 for x in inside for y in range(len(ids)) if y not in inside)
+        if ok:
+            found.append(sorted(ids[x] for x in sub))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_select_topk_matches_exhaustive_enumeration(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 9))
+    k = int(rng.integers(0, 5))
+    # quantised scores so that ties happen often
+    scores = rng.integers(-3, 4, size=n).astype(np.float32) * np.float32(0.5)
+    ids = sorted(rng.choice(100, size=n, replace=False).tolist())
+    assert ora.select_topk(scores, ids, k) == _brute_topk(scores, ids, k)
+
+
+def test_route_unit_matches_exhaustive_scoring_on_tiny_layer():
+    # the 1,024-token fp32 layer (one head, head_dim 64, top-4 chunks then top-8 groups)
+    w = hi.tiny_f32()
+    gs, cs = _summaries(w)
+    cidx, gidx, _ = ora.route(w.q, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, 1)
+    for j in range(w.seg_len // 64):
+        rows = ora.block_rows(w.q, 0, 0, j, 1)
+        J = j
+        full = np.array([max(float(r @ cs[0, 0, c].astype(np.float64)) for r in rows) for c in range(J)],
+                        np.float64).astype(np.float32)
+        # exhaustive: sort every candidate chunk
+        order = sorted(range(J), key=lambda c: (-full[c], c))[:4]
+        want_c = sorted(order)
+        got_c = [int(x) for x in cidx[0, 0, j] if x >= 0]
+        assert got_c == want_c
+        assert all(x == -1 for x in cidx[0, 0, j][len(want_c):])
+        cand = [8 * c + u for c in want_c for u in range(8)]
+        gsc = np.array([max(float(r @ gs[0, 0, g].astype(np.float64)) for r in rows) for g in cand],
+                       np.float64).astype(np.float32)
+        want_g = sorted(cand[i] for i in sorted(range(len(cand)), key=lambda i: (-gsc[i], cand[i]))[:8])
+        got_g = [int(x) for x in gidx[0, 0, j] if x >= 0]
+        assert got_g == want_g
+        # every selected group lies in a selected chunk, every selected chunk precedes block j
+        assert all(g // 8 in want_c for g in got_g)
+        assert all(c < J for c in got_c)
+
+
+def test_route_brute_force_subsets_small_budget():
+    w = hi.random_layer(seed=9, batch=1, n_q_heads=2, n_kv_heads=1, head_dim=16, t_hist=256,
+                        seg_len=192, top_chunks=3, top_groups=5, dtype="bf16")
+    gs, cs = _summaries(w)
+    for j in range(3):
+        c_sel, g_sel, sig, gids, tau = ora.route_unit(w.q, cs, gs, w.t_hist, 0, 0, j, 3, 5, 2)
+        assert c_sel == _brute_topk(sig, list(range(len(sig))), 3)
+        assert g_sel == _brute_topk(tau, gids, 5)
+
+
+def test_fewer_candidates_than_budget_and_empty_history():
+    w = hi.random_layer(seed=3, batch=1, n_q_heads=1, n_kv_heads=1, head_dim=16, t_hist=0,
+                        seg_len=256, top_chunks=5, top_groups=100, dtype="bf16")
+    gs, cs = _summaries(w)
+    cidx, gidx, _ = ora.route(w.q, cs, gs, 0, 256, 5, 100, 1)
+    assert np.all(cidx[0, 0, 0] == -1) and np.all(gidx[0, 0, 0] == -1)        # J = 0
+    assert cidx[0, 0, 1].tolist() == [0, -1, -1, -1, -1]
+    assert gidx[0, 0, 1, :8].tolist() == list(range(8)) and np.all(gidx[0, 0, 1, 8:] == -1)
+    assert cidx[0, 0, 3, :3].tolist() == [0, 1, 2]
+    assert gidx[0, 0, 3, :24].tolist() == list(range(24))
+
+
+def test_selection_acceptance_rule():
+    ids = [0, 1, 2, 3]
+    s = np.array([1.0, 2.0, 2.0 + 1e-7, -1.0], np.float32)
+    ok, ex = ora.selection_accepted([1, 2], ids, s, 2)
+    assert ok and ex == 0
+    ok, ex = ora.selection_accepted([0, 2], ids, s, 2)
+    assert not ok
+    s2 = np.array([2.0, 2.0 + 1e-6, 0.0, 0.0], np.float32)
+    ok, ex = ora.selection_accepted([0], ids, s2, 1)      # near-tie exemption
+    assert ok and ex == 1
+    ok, _ = ora.selection_accepted([1, 1], ids, s, 2)     # duplicates rejected
+    assert not ok
+
+
+def test_planted_chunks_are_recalled():
+    # a reduced planted workload: 1 sequence of 8,192 tokens, head layout 8/2/64
+    w = hi.planted_batch(batch=1, t_total=8192, seg_len=512, n_q_heads=8, n_kv_heads=2,
+                         head_dim=64, seed=55)
+    gs, cs = _summaries(w)
+    cidx, gidx, _ = ora.route(w.q, cs, gs, w.t_hist, w.seg_len, 16, 64, w.group_size)
+    planted = set(int(c) for c in w.extra["planted_chunks"][0])
+    for kvh in range(2):
+        for j in range(w.seg_len // 64):
+            assert planted <= set(int(c) for c in cidx[0, kvh, j])
+            pg = {8 * c + u for c in planted for u in range(8)}
+            assert pg <= set(int(g) for g in gidx[0, kvh, j])
