@@ -1,0 +1,181 @@
+/*
+ * hga.h -- C ABI of the Hierarchical Global Attention (HGA) routed-attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages on "Long-Context Fine-Tuning with Limited VRAM", arXiv 2607.15105):
+ * the causal history is cut into 64-token chunks, each kept as a compact
+ * summary vector, with 8-token group summaries inside each chunk; a query block
+ * scores the chunk summaries with its own projected queries (no learned router
+ * weights), keeps the top-k chunks, opens them at group level, keeps the top
+ * groups, and runs exact attention over the exact-token K/V of the selected
+ * groups (seventnews article, section "HGA的不同之处").  Training is segment-wise:
+ * only the active segment is differentiable, older K/V is detached (adnankhan.ai
+ * note, section "Raw Abstract / Excerpt").
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or synchronizes; every call only enqueues kernels
+ *    on `stream` (a hipStream_t handle; NULL = the default stream) and returns.
+ *  - Tensors are dense, row-major, 16-byte aligned.  Float tensors (q, k, v, o,
+ *    d_o, summaries, gradients) all have the element type shape->dtype
+ *    (HGA_F32: IEEE float32; HGA_BF16: bfloat16).  lse and the optional score
+ *    outputs are always float32; index tensors are int32.
+ *  - Cache layout: k_cache / v_cache are [batch, n_kv_heads, t_cap, head_dim].
+ *    Detached history occupies positions [0, t_hist); the active segment
+ *    occupies [t_hist, t_hist + seg_len).
+ *  - Query head h uses KV head h / (n_q_heads / n_kv_heads); one routing
+ *    decision is made per (sequence, KV head, 64-token query block) and shared
+ *    by the query heads of that KV head.
+ *  - Errors: every argument is checked on the host before anything is enqueued.
+ *    On error the call returns a negative hga_status, enqueues nothing and
+ *    leaves all outputs untouched.  HGA_ERR_HIP means a launch was rejected by
+ *    the HIP runtime (outputs then undefined).
+ *  - Calls are re-entrant and thread-safe; the library holds no mutable state.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HGA_OK = 0,
+  HGA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  HGA_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes                 */
+  HGA_ERR_UNSUPPORTED = -3, /* valid but unsupported configuration                */
+  HGA_ERR_CAPACITY = -4,    /* positions beyond t_cap                             */
+  HGA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                   */
+  HGA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required         */
+  HGA_ERR_HIP = -7          /* the HIP runtime rejected a launch                  */
+} hga_status;
+
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+
+typedef struct {
+  int32_t batch;        /* B >= 1                                                  */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads, Hq / Hkv in {1,2,4,8}      */
+  int32_t n_kv_heads;   /* Hkv >= 1                                                */
+  int32_t head_dim;     /* d in {64, 128}                                          */
+  int32_t chunk;        /* chunk length; must be 64                                */
+  int32_t group;        /* group length; must be 8                                 */
+  int32_t q_block;      /* query-block length; must be 64 (= chunk, aligned)       */
+  int32_t top_chunks;   /* k_c in [0, 64]: chunks kept per query block             */
+  int32_t top_groups;   /* k_g in [0, 8*k_c]: groups kept among the selected chunks */
+  int32_t dtype;        /* hga_dtype                                               */
+  float softmax_scale;  /* logits = softmax_scale * q.k; <= 0 means 1/sqrt(d)      */
+} hga_shape;
+
+/* Longest supported context in chunks (t_cap / 64) for routing. */
+#define HGA_MAX_CHUNKS 8192
+
+/*
+ * hga_build_summaries -- group and chunk summaries of the keys in
+ * [t_begin, t_end).  The pages describe a compact summary per 64-token chunk
+ * and a summary cache for its 8-token groups (seventnews, "HGA的不同之处";
+ * gist.science, "解决方案") without a formula; this library defines the summary
+ * as the mean of the keys, summed in fp32 in the fixed pairwise order
+ *   group sum  g = ((k0+k1)+(k2+k3)) + ((k4+k5)+(k6+k7))
+ *   chunk sum  c = the same tree over the chunk's 8 unscaled group sums
+ * and stores g/8 and c/64 in the key dtype (bf16: round to nearest even).
+ *
+ *   k_cache    [B, Hkv, t_cap, d]              read
+ *   group_sum  [B, Hkv, t_cap/8, d]            rows t_begin/8 .. t_end/8-1 written
+ *   chunk_sum  [B, Hkv, t_cap/64, d]           rows t_begin/64 .. t_end/64-1 written
+ *   t_begin, t_end: multiples of 64 with 0 <= t_begin <= t_end <= t_cap.
+ * Rows outside the range are not touched, so history summaries are built once
+ * and each new segment only adds its own rows.
+ */
+int hga_build_summaries(const hga_shape* shape, const void* k_cache, int64_t t_cap,
+                        int64_t t_begin, int64_t t_end, void* group_sum, void* chunk_sum,
+                        void* stream);
+
+/*
+ * hga_route -- two-level routing of every 64-token query block of the active
+ * segment (seventnews, "HGA的不同之处": queries score the chunk summaries, keep
+ * the top-k chunks, open them at group level; the router has no weights.
+ * Block-level decisions from several positions: same article, "因果泄露").
+ *
+ * For block j (positions t_hist+64j .. +63) of sequence b and KV head g:
+ *   rows       = the 64 positions x the Hq/Hkv query heads of KV head g
+ *   candidates = chunks 0 .. J-1, J = t_hist/64 + j (every complete earlier chunk)
+ *   sigma_c    = max over rows of (q . chunk_sum[c]), fp32
+ *   chunks     = top min(k_c, J) by (sigma desc, index asc)
+ *   groups     = the 8 groups of every selected chunk;
+ *   tau_x      = max over rows of (q . group_sum[x]), fp32
+ *   group_idx  = top min(k_g, #groups) by (tau desc, index asc)
+ * Outputs are stored ascending and padded with -1:
+ *   q          [B, Hq, seg_len, d]                       read
+ *   chunk_sum  [B, Hkv, t_cap/64, d], group_sum [B, Hkv, t_cap/8, d]   read
+ *   chunk_idx  [B, Hkv, seg_len/64, k_c] int32  (chunk ids)             written
+ *   group_idx  [B, Hkv, seg_len/64, k_g] int32  (group ids; token = 8*id) written
+ *   chunk_idx may be NULL when k_c == 0 and group_idx may be NULL when k_g == 0.
+ *   chunk_score, group_score: optional (may be NULL) float32 arrays shaped like
+ *   chunk_idx / group_idx holding sigma / tau of each selected id (-inf where
+ *   the id is -1).
+ * Requires seg_len > 0, t_hist and seg_len multiples of 64,
+ * t_hist + seg_len <= t_cap, (t_hist + seg_len)/64 <= HGA_MAX_CHUNKS.
+ */
+int hga_route(const hga_shape* shape, const void* q, const void* chunk_sum,
+              const void* group_sum, int64_t t_cap, int64_t t_hist, int64_t seg_len,
+              int32_t* chunk_idx, int32_t* group_idx, float* chunk_score, float* group_score,
+              void* stream);
+
+/*
+ * hga_attend_fwd -- exact attention of every active query over the exact
+ * tokens of its block's selected groups plus its own chunk up to and including
+ * its own position (summaries never act as values: seventnews, "HGA的不同之处";
+ * a bounded set of exact historical tokens per query block: the abstract).
+ *
+ *   q          [B, Hq, seg_len, d]                  read
+ *   k_cache, v_cache [B, Hkv, t_cap, d]             read (only selected groups and
+ *                                                   the active chunks are touched)
+ *   group_idx  [B, Hkv, seg_len/64, k_g] int32      read; as written by hga_route
+ *                                                   (ascending valid ids, then -1)
+ *   o          [B, Hq, seg_len, d]                  written
+ *   lse        [B, Hq, seg_len] float32             written: natural log of the sum
+ *                                                   of exp(softmax_scale * q.k) over
+ *                                                   the attended keys
+ * group_idx is trusted: ids must be valid groups before the query block.  It may
+ * be NULL when k_g == 0 (every query then attends its own chunk only).
+ */
+int hga_attend_fwd(const hga_shape* shape, const void* q, const void* k_cache,
+                   const void* v_cache, int64_t t_cap, int64_t t_hist, int64_t seg_len,
+                   const int32_t* group_idx, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace hga_attend_bwd needs (16-byte aligned); 0 on bad shape. */
+size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len);
+
+/*
+ * hga_attend_bwd -- gradients of hga_attend_fwd for the active segment only.
+ * History tokens (< t_hist) are detached and receive nothing, and no gradient
+ * flows into the summaries or the selection (adnankhan.ai note, "Raw Abstract /
+ * Excerpt": only the active segment stays differentiable; seventnews,
+ * "HGA的不同之处": the router has no weights of its own).
+ *
+ *   q, k_cache, v_cache, group_idx: as passed to hga_attend_fwd
+ *   o, lse     outputs of hga_attend_fwd for the same inputs
+ *   d_o        [B, Hq, seg_len, d]          upstream gradient of o
+ *   dq         [B, Hq, seg_len, d]          written
+ *   dk_active, dv_active [B, Hkv, seg_len, d]  written: gradients of the active
+ *              keys/values k_cache[:, :, t_hist + i] (summed over every query
+ *              row that attends them, across blocks and query heads)
+ *   workspace  device scratch of at least hga_attend_bwd_workspace_size() bytes
+ * The result is deterministic (no floating-point atomics).
+ */
+int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache,
+                   const void* v_cache, const void* o, const float* lse, const void* d_o,
+                   int64_t t_cap, int64_t t_hist, int64_t seg_len, const int32_t* group_idx,
+                   void* dq, void* dk_active, void* dv_active, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* hga_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HGA_H */

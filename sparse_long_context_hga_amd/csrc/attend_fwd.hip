@@ -1,0 +1,240 @@
+// Exact attention over the selected groups' exact-token K/V plus the own chunk.
+//
+// Pages: seventnews "BMW如何通过重新设计注意力机制，在16 GB GPU上实现16K上下文", section
+// "HGA的不同之处" (only the selected groups' exact K/V are loaded; summaries never
+// act as values or outputs) and the adnankhan.ai note, section "Raw Abstract /
+// Excerpt" (a bounded set of exact historical tokens per query block).  Reading
+// of this library: each query also attends its own 64-token chunk causally.
+//
+// bf16 path, one work-group per (sequence, KV head, query block), 2G waves of
+// 32 query rows each (the G query heads of the KV head share every gathered
+// tile: GQA-aware, one gather per KV head):
+//   * key tiles of 64 tokens = 8 selected groups (each group is one contiguous
+//     2 KiB run of K and of V in HBM), then the own chunk; double-buffered in
+//     swizzled LDS, the next tile's global loads in flight during the MFMAs;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys in rho order, B = the
+//     wave's 32 query rows held in registers): each lane ends with one query row
+//     and 32 of the 64 keys, so the online-softmax statistics live in the lane;
+//   * O^T += V^T P^T: P (bf16) is already in operand-B layout thanks to rho, and
+//     V^T comes from the row-major tile through ds_read_b64_tr_b16.
+// fp32 path: one thread per query row, plain fp32 loops (exact-precision mode).
+#include "hga_device.h"
+#include "hga_internal.h"
+
+#include <math.h>
+
+namespace hga {
+namespace {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* gidx;
+  void* o;
+  float* lse;
+  int64_t t_cap, t_hist, seg_len;
+  int Hq, Hkv, kg, nb, n_units;
+  float scale;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NT = 128 * G;
+  constexpr int KS = D / 16;       // k-steps over the head dimension
+  constexpr int DT = D / 32;       // 32-wide column tiles of O^T
+  __shared__ __align__(16) uint16_t tk[2][64 * D];
+  __shared__ __align__(16) uint16_t tv[2][64 * D];
+  __shared__ int sgid[512];
+
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  if (unit >= a.n_units) return;
+  const int j = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int J = (int)(a.t_hist / kChunk) + j;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
+  const int hh = w >> 1;                  // query head within the KV group
+  const int pos = 32 * (w & 1) + n;       // this lane's query position in the block
+  const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
+
+  const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bh * a.t_cap * D;
+  const uint16_t* vb = (const uint16_t*)a.v + (int64_t)bh * a.t_cap * D;
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + qrow * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+  }
+
+  const int n_valid = count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid);
+  const int n_sel_tiles = (n_valid + 7) >> 3;
+  const int n_tiles = n_sel_tiles + 1;
+
+  TileLoader<D, NT> ld;
+  ld.load(kb, vb, 0, n_sel_tiles, n_valid, sgid, J);
+  ld.store(tk[0], tv[0]);
+
+  const float c2 = a.scale * kLog2e;
+  float m2 = -INFINITY, lsum = 0.f;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) ld.load(kb, vb, t + 1, n_sel_tiles, n_valid, sgid, J);
+    __syncthreads();
+    const uint16_t* K = tk[buf];
+    const uint16_t* V = tv[buf];
+
+    // S^T for 64 keys: two 32-key subtiles.
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32(lds_row8<D>(K, 32 * kt + rho(n), 16 * ks + 8 * h), qf[ks], s[kt]);
+    }
+    // Scale, mask, tile maximum.  Element r of subtile kt is key 32kt + out_row(r, h).
+    const bool local = t == n_sel_tiles;
+    const int kv_lim = local ? pos : 8 * (n_valid - 8 * t) - 1;   // last valid key index in the tile
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + out_row(r, h);
+        const float x = key <= kv_lim ? s[kt][r] * c2 : -INFINITY;
+        s[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = wave_max32(mx);
+    const float m_new = fmaxf(m2, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m2 - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = m_new == -INFINITY ? 0.f : exp2f(s[kt][r] - m_new);
+        s[kt][r] = p;
+        rs += p;
+      }
+    rs = wave_sum32(rs);
+    lsum = lsum * alpha + rs;
+    m2 = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+
+    // O^T += V^T P^T over 4 k-steps of 16 keys.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = s[ks >> 1][8 * (ks & 1) + e];
+      const bf16x8 pf = f32x8_to_bf16x8(pv);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(lds_col8<D>(V, 16 * ks, 32 * dt), pf, oacc[dt]);
+    }
+    if (t + 1 < n_tiles) ld.store(tk[buf ^ 1], tv[buf ^ 1]);
+  }
+
+  // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
+  const float inv = 1.f / lsum;
+  uint16_t* op = (uint16_t*)a.o + qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * dt + 8 * g + 4 * h;
+      *reinterpret_cast<uint2*>(op + col) =
+          make_uint2(pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
+                     pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv));
+    }
+  if (h == 0) a.lse[qrow] = (m2 + log2f(lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------- fp32 (SIMT)
+template <int D>
+__global__ __launch_bounds__(512) void attend_fwd_f32_kernel(FwdArgs a, int G) {
+  __shared__ int sgid[512];
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  if (unit >= a.n_units) return;
+  const int j = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int J = (int)(a.t_hist / kChunk) + j;
+  const int nt = blockDim.x;
+  int n_valid = 0;
+  for (int i0 = 0; i0 < a.kg; i0 += nt) {
+    const int i = i0 + threadIdx.x;
+    int v = -1;
+    if (i < a.kg) { v = a.gidx[(int64_t)unit * a.kg + i]; sgid[i] = v; }
+    n_valid += __syncthreads_count(v >= 0);
+  }
+  const int hh = threadIdx.x / kQBlock, pos = threadIdx.x % kQBlock;
+  const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
+  const float* qp = (const float*)a.q + qrow * D;
+  const float* kb = (const float*)a.k + (int64_t)bh * a.t_cap * D;
+  const float* vb = (const float*)a.v + (int64_t)bh * a.t_cap * D;
+  float qv[D], acc[D];
+  for (int e = 0; e < D; ++e) { qv[e] = qp[e]; acc[e] = 0.f; }
+  float m = -INFINITY, lsum = 0.f;
+  const int n_keys = 8 * n_valid + pos + 1;
+  for (int i = 0; i < n_keys; ++i) {
+    const int64_t tok = i < 8 * n_valid ? (int64_t)kGroup * sgid[i >> 3] + (i & 7)
+                                        : (int64_t)kChunk * J + (i - 8 * n_valid);
+    const float* kr = kb + tok * D;
+    float dot = 0.f;
+    for (int e = 0; e < D; ++e) dot = fmaf(qv[e], kr[e], dot);
+    const float x = dot * a.scale;
+    const float m_new = fmaxf(m, x);
+    const float alpha = expf(m - m_new);
+    const float p = expf(x - m_new);
+    lsum = lsum * alpha + p;
+    const float* vr = vb + tok * D;
+    for (int e = 0; e < D; ++e) acc[e] = acc[e] * alpha + p * vr[e];
+    m = m_new;
+  }
+  float* op = (float*)a.o + qrow * D;
+  for (int e = 0; e < D; ++e) op[e] = acc[e] / lsum;
+  a.lse[qrow] = m + logf(lsum);
+}
+
+template <int D, int G>
+void launch_bf16(const FwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((attend_fwd_bf16_kernel<D, G>), dim3(grid), dim3(128 * G), 0, s, a);
+}
+template <int D>
+void launch_bf16_g(const FwdArgs& a, int G, int grid, hipStream_t s) {
+  switch (G) {
+    case 1: launch_bf16<D, 1>(a, grid, s); break;
+    case 2: launch_bf16<D, 2>(a, grid, s); break;
+    case 4: launch_bf16<D, 4>(a, grid, s); break;
+    default: launch_bf16<D, 8>(a, grid, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
+                             const int32_t* group_idx, void* o, float* lse, hipStream_t s) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.gidx = group_idx; a.o = o; a.lse = lse;
+  a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
+  a.Hq = d.Hq; a.Hkv = d.Hkv; a.kg = d.kg; a.nb = d.nb; a.n_units = d.B * d.Hkv * d.nb;
+  a.scale = d.scale;
+  const int grid = xcd_grid(a.n_units);
+  if (bf16) {
+    if (d.D == 128) launch_bf16_g<128>(a, d.G, grid, s);
+    else launch_bf16_g<64>(a, d.G, grid, s);
+  } else {
+    if (d.D == 128) hipLaunchKernelGGL((attend_fwd_f32_kernel<128>), dim3(grid), dim3(64 * d.G), 0, s, a, d.G);
+    else hipLaunchKernelGGL((attend_fwd_f32_kernel<64>), dim3(grid), dim3(64 * d.G), 0, s, a, d.G);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hga

@@ -1,0 +1,145 @@
+// C ABI of the HGA routed-attention library: host-side argument validation and
+// kernel dispatch.  Every check runs before anything is enqueued, so a rejected
+// call has no effect on the device.
+#include "hga.h"
+#include "hga_internal.h"
+
+#include <math.h>
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks the static shape and the positions, fills `d`.  need_seg: seg_len must be > 0.
+int resolve(const hga_shape* s, int64_t t_cap, int64_t t_hist, int64_t seg_len, hga::Dims& d) {
+  if (!s) return HGA_ERR_NULL;
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
+    return HGA_ERR_SHAPE;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HGA_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return HGA_ERR_UNSUPPORTED;
+  if (s->chunk != 64 || s->group != 8 || s->q_block != 64) return HGA_ERR_UNSUPPORTED;
+  if (s->dtype != HGA_F32 && s->dtype != HGA_BF16) return HGA_ERR_UNSUPPORTED;
+  if (s->top_chunks < 0 || s->top_groups < 0) return HGA_ERR_SHAPE;
+  if (s->top_chunks > 64) return HGA_ERR_UNSUPPORTED;
+  if (s->top_groups > 8 * s->top_chunks) return HGA_ERR_SHAPE;
+  if (!isfinite(s->softmax_scale)) return HGA_ERR_SHAPE;
+  if (t_cap <= 0 || t_cap % 64 != 0) return HGA_ERR_SHAPE;
+  if (t_hist < 0 || t_hist % 64 != 0 || seg_len < 0 || seg_len % 64 != 0) return HGA_ERR_SHAPE;
+  if (t_hist + seg_len > t_cap) return HGA_ERR_CAPACITY;
+  // unit counts are 32-bit on the device
+  if ((int64_t)s->batch * s->n_kv_heads * (seg_len / 64 + 1) > (int64_t)1 << 30) return HGA_ERR_UNSUPPORTED;
+  d.B = s->batch;
+  d.Hq = s->n_q_heads;
+  d.Hkv = s->n_kv_heads;
+  d.G = G;
+  d.D = s->head_dim;
+  d.kc = s->top_chunks;
+  d.kg = s->top_groups;
+  d.t_cap = t_cap;
+  d.t_hist = t_hist;
+  d.seg_len = seg_len;
+  d.nb = (int)(seg_len / 64);
+  d.scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
+  return HGA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int hga_build_summaries(const hga_shape* shape, const void* k_cache, int64_t t_cap, int64_t t_begin,
+                        int64_t t_end, void* group_sum, void* chunk_sum, void* stream) {
+  hga::Dims d;
+  if (t_begin < 0 || t_end < t_begin || t_begin % 64 != 0 || t_end % 64 != 0) {
+    if (!shape) return HGA_ERR_NULL;
+    return HGA_ERR_SHAPE;
+  }
+  int st = resolve(shape, t_cap, t_begin, t_end - t_begin, d);
+  if (st != HGA_OK) return st;
+  if (t_end == t_begin) return HGA_OK;
+  if (!k_cache || !group_sum || !chunk_sum) return HGA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(group_sum) || !aligned16(chunk_sum)) return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_summaries(d, shape->dtype == HGA_BF16, k_cache, t_begin, t_end, group_sum,
+                                          chunk_sum, (hipStream_t)stream));
+}
+
+int hga_route(const hga_shape* shape, const void* q, const void* chunk_sum, const void* group_sum,
+              int64_t t_cap, int64_t t_hist, int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx,
+              float* chunk_score, float* group_score, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, t_hist, seg_len, d);
+  if (st != HGA_OK) return st;
+  if (seg_len == 0) return HGA_ERR_SHAPE;
+  if ((t_hist + seg_len) / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
+  if (!q || !chunk_sum || !group_sum || (d.kc > 0 && !chunk_idx) || (d.kg > 0 && !group_idx))
+    return HGA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(chunk_sum) || !aligned16(group_sum) ||
+      (chunk_idx && !aligned16(chunk_idx)) || (group_idx && !aligned16(group_idx)) ||
+      (chunk_score && !aligned16(chunk_score)) ||
+      (group_score && !aligned16(group_score)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_route(d, shape->dtype == HGA_BF16, q, chunk_sum, group_sum, chunk_idx,
+                                      group_idx, chunk_score, group_score, (hipStream_t)stream));
+}
+
+int hga_attend_fwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                   int64_t t_cap, int64_t t_hist, int64_t seg_len, const int32_t* group_idx, void* o,
+                   float* lse, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, t_hist, seg_len, d);
+  if (st != HGA_OK) return st;
+  if (seg_len == 0) return HGA_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !o || !lse || (d.kg > 0 && !group_idx)) return HGA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      (group_idx && !aligned16(group_idx)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_attend_fwd(d, shape->dtype == HGA_BF16, q, k_cache, v_cache, group_idx, o,
+                                           lse, (hipStream_t)stream));
+}
+
+size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len) {
+  hga::Dims d;
+  if (resolve(shape, t_hist + seg_len > 0 ? t_hist + seg_len : 64, t_hist, seg_len, d) != HGA_OK) return 0;
+  return hga::bwd_workspace_bytes(d);
+}
+
+int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                   const void* o, const float* lse, const void* d_o, int64_t t_cap, int64_t t_hist,
+                   int64_t seg_len, const int32_t* group_idx, void* dq, void* dk_active, void* dv_active,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, t_hist, seg_len, d);
+  if (st != HGA_OK) return st;
+  if (seg_len == 0) return HGA_ERR_SHAPE;
+  if (seg_len / 64 > 1024) return HGA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !o || !lse || !d_o || !dq || !dk_active || !dv_active ||
+      (d.kg > 0 && !group_idx))
+    return HGA_ERR_NULL;
+  if (!workspace || workspace_bytes < hga::bwd_workspace_bytes(d)) return HGA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(d_o) || !aligned16(dq) || !aligned16(dk_active) || !aligned16(dv_active) ||
+      !aligned16(workspace) || (group_idx && !aligned16(group_idx)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_attend_bwd(d, shape->dtype == HGA_BF16, q, k_cache, v_cache, o, lse, d_o,
+                                           group_idx, dq, dk_active, dv_active, workspace,
+                                           (hipStream_t)stream));
+}
+
+const char* hga_status_string(int status) {
+  switch (status) {
+    case HGA_OK: return "ok";
+    case HGA_ERR_NULL: return "a required pointer is NULL";
+    case HGA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case HGA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HGA_ERR_CAPACITY: return "positions exceed the cache capacity t_cap";
+    case HGA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case HGA_ERR_WORKSPACE: return "workspace missing or too small";
+    case HGA_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// Two-level routing: chunk scores -> top-k chunks -> group scores -> top-k groups.
+//
+// Pages: seventnews "BMW如何通过重新设计注意力机制，在16 GB GPU上实现16K上下文", section
+// "HGA的不同之处" (queries score the chunk summaries, keep the top-k chunks, open
+// them at group level; no learned router weights) and section "一个真正的警告：
+// 因果泄露" (one decision per block from the scores of several query positions).
+// Readings of this library: the per-row score is q . summary in fp32; the block
+// score is the maximum over the block's rows (64 positions x the query heads of
+// the KV head); candidates are every complete chunk before the block; groups are
+// the 8 groups of every selected chunk; ties go to the lower index; outputs are
+// ascending and padded with -1.
+//
+// One work-group (256 threads) per (sequence, KV head, query block).  The bf16
+// path scores with v_mfma_f32_32x32x16_bf16: operand A = 32 query rows (held in
+// registers for the whole kernel), operand B = 32 summary rows, so each lane
+// ends with one candidate column and 16 of the rows and the row-maximum is a
+// register reduction plus one cross-half exchange.  Block maxima of the waves
+// meet in LDS through an atomic max on order-preserving integer keys; the top-k
+// is an exact 4-pass radix select over those keys followed by an index-ordered
+// compaction (deterministic; ties resolved by index).
+#include "hga_device.h"
+#include "hga_internal.h"
+
+#include <math.h>
+
+namespace hga {
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kMaxChunks = 8192;      // = HGA_MAX_CHUNKS
+constexpr int kMaxGroupCand = 512;    // 8 * max top_chunks
+
+struct RouteArgs {
+  const void* q;
+  const void* csum;
+  const void* gsum;
+  int32_t* cidx;
+  int32_t* gidx;
+  float* cscore;
+  float* gscore;
+  int64_t t_cap, t_hist, seg_len;
+  int Hq, Hkv, kc, kg, nb, n_units;
+};
+
+struct SelectShared {
+  uint32_t hist[256];
+  int scan[kRouteThreads / 64];
+  int digit, above;
+};
+
+// Indices of the k largest keys[0..n) (ties -> lower index), written ascending to
+// out[0..min(k,n)).  Keys must be distinct from 0 for real candidates.  Returns
+// the number written.  All threads of the block must call it.
+__device__ int block_topk(const uint32_t* keys, int n, int k, int* out, SelectShared& sh) {
+  const int tid = threadIdx.x;
+  if (k <= 0 || n <= 0) return 0;
+  if (k >= n) {
+    for (int i = tid; i < n; i += kRouteThreads) out[i] = i;
+    __syncthreads();
+    return n;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int kk = k;  // rank (1-based) of the k-th key among keys matching `prefix`
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kRouteThreads) {
+      const uint32_t u = keys[i];
+      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // Suffix sums over digits: thread t looks at digit 255 - t.
+    const int hv = (int)sh.hist[255 - tid];
+    int tot;
+    const int ex = block_exclusive_scan<kRouteThreads>(hv, sh.scan, tot);  // keys in higher digits
+    if (ex < kk && kk <= ex + hv) {
+      sh.digit = 255 - tid;
+      sh.above = ex;
+    }
+    __syncthreads();
+    prefix |= ((uint32_t)sh.digit) << shift;
+    pmask |= 255u << shift;
+    kk -= sh.above;
+    __syncthreads();
+  }
+  // Threshold key T = prefix: take every key > T and the kk lowest-index keys == T.
+  const int per = (n + kRouteThreads - 1) / kRouteThreads;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int n_eq = 0;
+  for (int i = lo; i < hi; ++i) n_eq += keys[i] == prefix;
+  int tot;
+  int eq_before = block_exclusive_scan<kRouteThreads>(n_eq, sh.scan, tot);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t u = keys[i];
+      if (u > prefix) ++n_sel;
+      else if (u == prefix) { n_sel += e < kk; ++e; }
+    }
+  }
+  int sel_before = block_exclusive_scan<kRouteThreads>(n_sel, sh.scan, tot);
+  {
+    int e = eq_before, o = sel_before;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t u = keys[i];
+      bool take = false;
+      if (u > prefix) take = true;
+      else if (u == prefix) { take = e < kk; ++e; }
+      if (take) out[o++] = i;
+    }
+  }
+  __syncthreads();
+  return k;
+}
+
+// ---------------------------------------------------------------- bf16 / MFMA
+// Rows of the block: row = hh * 64 + pos (hh = query head within the KV group).
+// Row tile rt (32 rows) belongs to wave rt % 4.
+template <int D, int G>
+__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int NRT = 2 * G;                      // 32-row tiles in the block
+  constexpr int RPW = (NRT + 3) / 4;              // row tiles per wave
+  __shared__ uint32_t ckeys[kMaxChunks];
+  __shared__ uint32_t gkeys[kMaxGroupCand];
+  __shared__ int csel[64];
+  __shared__ int gsel[kMaxGroupCand];
+  __shared__ SelectShared sh;
+
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  if (unit >= a.n_units) return;
+  const int j = unit % a.nb;
+  const int bh = unit / a.nb;                     // b * Hkv + kvh
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int J = (int)(a.t_hist / kChunk) + j;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  const uint16_t* cs = (const uint16_t*)a.csum + (int64_t)bh * (a.t_cap / kChunk) * D;
+  const uint16_t* gs = (const uint16_t*)a.gsum + (int64_t)bh * (a.t_cap / kGroup) * D;
+
+  // Query fragments (MFMA operand A): lane holds row n of each of its row tiles.
+  bf16x8 qf[RPW][KS];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int rt = w + 4 * i;
+    if (rt < NRT) {
+      const int hh = rt >> 1, pos = 32 * (rt & 1) + n;
+      const uint16_t* qp = q + ((((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + j * kQBlock + pos) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+    }
+  }
+
+  for (int i = tid; i < J; i += kRouteThreads) ckeys[i] = 0u;
+  __syncthreads();
+
+  // ---- chunk scores: candidate tiles of 32 chunks
+  for (int ct = 0; ct * 32 < J; ++ct) {
+    const int c = ct * 32 + n;
+    const int cl = min(c, J - 1);
+    bf16x8 bfr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8*>(cs + (int64_t)cl * D + 16 * ks + 8 * h);
+    float best = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      if (w + 4 * i < NRT) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32(qf[i][ks], bfr[ks], acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
+      }
+    }
+    best = wave_max32(best);
+    if (h == 0 && c < J && w < NRT) atomicMax(&ckeys[c], score_key(best));
+  }
+  __syncthreads();
+
+  const int nc = block_topk(ckeys, J, a.kc, csel, sh);   // ascending chunk ids
+
+  // ---- group scores over the 8 groups of each selected chunk
+  const int ng_cand = 8 * nc;
+  for (int i = tid; i < ng_cand; i += kRouteThreads) gkeys[i] = 0u;
+  __syncthreads();
+  for (int gt = 0; gt * 32 < ng_cand; ++gt) {
+    const int slot = gt * 32 + n;
+    const int sl = min(slot, ng_cand - 1);
+    const int gid = 8 * csel[sl >> 3] + (sl & 7);
+    bf16x8 bfr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8*>(gs + (int64_t)gid * D + 16 * ks + 8 * h);
+    float best = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      if (w + 4 * i < NRT) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32(qf[i][ks], bfr[ks], acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
+      }
+    }
+    best = wave_max32(best);
+    if (h == 0 && slot < ng_cand && w < NRT) atomicMax(&gkeys[slot], score_key(best));
+  }
+  __syncthreads();
+
+  const int ng = block_topk(gkeys, ng_cand, a.kg, gsel, sh);   // ascending slots == ascending ids
+
+  // ---- outputs
+  int32_t* co = a.cidx + (int64_t)unit * a.kc;
+  int32_t* go = a.gidx + (int64_t)unit * a.kg;
+  for (int i = tid; i < a.kc; i += kRouteThreads) {
+    co[i] = i < nc ? csel[i] : -1;
+    if (a.cscore) a.cscore[(int64_t)unit * a.kc + i] = i < nc ? key_score(ckeys[csel[i]]) : -INFINITY;
+  }
+  for (int i = tid; i < a.kg; i += kRouteThreads) {
+    const int slot = i < ng ? gsel[i] : 0;
+    go[i] = i < ng ? 8 * csel[slot >> 3] + (slot & 7) : -1;
+    if (a.gscore) a.gscore[(int64_t)unit * a.kg + i] = i < ng ? key_score(gkeys[slot]) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- fp32 (SIMT)
+// Same routing with fp32 dot products on the vector ALUs (exact-precision mode).
+template <int D>
+__global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a, int G) {
+  __shared__ uint32_t ckeys[kMaxChunks];
+  __shared__ uint32_t gkeys[kMaxGroupCand];
+  __shared__ int csel[64];
+  __shared__ int gsel[kMaxGroupCand];
+  __shared__ SelectShared sh;
+
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  if (unit >= a.n_units) return;
+  const int j = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int J = (int)(a.t_hist / kChunk) + j;
+  const int tid = threadIdx.x;
+  const float* q = (const float*)a.q;
+  const float* cs = (const float*)a.csum + (int64_t)bh * (a.t_cap / kChunk) * D;
+  const float* gs = (const float*)a.gsum + (int64_t)bh * (a.t_cap / kGroup) * D;
+  const int R = G * kQBlock;
+
+  auto block_max = [&](const float* srow) {
+    float best = -INFINITY;
+    for (int r = 0; r < R; ++r) {
+      const int hh = r / kQBlock, pos = r % kQBlock;
+      const float* qp = q + ((((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + j * kQBlock + pos) * D;
+      float acc = 0.f;
+      for (int e = 0; e < D; ++e) acc = fmaf(qp[e], srow[e], acc);
+      best = fmaxf(best, acc);
+    }
+    return best;
+  };
+
+  for (int c = tid; c < J; c += kRouteThreads) ckeys[c] = score_key(block_max(cs + (int64_t)c * D));
+  __syncthreads();
+  const int nc = block_topk(ckeys, J, a.kc, csel, sh);
+  const int ng_cand = 8 * nc;
+  for (int s = tid; s < ng_cand; s += kRouteThreads)
+    gkeys[s] = score_key(block_max(gs + (int64_t)(8 * csel[s >> 3] + (s & 7)) * D));
+  __syncthreads();
+  const int ng = block_topk(gkeys, ng_cand, a.kg, gsel, sh);
+
+  int32_t* co = a.cidx + (int64_t)unit * a.kc;
+  int32_t* go = a.gidx + (int64_t)unit * a.kg;
+  for (int i = tid; i < a.kc; i += kRouteThreads) {
+    co[i] = i < nc ? csel[i] : -1;
+    if (a.cscore) a.cscore[(int64_t)unit * a.kc + i] = i < nc ? key_score(ckeys[csel[i]]) : -INFINITY;
+  }
+  for (int i = tid; i < a.kg; i += kRouteThreads) {
+    const int slot = i < ng ? gsel[i] : 0;
+    go[i] = i < ng ? 8 * csel[slot >> 3] + (slot & 7) : -1;
+    if (a.gscore) a.gscore[(int64_t)unit * a.kg + i] = i < ng ? key_score(gkeys[slot]) : -INFINITY;
+  }
+}
+
+template <int D, int G>
+void launch_bf16(const RouteArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((route_bf16_kernel<D, G>), dim3(grid), dim3(kRouteThreads), 0, s, a);
+}
+
+template <int D>
+void launch_bf16_g(const RouteArgs& a, int G, int grid, hipStream_t s) {
+  switch (G) {
+    case 1: launch_bf16<D, 1>(a, grid, s); break;
+    case 2: launch_bf16<D, 2>(a, grid, s); break;
+    case 4: launch_bf16<D, 4>(a, grid, s); break;
+    default: launch_bf16<D, 8>(a, grid, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* chunk_sum,
+                        const void* group_sum, int32_t* chunk_idx, int32_t* group_idx,
+                        float* chunk_score, float* group_score, hipStream_t s) {
+  RouteArgs a;
+  a.q = q; a.csum = chunk_sum; a.gsum = group_sum;
+  a.cidx = chunk_idx; a.gidx = group_idx; a.cscore = chunk_score; a.gscore = group_score;
+  a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
+  a.Hq = d.Hq; a.Hkv = d.Hkv; a.kc = d.kc; a.kg = d.kg; a.nb = d.nb;
+  a.n_units = d.B * d.Hkv * d.nb;
+  const int grid = xcd_grid(a.n_units);
+  if (bf16) {
+    if (d.D == 128) launch_bf16_g<128>(a, d.G, grid, s);
+    else launch_bf16_g<64>(a, d.G, grid, s);
+  } else {
+    if (d.D == 128) hipLaunchKernelGGL((route_f32_kernel<128>), dim3(grid), dim3(kRouteThreads), 0, s, a, d.G);
+    else hipLaunchKernelGGL((route_f32_kernel<64>), dim3(grid), dim3(kRouteThreads), 0, s, a, d.G);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hga

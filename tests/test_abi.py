@@ -1,0 +1,116 @@
+"""The C ABI on the host: the library loads, exports every declared entry point,
+and rejects bad arguments before enqueueing anything (no GPU needed: every
+call below fails validation, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hga.h")
+
+hga = pytest.importorskip("sparse_long_context_hga_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hga.LIB_PATH):
+        pytest.fail("libhga.so not built (run __graft_entry__.build())")
+    return hga.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hga_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == {"hga_build_summaries", "hga_route", "hga_attend_fwd",
+                          "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in hga._lib.SIGNATURES
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        assert hga.hga_status_string(code) not in ("", "unknown status")
+    assert hga.hga_status_string(-99) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, top_chunks=16, top_groups=64,
+                dtype="bf16")
+    base.update(kw)
+    return hga.make_shape(**base)
+
+
+A = ctypes.c_void_p(0x10000)   # fake, aligned, never dereferenced (every call fails validation)
+M = ctypes.c_void_p(0x10008)   # fake, misaligned
+
+
+def _route(L, s, t_cap=16384, t_hist=14336, seg=2048, q=A, cidx=A, gidx=A):
+    return L.hga_route(ctypes.byref(s) if s is not None else None, q, A, A, t_cap, t_hist, seg, cidx, gidx,
+                       None, None, None)
+
+
+def test_route_validation(L):
+    assert _route(L, None) == -1
+    assert _route(L, _shape(), q=None) == -1
+    assert _route(L, _shape(), cidx=None) == -1
+    assert _route(L, _shape(n_q_heads=24)) == -3            # G = 3
+    assert _route(L, _shape(n_q_heads=30)) == -2            # not a multiple
+    assert _route(L, _shape(head_dim=96)) == -3
+    assert _route(L, _shape(top_chunks=65, top_groups=64)) == -3
+    assert _route(L, _shape(top_groups=129)) == -2          # > 8 * top_chunks
+    assert _route(L, _shape(top_chunks=-1)) == -2
+    assert _route(L, _shape(), t_hist=100) == -2
+    assert _route(L, _shape(), seg=0) == -2
+    assert _route(L, _shape(), t_hist=16384) == -4          # beyond t_cap
+    assert _route(L, _shape(), t_cap=1 << 20, t_hist=(1 << 19), seg=2048) == -3   # > max chunks
+    assert _route(L, _shape(), q=M) == -5
+    s = _shape()
+    s.chunk = 32
+    assert _route(L, s) == -3
+    s = _shape()
+    s.dtype = 7
+    assert _route(L, s) == -3
+    s = _shape()
+    s.softmax_scale = float("nan")
+    assert _route(L, s) == -2
+
+
+def test_summaries_validation(L):
+    s = _shape()
+    f = L.hga_build_summaries
+    assert f(None, A, 16384, 0, 64, A, A, None) == -1
+    assert f(ctypes.byref(s), A, 16384, 32, 64, A, A, None) == -2
+    assert f(ctypes.byref(s), A, 16384, 128, 64, A, A, None) == -2
+    assert f(ctypes.byref(s), A, 16384, 0, 16448, A, A, None) == -4
+    assert f(ctypes.byref(s), None, 16384, 0, 64, A, A, None) == -1
+    assert f(ctypes.byref(s), M, 16384, 0, 64, A, A, None) == -5
+    assert f(ctypes.byref(s), None, 16384, 64, 64, None, None, None) == 0   # empty range: no-op
+
+
+def test_attend_validation(L):
+    s = _shape()
+    fw = L.hga_attend_fwd
+    assert fw(ctypes.byref(s), A, A, A, 16384, 14336, 2048, None, A, A, None) == -1   # group_idx needed
+    assert fw(ctypes.byref(s), A, A, A, 16384, 14336, 4096, A, A, A, None) == -4
+    assert fw(ctypes.byref(s), A, A, M, 16384, 14336, 2048, A, A, A, None) == -5
+    need = hga.hga_attend_bwd_workspace_size(s, 14336, 2048)
+    assert need == 32 * 2048 * 4
+    bw = L.hga_attend_bwd
+    args = [A, A, A, A, A, A, 16384, 14336, 2048, A, A, A, A]
+    assert bw(ctypes.byref(s), *args, A, need - 1, None) == -6
+    assert bw(ctypes.byref(s), *args, None, need, None) == -6
+    assert bw(ctypes.byref(s), *args[:-1], None, A, need, None) == -1
+    args_m = list(args)
+    args_m[5] = M
+    assert bw(ctypes.byref(s), *args_m, A, need, None) == -5
+    big = hga.hga_attend_bwd_workspace_size(s, 0, 64 * 1025)
+    assert bw(ctypes.byref(s), A, A, A, A, A, A, 1 << 17, 0, 64 * 1025, A, A, A, A, A, big, None) == -3
+    assert hga.hga_attend_bwd_workspace_size(_shape(head_dim=80), 0, 64) == 0
