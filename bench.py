@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the HGA routed-attention layer step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+build the active segment's summaries, route every query block, attention
+forward, attention backward (dQ and the active segment's dK/dV).  Inputs are
+resident in HBM before the timed region; the history summaries are built once,
+untimed, like a cache that earlier segments filled.
+
+Default workload: a Qwen3-8B-shaped attention layer (32 query / 8 KV heads,
+head_dim 128, bf16) at 16,384 tokens of context: 14,336 detached history tokens
+plus a 2,048-token active segment, top-16 chunks / top-64 groups, block-structured
+keys.  Prints one JSON line (tokens/s of the active segment, whole job).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "HGA attention-layer tokens/s (fwd+bwd) at 16K ctx; % of HBM and MFMA roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
+                   choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k"])
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="also run one device copy of this size first (reference for HBM counters)")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ algorithmic work
+def algorithmic_work(w, gidx):
+    """Algorithmic HBM bytes and MFMA flops per kernel for one step, from the
+    selection actually made (number of valid groups per unit)."""
+    import numpy as np
+    B, Hq, Hkv, d, S, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seg_len, w.group_size
+    el = 2 if w.dtype == "bf16" else 4
+    nb = S // 64
+    R = G * 64                                       # query rows per unit
+    n_sel = (gidx >= 0).sum(axis=-1) * 8             # selected tokens per unit [B,Hkv,nb]
+    tok_sel = float(n_sel.sum())
+    units = B * Hkv * nb
+    loc_keys = 32.5                                  # causal own-chunk keys per row (mean)
+    kv_sel = tok_sel * d * el * 2                    # gathered K and V
+    kv_loc = units * 64 * d * el * 2
+    q_bytes = B * Hq * S * d * el
+    # forward: Q, gathered K/V, own chunk K/V, O, LSE, selection
+    fwd_bytes = q_bytes + kv_sel + kv_loc + q_bytes + B * Hq * S * 4 + gidx.size * 4
+    fwd_flops = 2 * 2 * R * d * tok_sel + 2 * 2 * R * d * loc_keys * units
+    # dQ: Q, dO, O, LSE, gathered K/V, own chunk K/V, dQ, D
+    dq_bytes = 3 * q_bytes + kv_sel + kv_loc + q_bytes + 2 * B * Hq * S * 4 + gidx.size * 4
+    dq_flops = 3 * 2 * R * d * tok_sel + 3 * 2 * R * d * loc_keys * units
+    # dK/dV: own K/V, Q/dO rows of every visiting block, dK, dV
+    act_lo = w.t_hist // 8
+    visits = 0
+    sel_act_tokens = 0
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(nb):
+                g = gidx[b, h, j]
+                g = g[g >= act_lo]
+                sel_act_tokens += 8 * len(g)
+                visits += len(np.unique(g // 8))
+    visits += units                                   # own block of every chunk
+    dkdv_bytes = kv_loc + visits * 2 * R * d * el + visits * 2 * R * 4 + kv_loc
+    dkdv_flops = 4 * 2 * R * d * (sel_act_tokens + loc_keys * units)
+    # routing: Q block rows x candidate chunk summaries, then 8*k_c group summaries
+    J = np.arange(nb) + w.t_hist // 64
+    route_flops = B * Hkv * float(np.sum(2 * R * d * (J + 8 * np.minimum(w.top_chunks, J))))
+    route_bytes = q_bytes + B * Hkv * (w.t_hist + S) // 64 * d * el + gidx.size * 4 * 2
+    sum_bytes = B * Hkv * S * d * el + B * Hkv * (S // 8 + S // 64) * d * el
+    return {
+        "summaries": {"bytes": sum_bytes, "flops": 0.0},
+        "route": {"bytes": route_bytes, "flops": route_flops},
+        "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops},
+        "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops},
+        "attend_bwd_dkdv": {"bytes": dkdv_bytes, "flops": dkdv_flops},
+    }
+
+
+def make_workload(name):
+    import hga_inputs as hi
+    return {"qwen3_8b_layer_ctx16k": hi.qwen_16k, "qwen3_8b_layer_ctx4k": hi.qwen_2k_hist,
+            "planted_b8_ctx32k": hi.planted_batch}[name]()
+
+
+# ------------------------------------------------------------------ CPU oracle leg
+def cpu_baseline(w, min_seconds=10.0, max_reps=5):
+    """The CPU oracle, as it stands, on the same step (all of it), repeated until
+    about `min_seconds` of work; returns tokens/s from the median repetition."""
+    import numpy as np
+    from oracle import hga_oracle as ora
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, H, T, d = w.k_cache.shape
+    gs = np.zeros((B, H, T // 8, d), np.float32)
+    cs = np.zeros((B, H, T // 64, d), np.float32)
+    ora.build_summaries(w.k_cache, 0, w.t_hist, w.dtype, gs, cs)   # history: untimed, as on the GPU
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
+        t0 = time.perf_counter()
+        ora.build_summaries(w.k_cache, w.t_hist, w.t_hist + w.seg_len, w.dtype, gs, cs)
+        _, gidx, _ = ora.route(w.q, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, w.group_size)
+        ora.attend_fwd(w.q, w.k_cache, w.v_cache, w.t_hist, gidx, w.softmax_scale, w.group_size)
+        if w.d_o is not None:
+            ora.attend_bwd(w.q, w.k_cache, w.v_cache, w.d_o, w.t_hist, gidx, w.softmax_scale, w.group_size)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": w.batch * w.seg_len / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full step of this workload (active summaries, route, forward, backward), "
+                      f"{len(times)} repetitions, median {t:.2f} s"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the HGA layer path has no multi-GPU mode "
+              "(sharding is by sequence and KV head, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import sparse_long_context_hga_amd as hga
+    from sparse_long_context_hga_amd.layer import HGALayerBuffers
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    hga.lib()
+    w = make_workload(args.workload)
+    print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
+          f"t_hist={w.t_hist} S={w.seg_len} k_c={w.top_chunks} k_g={w.top_groups}", file=sys.stderr, flush=True)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda x: torch.from_numpy(x).to("cuda").to(dt).contiguous()   # noqa: E731
+    shape = hga.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.top_chunks, w.top_groups,
+                           w.dtype, w.softmax_scale)
+    L = HGALayerBuffers(shape, dev(w.q), dev(w.k_cache), dev(w.v_cache), w.t_hist,
+                        dev(w.d_o) if w.d_o is not None else None)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    L.summaries(0, w.t_hist)                                  # history summaries: built once, untimed
+    torch.cuda.synchronize()
+
+    calls = [
+        ("summaries", lambda: L.summaries(w.t_hist, w.t_hist + w.seg_len)),
+        ("route", L.route),
+        ("attend_fwd", L.fwd),
+        ("attend_bwd", L.bwd),
+    ]
+    for _ in range(args.warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; events between the calls on the stream the library launches on.
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(calls):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {name: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps))
+                for i, (name, _) in enumerate(calls)}
+    step_ms_events = statistics.mean(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps))
+    ms_per_step = wall * 1e3 / args.steps
+
+    gidx = L.gidx.cpu().numpy()
+    work = algorithmic_work(w, gidx)
+    kern_ms = {"summaries": per_call["summaries"], "route": per_call["route"],
+               "attend_fwd": per_call["attend_fwd"], "attend_bwd": per_call["attend_bwd"]}
+    work["attend_bwd"] = {"bytes": work["attend_bwd_dq"]["bytes"] + work["attend_bwd_dkdv"]["bytes"],
+                          "flops": work["attend_bwd_dq"]["flops"] + work["attend_bwd_dkdv"]["flops"]}
+    kernels = {}
+    for k, ms in kern_ms.items():
+        wk = work[k]
+        kernels[k] = {"ms": round(ms, 5), "GB/s": round(wk["bytes"] / (ms * 1e-3) / 1e9, 1),
+                      "TFLOP/s": round(wk["flops"] / (ms * 1e-3) / 1e12, 2)}
+    dom = max(("attend_fwd", "attend_bwd", "route"), key=lambda k: kern_ms[k])
+    ach = work[dom]["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+
+    tokens = w.batch * w.seg_len
+    out = {
+        "metric": METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "t_hist": w.t_hist,
+                   "seg_len": w.seg_len, "context": w.t_hist + w.seg_len, "top_chunks": w.top_chunks,
+                   "top_groups": w.top_groups, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "step_ms_events": round(step_ms_events, 5),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,6 +13,7 @@ import torch
 
 import hga_inputs as hi
 import sparse_long_context_hga_amd as hga
+from sparse_long_context_hga_amd.layer import HGALayerBuffers
 from oracle import hga_oracle as ora
 
 # Acceptance thresholds (O / LSE max-abs per dtype, gradients relative L2, near-tie margin).
@@ -39,64 +40,14 @@ def shape_of(w: hi.Workload, top_chunks: Optional[int] = None, top_groups: Optio
                           w.top_groups if top_groups is None else top_groups, w.dtype, w.softmax_scale)
 
 
-class DeviceLayer:
-    """Device copies of a workload plus the output buffers of one layer step."""
+class DeviceLayer(HGALayerBuffers):
+    """Device copies of a workload plus the buffers of one layer step."""
 
     def __init__(self, w: hi.Workload, device="cuda"):
         self.w = w
-        B, Hq, Hkv, d, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seg_len
-        dt = tdt(w.dtype)
-        self.shape = shape_of(w)
-        self.q = to_dev(w.q, w.dtype, device)
-        self.k = to_dev(w.k_cache, w.dtype, device)
-        self.v = to_dev(w.v_cache, w.dtype, device)
-        self.do = to_dev(w.d_o, w.dtype, device) if w.d_o is not None else None
-        nb = S // 64
-        self.gsum = torch.zeros(B, Hkv, w.t_cap // 8, d, dtype=dt, device=device)
-        self.csum = torch.zeros(B, Hkv, w.t_cap // 64, d, dtype=dt, device=device)
-        self.cidx = torch.empty(B, Hkv, nb, max(1, w.top_chunks), dtype=torch.int32, device=device)[..., :w.top_chunks]
-        self.gidx = torch.empty(B, Hkv, nb, max(1, w.top_groups), dtype=torch.int32, device=device)[..., :w.top_groups]
-        self.cidx = self.cidx.contiguous()
-        self.gidx = self.gidx.contiguous()
-        self.cscore = torch.empty(B, Hkv, nb, w.top_chunks, dtype=torch.float32, device=device)
-        self.gscore = torch.empty(B, Hkv, nb, w.top_groups, dtype=torch.float32, device=device)
-        self.o = torch.empty(B, Hq, S, d, dtype=dt, device=device)
-        self.lse = torch.empty(B, Hq, S, dtype=torch.float32, device=device)
-        self.dq = torch.empty_like(self.q)
-        self.dk = torch.empty(B, Hkv, S, d, dtype=dt, device=device)
-        self.dv = torch.empty(B, Hkv, S, d, dtype=dt, device=device)
-        ws = hga.hga_attend_bwd_workspace_size(self.shape, w.t_hist, S)
-        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
-
-    # -- the four library calls
-    def summaries(self, t_begin: int, t_end: int):
-        hga.hga_build_summaries(self.shape, self.k, self.w.t_cap, t_begin, t_end, self.gsum, self.csum)
-
-    def route(self, csum=None, gsum=None):
-        w = self.w
-        hga.hga_route(self.shape, self.q, self.csum if csum is None else csum,
-                      self.gsum if gsum is None else gsum, w.t_cap, w.t_hist, w.seg_len,
-                      self.cidx, self.gidx, self.cscore, self.gscore)
-
-    def fwd(self, gidx=None):
-        w = self.w
-        hga.hga_attend_fwd(self.shape, self.q, self.k, self.v, w.t_cap, w.t_hist, w.seg_len,
-                           self.gidx if gidx is None else gidx, self.o, self.lse)
-
-    def bwd(self, gidx=None):
-        w = self.w
-        hga.hga_attend_bwd(self.shape, self.q, self.k, self.v, self.o, self.lse, self.do, w.t_cap,
-                           w.t_hist, w.seg_len, self.gidx if gidx is None else gidx, self.dq, self.dk,
-                           self.dv, self.ws)
-
-    def step(self):
-        """One pass of the hot path: active-segment summaries, route, forward, backward."""
-        w = self.w
-        self.summaries(w.t_hist, w.t_hist + w.seg_len)
-        self.route()
-        self.fwd()
-        if self.do is not None:
-            self.bwd()
+        do = to_dev(w.d_o, w.dtype, device) if w.d_o is not None else None
+        super().__init__(shape_of(w), to_dev(w.q, w.dtype, device), to_dev(w.k_cache, w.dtype, device),
+                         to_dev(w.v_cache, w.dtype, device), w.t_hist, do)
 
 
 # ---------------------------------------------------------------- oracle side
