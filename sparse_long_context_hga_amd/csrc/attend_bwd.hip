@@ -27,7 +27,12 @@
 namespace hga {
 namespace {
 
+constexpr int kStages = 2;   // K/V tile buffer sets of the dQ kernel
+
 constexpr int kMaxBlocks = 1024;   // query blocks per segment supported by the dkdv kernel
+constexpr int kTargetRounds = 8;   // dK/dV work is cut into items of about this many rounds
+constexpr int kMaxParts = 8;       // at most this many items per active chunk
+constexpr int kBuckets = 64;       // work-list buckets (rounds per work item, capped)
 
 struct BwdArgs {
   const void* q;
@@ -40,7 +45,13 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;      // [B, Hq, S] rowsum(dO * O)
+  float* dvec;      // [B, Hq, S] rowsum(dO * O)            (workspace)
+  int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
+  int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
+  int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
+  int* bcount;      // [64] work items per bucket (bucket = rounds, capped at 63) (workspace)
+  int* bitems;      // [64, B*Hkv*S/64*kMaxParts] work items (chunk * kMaxParts + part) (workspace)
+  float* parts;     // [B, Hkv, S/64, kMaxParts, 2, 64, d] fp32 partials (workspace)
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kg, nb, n_units;
   float scale;
@@ -62,11 +73,20 @@ __device__ __forceinline__ float dot8_bf16(bf16x8 x, bf16x8 y) {
 template <int D, int G>
 __global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   constexpr int NT = 128 * G;
+  constexpr int NW = 2 * G;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __align__(16) uint16_t tk[2][64 * D];
-  __shared__ __align__(16) uint16_t tv[2][64 * D];
+  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
+  __shared__ __align__(16) uint16_t k2[64 * D], v2[64 * D], k3[64 * D], v3[64 * D];
   __shared__ int sgid[512];
+  auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return k0; else if constexpr (B() == 1) return k1;
+    else if constexpr (B() == 2) return k2; else return k3;
+  };
+  auto VB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return v0; else if constexpr (B() == 1) return v1;
+    else if constexpr (B() == 2) return v2; else return v3;
+  };
 
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   if (unit >= a.n_units) return;
@@ -96,54 +116,80 @@ __global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) 
   }
   const float Dr = wave_sum32(dpart);
   if (h == 0) a.dvec[qrow] = Dr;
+  if (unit == 0 && tid < kBuckets) a.bcount[tid] = 0;   // work-list counters for the plan kernel
   const float lse2 = a.lse[qrow] * kLog2e;
 
   const int n_valid = count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid);
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
-  TileLoader<D, NT> ld;
-  ld.load(kb, vb, 0, n_sel_tiles, n_valid, sgid, J);
-  ld.store(tk[0], tv[0]);
+  auto token = [&](int t, int r) __attribute__((always_inline)) -> int64_t {
+    if (t < n_sel_tiles) {
+      const int slot = 8 * t + (r >> 3);
+      return slot < n_valid ? (int64_t)kGroup * sgid[slot] + (r & 7) : (int64_t)kChunk * J;
+    }
+    return (int64_t)kChunk * J + r;
+  };
+  auto issue = [&](int t, auto B) __attribute__((always_inline)) {
+    dma_tile<D, NW>(KB(B), [&](int r) { return kb + token(t, r) * D; });
+    dma_tile<D, NW>(VB(B), [&](int r) { return vb + token(t, r) * D; });
+  };
 
   const float c2 = a.scale * kLog2e;
   f32x16 dqacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dqacc[dt] = f32x16{};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) ld.load(kb, vb, t + 1, n_sel_tiles, n_valid, sgid, J);
-    __syncthreads();
-    const uint16_t* K = tk[buf];
-    const uint16_t* V = tv[buf];
+  auto compute = [&](int t, auto B) __attribute__((always_inline)) {
+    const uint16_t* K = KB(B);
+    const uint16_t* V = VB(B);
     const bool local = t == n_sel_tiles;
-    const int kv_lim = local ? pos : 8 * (n_valid - 8 * t) - 1;
+    const bool full = !local && 8 * (t + 1) <= n_valid;
+    const int kv_lim = full ? 63 : local ? pos : 8 * (n_valid - 8 * t) - 1;
     // One 32-key subtile at a time keeps the live score registers to 2 x 16.
+    const ColReader<D> colrd;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      const RowReader<D> rowrd(32 * kt + rho(n));
       f32x16 s = {}, dpv = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(lds_row8<D>(K, 32 * kt + rho(n), 16 * ks + 8 * h), qf[ks], s);
-        dpv = mfma32(lds_row8<D>(V, 32 * kt + rho(n), 16 * ks + 8 * h), dof[ks], dpv);
+      for (int hb = 0; hb < 2; ++hb) {               // two batches of KS/2 k-steps
+        bf16x8 ka[KS / 2], va[KS / 2];
+#pragma unroll
+        for (int i = 0; i < KS / 2; ++i) {
+          ka[i] = rowrd(K, 16 * (hb * KS / 2 + i) + 8 * h);
+          va[i] = rowrd(V, 16 * (hb * KS / 2 + i) + 8 * h);
+        }
+#pragma unroll
+        for (int i = 0; i < KS / 2; ++i) {
+          s = mfma32(ka[i], qf[hb * KS / 2 + i], s);
+          dpv = mfma32(va[i], dof[hb * KS / 2 + i], dpv);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
       }
+      // K^T fragments for the dQ update (independent of dS: read before the softmax math).
+      bf16x8 kt_fr[2][DT];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) kt_fr[half][dt] = colrd(K, 32 * kt + 16 * half, 32 * dt);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + out_row(r, h);
-        const float p = key <= kv_lim ? exp2f(s[r] * c2 - lse2) : 0.f;
+        float p = fast_exp2(fmaf(s[r], c2, -lse2));
+        if (!full && 32 * kt + out_row(r, h) > kv_lim) p = 0.f;
         ds[r] = p * (dpv[r] - Dr);
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const bf16x8 dsf = f32x8_to_bf16x8(ds + 8 * half);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          dqacc[dt] = mfma32(lds_col8<D>(K, 32 * kt + 16 * half, 32 * dt), dsf, dqacc[dt]);
+        for (int dt = 0; dt < DT; ++dt) dqacc[dt] = mfma32(kt_fr[half][dt], dsf, dqacc[dt]);
       }
     }
-    if (t + 1 < n_tiles) ld.store(tk[buf ^ 1], tv[buf ^ 1]);
-  }
+  };
+
+  pipeline<kStages, 2 * dma_per_wave<D, NW>()>(n_tiles, issue, compute);
 
   uint16_t* qo = (uint16_t*)a.dq + qrow * D;
 #pragma unroll
@@ -151,36 +197,161 @@ __global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) 
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int col = 32 * dt + 8 * g + 4 * h;
-      *reinterpret_cast<uint2*>(qo + col) =
-          make_uint2(pack_bf16x2(dqacc[dt][4 * g] * a.scale, dqacc[dt][4 * g + 1] * a.scale),
-                     pack_bf16x2(dqacc[dt][4 * g + 2] * a.scale, dqacc[dt][4 * g + 3] * a.scale));
+      *reinterpret_cast<uint2*>(qo + col) = f32x4_to_bf16x4_bits(
+          dqacc[dt][4 * g] * a.scale, dqacc[dt][4 * g + 1] * a.scale, dqacc[dt][4 * g + 2] * a.scale,
+          dqacc[dt][4 * g + 3] * a.scale);
     }
 }
 
 // ---------------------------------------------------------------- dK/dV (bf16)
-// 4 waves: wave w owns keys 32*(w&1) .. +31 of the chunk and, for every staged
-// 64-row tile, the rows 32*(w>>1) .. +31; the two row halves are summed at the end.
+// Work item (sequence, KV head, active chunk, part).  A chunk is attended by its
+// own block (causally) and by every later block whose selection holds one of its
+// groups; each such block contributes G "rounds" (64 rows of one query head).
+// Lightly visited chunks (<= kDirectVisits visits) are done by part 0 alone, which
+// writes bf16 dK/dV; popular chunks are split by query head over G work-groups
+// that write fp32 partials, summed in part order by the finalize kernel
+// (deterministic; no atomics).
+// Inside a work-group: 4 waves; wave w owns keys 32*(w&1) .. +31 of the chunk
+// and rows 32*(w>>1) .. +31 of every round; the next round's Q/dO rows are
+// prefetched into registers while the current round is computed.
+
+struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) vector
+  static size_t up(size_t x) { return (x + 255) & ~(size_t)255; }
+  static size_t flags_off(size_t rows) { return up(rows * 4); }
+  static size_t nvis_off(size_t rows, size_t units) { return up(flags_off(rows) + units * 4); }
+  static size_t vis_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
+  static size_t bcount_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
+  static size_t bitems_off(size_t rows, size_t units, size_t nb) { return up(bcount_off(rows, units, nb) + kBuckets * 4); }
+  static size_t part_off(size_t rows, size_t units, size_t nb) {
+    return up(bitems_off(rows, units, nb) + (size_t)kBuckets * units * kMaxParts * 4);
+  }
+};
+
+// Inverse of the selection for the active segment: for every active chunk, the
+// ascending list of query blocks that attend it (its own block, causally, and
+// every later block whose group list holds one of its 8 groups), with the mask of
+// the selected groups, and whether its dK/dV work is split over the query heads.
+// One wave per (sequence, KV head, active chunk); reads only group_idx.
+template <int G>
+__global__ __launch_bounds__(64) void attend_bwd_plan_kernel(BwdArgs a) {
+  __shared__ uint32_t mask[kMaxBlocks];
+  const int unit = blockIdx.x;
+  if (unit >= a.n_units) return;
+  const int cc = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int l = threadIdx.x;
+  const int64_t g_lo = (a.t_hist / kChunk + cc) * 8;
+  for (int i = l; i < a.nb; i += 64) mask[i] = i == cc ? 0xFFu : 0u;
+  __syncthreads();
+  const int later = a.nb - 1 - cc;
+  const int32_t* g0 = a.gidx + ((int64_t)bh * a.nb + cc + 1) * a.kg;
+  const int total = later * a.kg;
+  // 16 independent loads in flight per lane, then the tests.
+  for (int e0 = 0; e0 < total; e0 += 64 * 16) {
+    int32_t gv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + 64 * u + l;
+      gv[u] = e < total ? g0[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t gid = gv[u];
+      if (gid >= g_lo && gid < g_lo + 8)
+        atomicOr(&mask[cc + 1 + (e0 + 64 * u + l) / a.kg], 1u << (int)(gid - g_lo));
+    }
+  }
+  __syncthreads();
+  int n = 0;
+  int* out = a.vis + (int64_t)unit * a.nb;
+  for (int j0 = cc; j0 < a.nb; j0 += 64) {
+    const int jj = j0 + l;
+    const uint32_t m = jj < a.nb ? mask[jj] : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    if (m != 0u) out[n + __popcll(bal & ((1ull << l) - 1ull))] = jj | (int)(m << 16);
+    n += __popcll(bal);
+  }
+  if (l == 0) {
+    // G rounds (query heads) per attending block; cut into np balanced items.
+    const int rounds = G * n;
+    const int np = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
+    const size_t cap = (size_t)a.n_units * kMaxParts;
+    for (int k = 0; k < np; ++k) {
+      const int rk = (k + 1) * rounds / np - k * rounds / np;
+      const int bucket = min(rk, kBuckets - 1);
+      const int pos = atomicAdd(&a.bcount[bucket], 1);
+      a.bitems[bucket * cap + pos] = unit * kMaxParts + k;
+    }
+    a.nvis[unit] = n;
+    a.flags[unit] = np;
+  }
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void attend_bwd_dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int CH = D / 8;
-  __shared__ __align__(16) uint16_t tqdo[2 * 64 * D];   // Q tile, then dO tile
-  __shared__ float slse[64], sdr[64];
-  __shared__ uint32_t vmask[kMaxBlocks];
-  uint16_t* tq = tqdo;
-  uint16_t* tdo = tqdo + 64 * D;
+  __shared__ __align__(16) uint16_t q0[64 * D], do0[64 * D], q1[64 * D], do1[64 * D], q2[64 * D], do2[64 * D];
+  __shared__ __align__(16) float ls0[64], dr0[64], ls1[64], dr1[64], ls2[64], dr2[64];
+  __shared__ uint32_t vmask[kMaxBlocks];   // group mask of the i-th attending block
+  __shared__ int vlist[kMaxBlocks];        // i-th attending block
+  __shared__ int s_item;
+  auto QB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return q0; else if constexpr (B() == 1) return q1; else return q2;
+  };
+  auto OB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return do0; else if constexpr (B() == 1) return do1; else return do2;
+  };
+  auto LB = [&](auto B) __attribute__((always_inline)) -> float* {
+    if constexpr (B() == 0) return ls0; else if constexpr (B() == 1) return ls1; else return ls2;
+  };
+  auto RB = [&](auto B) __attribute__((always_inline)) -> float* {
+    if constexpr (B() == 0) return dr0; else if constexpr (B() == 1) return dr1; else return dr2;
+  };
 
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  if (unit >= a.n_units) return;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
+  // Work item number blockIdx.x in heaviest-bucket-first order (the plan kernel filled the buckets).
+  if (w == 0) {
+    const int c = a.bcount[kBuckets - 1 - l];            // lane l: bucket 63 - l
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (l >= off) incl += y;
+    }
+    const int rank = (int)blockIdx.x;
+    const uint64_t hit = __ballot(rank < incl);
+    const int lb = hit ? __ffsll((long long)hit) - 1 : 0;   // first lane whose prefix covers rank
+    const int before = __shfl(incl, lb, 64) - __shfl(c, lb, 64);
+    if (l == 0)
+      s_item = hit ? a.bitems[(size_t)(kBuckets - 1 - lb) * ((size_t)a.n_units * kMaxParts) + (rank - before)] : -1;
+  }
+  __syncthreads();
+  const int item = s_item;
+  if (item < 0) return;
+  const int part = item % kMaxParts;
+  const int unit = item / kMaxParts;
   const int cc = unit % a.nb;                      // active chunk == its own query block
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int64_t cglob = a.t_hist / kChunk + cc;    // global chunk id
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
+  // Wave w owns keys 32*(w&1) .. +31 and rows 32*(w>>1) .. +31 of every round; the
+  // two row halves are summed at the end.
   const int kh = w & 1, rh = w >> 1;
   const int key = 32 * kh + n;                     // this lane's key (operand-B column)
   const int64_t tok = cglob * kChunk + key;
+
+  const int np = a.flags[unit];
+  const int n_visits = a.nvis[unit];
+  for (int i = tid; i < n_visits; i += 256) {
+    const int v = a.vis[(int64_t)unit * a.nb + i];
+    vlist[i] = v & 0xFFFF;
+    vmask[i] = (uint32_t)v >> 16;
+  }
+  __syncthreads();
+  // This item's slice of the chunk's rounds (round r = attending block r / G, query head r % G).
+  const int rounds = G * n_visits;
+  const int r_lo = part * rounds / np, r_hi = (part + 1) * rounds / np;
 
   bf16x8 kf[KS], vf[KS];
   {
@@ -193,98 +364,171 @@ __global__ __launch_bounds__(256) void attend_bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   }
 
-  // Which later blocks selected groups of this chunk (bit u = group 8*cglob + u).
-  for (int i = tid; i < a.nb; i += 256) vmask[i] = 0u;
-  __syncthreads();
-  for (int jj = cc + 1 + w; jj < a.nb; jj += 4) {
-    const int32_t* g = a.gidx + ((int64_t)bh * a.nb + jj) * a.kg;
-    for (int i = l; i < a.kg; i += 64) {
-      const int64_t gid = g[i];
-      if (gid >= cglob * 8 && gid < cglob * 8 + 8) atomicOr(&vmask[jj], 1u << (int)(gid - cglob * 8));
-    }
-  }
-  __syncthreads();
+  const uint16_t* qg = (const uint16_t*)a.q;
+  const uint16_t* dg = (const uint16_t*)a.d_o;
+  auto round_row0 = [&](int r) __attribute__((always_inline)) -> int64_t {
+    const int jj = vlist[r / G];
+    const int hh = r % G;
+    return (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)jj * kQBlock;
+  };
+  // Round: the 64 rows of one query head of one attending block -> Q, dO tiles, LSE, D.
+  // Every wave copies the 64 LSE and D values itself (identical data), so that all
+  // waves issue the same number of copies per round.
+  auto issue = [&](int i, auto B) __attribute__((always_inline)) {
+    const int64_t row0 = round_row0(r_lo + i);
+    dma_tile<D, 4>(QB(B), [&](int rr) { return qg + (row0 + rr) * D; });
+    dma_tile<D, 4>(OB(B), [&](int rr) { return dg + (row0 + rr) * D; });
+    __builtin_amdgcn_global_load_lds((const void*)(a.lse + row0 + l), (lds_void_t*)LB(B), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(a.dvec + row0 + l), (lds_void_t*)RB(B), 4, 0, 0);
+  };
 
   const float c2 = a.scale * kLog2e;
   f32x16 dvacc[DT], dkacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) { dvacc[dt] = f32x16{}; dkacc[dt] = f32x16{}; }
 
-  for (int jj = cc; jj < a.nb; ++jj) {
-    const uint32_t mask = jj == cc ? 0xFFu : vmask[jj];
-    if (mask == 0u) continue;
-    for (int hh = 0; hh < G; ++hh) {
-      const int64_t qrow0 = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)jj * kQBlock;
-      const uint16_t* qp = (const uint16_t*)a.q + qrow0 * D;
-      const uint16_t* dp = (const uint16_t*)a.d_o + qrow0 * D;
-      for (int idx = tid; idx < 64 * CH; idx += 256) {
-        const int r = idx / CH, c = idx % CH;
-        const int off = r * D + 8 * swz_chunk<D>(r, c);
-        *reinterpret_cast<uint4*>(tq + off) = *reinterpret_cast<const uint4*>(qp + (int64_t)r * D + 8 * c);
-        *reinterpret_cast<uint4*>(tdo + off) = *reinterpret_cast<const uint4*>(dp + (int64_t)r * D + 8 * c);
-      }
-      if (tid < 64) {
-        slse[tid] = a.lse[qrow0 + tid] * kLog2e;
-        sdr[tid] = a.dvec[qrow0 + tid];
-      }
-      __syncthreads();
-
-      f32x16 s = {}, dpv = {};
+  auto compute = [&](int i, auto B) __attribute__((always_inline)) {
+    const uint16_t* tq = QB(B);
+    const uint16_t* tdo = OB(B);
+    const float* ls = LB(B);
+    const float* drv = RB(B);
+    const int vi = (r_lo + i) / G;
+    const bool own = vlist[vi] == cc;
+    const bool key_on = ((vmask[vi] >> (key >> 3)) & 1u) != 0u;
+    const RowReader<D> rowrd(32 * rh + rho(n));
+    const ColReader<D> colrd;
+    f32x16 s = {}, dpv = {};
+    {
+      // All row fragments first, then the MFMAs: the reads overlap each other and the
+      // first MFMAs instead of each read waiting out the LDS latency alone.
+      bf16x8 qa[KS], da[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(lds_row8<D>(tq, 32 * rh + rho(n), 16 * ks + 8 * h), kf[ks], s);
-        dpv = mfma32(lds_row8<D>(tdo, 32 * rh + rho(n), 16 * ks + 8 * h), vf[ks], dpv);
-      }
-      float p[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rh + out_row(r, h);
-        const bool valid = jj == cc ? key <= row : ((mask >> (key >> 3)) & 1u) != 0u;
-        p[r] = valid ? exp2f(s[r] * c2 - slse[row]) : 0.f;
-        ds[r] = p[r] * (dpv[r] - sdr[row]);
+        qa[ks] = rowrd(tq, 16 * ks + 8 * h);
+        da[ks] = rowrd(tdo, 16 * ks + 8 * h);
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pf = f32x8_to_bf16x8(p + 8 * ks);
-        const bf16x8 dsf = f32x8_to_bf16x8(ds + 8 * ks);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dvacc[dt] = mfma32(lds_col8<D>(tdo, 32 * rh + 16 * ks, 32 * dt), pf, dvacc[dt]);
-          dkacc[dt] = mfma32(lds_col8<D>(tq, 32 * rh + 16 * ks, 32 * dt), dsf, dkacc[dt]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(qa[ks], kf[ks], s);
+        dpv = mfma32(da[ks], vf[ks], dpv);
       }
-      __syncthreads();
+      // One batch: every read, then every MFMA.  (While copies into LDS are in flight
+      // the compiler can only wait for all outstanding LDS reads at once.)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
     }
-  }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {                 // rows 16ks .. 16ks+15 of the wave's 32
+      // Transposed fragments of dO and Q for these rows (independent of P: issued first).
+      bf16x8 fo[DT], fq[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        fo[dt] = colrd(tdo, 32 * rh + 16 * ks, 32 * dt);
+        fq[dt] = colrd(tq, 32 * rh + 16 * ks, 32 * dt);
+      }
+      // LSE and D of the 8 consecutive rows this lane holds (two 16-byte LDS reads each).
+      const int row0 = 32 * rh + 16 * ks + 8 * h;
+      const f32x4v l0 = *reinterpret_cast<const f32x4v*>(ls + row0);
+      const f32x4v l1 = *reinterpret_cast<const f32x4v*>(ls + row0 + 4);
+      const f32x4v d0 = *reinterpret_cast<const f32x4v*>(drv + row0);
+      const f32x4v d1 = *reinterpret_cast<const f32x4v*>(drv + row0 + 4);
+      float p[8], ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float lse = e < 4 ? l0[e & 3] : l1[e & 3];
+        const float dr = e < 4 ? d0[e & 3] : d1[e & 3];
+        const bool valid = own ? key <= row0 + e : key_on;
+        const float pe = fast_exp2(fmaf(s[8 * ks + e], c2, -lse * kLog2e));
+        p[e] = valid ? pe : 0.f;
+        ds[e] = p[e] * (dpv[8 * ks + e] - dr);
+      }
+      const bf16x8 pf = f32x8_to_bf16x8(p);
+      const bf16x8 dsf = f32x8_to_bf16x8(ds);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dvacc[dt] = mfma32(fo[dt], pf, dvacc[dt]);
+        dkacc[dt] = mfma32(fq[dt], dsf, dkacc[dt]);
+      }
+    }
+  };
 
-  // Sum the two row halves (waves 2,3 -> waves 0,1) through LDS, one tensor at a time.
-  float* red = reinterpret_cast<float*>(tqdo);   // 2 * 64 * D bf16 = room for 2 * DT * 16 * 64 floats
+  pipeline<3, 2 * dma_per_wave<D, 4>() + 2>(r_hi - r_lo, issue, compute);
+  __syncthreads();
+
+  // Sum the two row halves (waves 2,3 -> waves 0,1) through LDS, then write bf16 dK/dV
+  // (chunk done by one item) or this item's fp32 partial.
   const int64_t orow = (int64_t)bh * a.seg_len + (int64_t)cc * kChunk + key;
-  auto reduce_store = [&](f32x16 (&acc)[DT], void* dst, float sc) {
+  float* partial = a.parts + ((size_t)unit * kMaxParts + part) * (size_t)(2 * 64 * D);
+  float* red = reinterpret_cast<float*>(kh == 0 ? q0 : q1);   // per key half: DT*16*64 floats
+  static_assert(sizeof(q0) >= DT * 16 * 64 * sizeof(float), "reduction buffer");
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
     if (rh == 1) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[((kh * DT + dt) * 16 + r) * 64 + l] = acc[dt][r];
+        for (int e = 0; e < 16; ++e) red[(dt * 16 + e) * 64 + l] = which ? dkacc[dt][e] : dvacc[dt][e];
     }
     __syncthreads();
     if (rh == 0) {
-      uint16_t* out = (uint16_t*)dst + orow * D;
+      const float sc = which ? a.scale : 1.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float x[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = (acc[dt][4 * g + i] + red[((kh * DT + dt) * 16 + 4 * g + i) * 64 + l]) * sc;
+          for (int i = 0; i < 4; ++i)
+            x[i] = (which ? dkacc[dt][4 * g + i] : dvacc[dt][4 * g + i]) + red[(dt * 16 + 4 * g + i) * 64 + l];
           const int col = 32 * dt + 8 * g + 4 * h;
-          *reinterpret_cast<uint2*>(out + col) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+          if (np > 1) {
+            *reinterpret_cast<float4*>(partial + (size_t)which * 64 * D + (size_t)key * D + col) =
+                make_float4(x[0], x[1], x[2], x[3]);
+          } else {
+            uint16_t* out = (uint16_t*)(which ? a.dk : a.dv) + orow * D;
+            *reinterpret_cast<uint2*>(out + col) = f32x4_to_bf16x4_bits(x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc);
+          }
         }
     }
     __syncthreads();
-  };
-  reduce_store(dvacc, a.dv, 1.f);
-  reduce_store(dkacc, a.dk, a.scale);
+  }
+}
+
+// Sum the partials of chunks cut into several items, in item order, and write bf16
+// dK/dV.  Work-group (chunk, slice): rows 8*slice .. +7 of dV and dK (512 float4s,
+// two per thread); the loads of all partials are issued together.
+constexpr int kFinalizeSlices = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_bwd_dkdv_finalize_kernel(BwdArgs a) {
+  const int unit = blockIdx.x / kFinalizeSlices;
+  const int slice = blockIdx.x % kFinalizeSlices;
+  if (unit >= a.n_units) return;
+  const int np = a.flags[unit];
+  if (np <= 1) return;
+  const float* part0 = a.parts + (size_t)unit * kMaxParts * (2 * 64 * D);
+  const int cc = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int64_t orow0 = (int64_t)bh * a.seg_len + (int64_t)cc * kChunk;
+  constexpr int ROWS = 64 / kFinalizeSlices;
+  constexpr int PER = 2 * ROWS * D / 4 / 256;      // float4s per thread
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f4 = threadIdx.x + 256 * i;           // float4 index within the slice
+    const int which = f4 / (ROWS * D / 4);          // 0: dV, 1: dK
+    const int within = (f4 % (ROWS * D / 4)) * 4 + slice * ROWS * D;   // element in the 64 x D tensor
+    float4 x[kMaxParts];
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p)
+      if (p < np) x[p] = *reinterpret_cast<const float4*>(part0 + (size_t)p * (2 * 64 * D) + (size_t)which * 64 * D + within);
+    float4 acc = x[0];
+#pragma unroll
+    for (int p = 1; p < kMaxParts; ++p)
+      if (p < np) { acc.x += x[p].x; acc.y += x[p].y; acc.z += x[p].z; acc.w += x[p].w; }
+    const float sc = which ? a.scale : 1.f;
+    uint16_t* out = (uint16_t*)(which ? a.dk : a.dv) + (orow0 + within / D) * D + within % D;
+    *reinterpret_cast<uint2*>(out) = f32x4_to_bf16x4_bits(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+  }
 }
 
 // ---------------------------------------------------------------- fp32 (SIMT)
@@ -381,7 +625,9 @@ __global__ __launch_bounds__(256) void attend_bwd_dkdv_f32_kernel(BwdArgs a, int
 template <int D, int G>
 void launch_bf16(const BwdArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((attend_bwd_dq_bf16_kernel<D, G>), dim3(grid), dim3(128 * G), 0, s, a);
-  hipLaunchKernelGGL((attend_bwd_dkdv_bf16_kernel<D, G>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attend_bwd_plan_kernel<G>), dim3(a.n_units), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((attend_bwd_dkdv_bf16_kernel<D, G>), dim3(a.n_units * kMaxParts), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attend_bwd_dkdv_finalize_kernel<D>), dim3(a.n_units * kFinalizeSlices), dim3(256), 0, s, a);
 }
 template <int D>
 void launch_bf16_g(const BwdArgs& a, int G, int grid, hipStream_t s) {
@@ -396,8 +642,12 @@ void launch_bf16_g(const BwdArgs& a, int G, int grid, hipStream_t s) {
 }  // namespace
 
 size_t bwd_workspace_bytes(const Dims& d) {
+  // rowsum(dO*O) per query row, one flag per (sequence, KV head, active chunk), and
+  // G fp32 dK/dV partials per active chunk (bf16 path only).
   const size_t rows = (size_t)d.B * d.Hq * (size_t)d.seg_len;
-  return ((rows * sizeof(float)) + 255) & ~(size_t)255;
+  const size_t units = (size_t)d.B * d.Hkv * (size_t)d.nb;
+  const size_t parts = units * (size_t)kMaxParts * 2 * 64 * (size_t)d.D * sizeof(float);
+  return DkdvLayout::part_off(rows, units, (size_t)d.nb) + parts;
 }
 
 hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
@@ -407,6 +657,16 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o; a.lse = lse; a.gidx = group_idx;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dvec = (float*)workspace;
+  {
+    const size_t rows = (size_t)d.B * d.Hq * (size_t)d.seg_len;
+    const size_t units = (size_t)d.B * d.Hkv * (size_t)d.nb;
+    a.flags = (int*)((char*)workspace + DkdvLayout::flags_off(rows));
+    a.nvis = (int*)((char*)workspace + DkdvLayout::nvis_off(rows, units));
+    a.vis = (int*)((char*)workspace + DkdvLayout::vis_off(rows, units));
+    a.bcount = (int*)((char*)workspace + DkdvLayout::bcount_off(rows, units, (size_t)d.nb));
+    a.bitems = (int*)((char*)workspace + DkdvLayout::bitems_off(rows, units, (size_t)d.nb));
+    a.parts = (float*)((char*)workspace + DkdvLayout::part_off(rows, units, (size_t)d.nb));
+  }
   a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kg = d.kg; a.nb = d.nb; a.n_units = d.B * d.Hkv * d.nb;
   a.scale = d.scale;

@@ -26,6 +26,8 @@
 namespace hga {
 namespace {
 
+constexpr int kStages = 3;   // K/V tile buffer sets (tiles in flight + 1)
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -41,11 +43,22 @@ struct FwdArgs {
 template <int D, int G>
 __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = 128 * G;
+  constexpr int NW = 2 * G;
   constexpr int KS = D / 16;       // k-steps over the head dimension
   constexpr int DT = D / 32;       // 32-wide column tiles of O^T
-  __shared__ __align__(16) uint16_t tk[2][64 * D];
-  __shared__ __align__(16) uint16_t tv[2][64 * D];
+  // Four tile buffer sets as distinct arrays: the compiler can then see that reads
+  // of one never alias the asynchronous copies into another (3 tiles in flight).
+  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
+  __shared__ __align__(16) uint16_t k2[64 * D], v2[64 * D], k3[64 * D], v3[64 * D];
   __shared__ int sgid[512];
+  auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return k0; else if constexpr (B() == 1) return k1;
+    else if constexpr (B() == 2) return k2; else return k3;
+  };
+  auto VB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return v0; else if constexpr (B() == 1) return v1;
+    else if constexpr (B() == 2) return v2; else return v3;
+  };
 
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   if (unit >= a.n_units) return;
@@ -72,9 +85,19 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
 
-  TileLoader<D, NT> ld;
-  ld.load(kb, vb, 0, n_sel_tiles, n_valid, sgid, J);
-  ld.store(tk[0], tv[0]);
+  // Token of row r of tile t: selected tiles hold 8 groups, the last tile is the own
+  // chunk.  Rows past the selection read the own chunk's first token (masked later).
+  auto token = [&](int t, int r) __attribute__((always_inline)) -> int64_t {
+    if (t < n_sel_tiles) {
+      const int slot = 8 * t + (r >> 3);
+      return slot < n_valid ? (int64_t)kGroup * sgid[slot] + (r & 7) : (int64_t)kChunk * J;
+    }
+    return (int64_t)kChunk * J + r;
+  };
+  auto issue = [&](int t, auto B) __attribute__((always_inline)) {
+    dma_tile<D, NW>(KB(B), [&](int r) { return kb + token(t, r) * D; });
+    dma_tile<D, NW>(VB(B), [&](int r) { return vb + token(t, r) * D; });
+  };
 
   const float c2 = a.scale * kLog2e;
   float m2 = -INFINITY, lsum = 0.f;
@@ -82,43 +105,56 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) ld.load(kb, vb, t + 1, n_sel_tiles, n_valid, sgid, J);
-    __syncthreads();
-    const uint16_t* K = tk[buf];
-    const uint16_t* V = tv[buf];
-
-    // S^T for 64 keys: two 32-key subtiles.
+  auto compute = [&](int t, auto B) __attribute__((always_inline)) {
+    const uint16_t* K = KB(B);
+    const uint16_t* V = VB(B);
+    // S^T for 64 keys: two 32-key subtiles.  All K fragments are read in one batch,
+    // then the MFMAs run (while copies into LDS are in flight the compiler can only
+    // wait for all outstanding LDS reads at once).
     f32x16 s[2];
+    {
+      const RowReader<D> rd0(rho(n)), rd1(32 + rho(n));
+      bf16x8 kfr[2][KS];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
+      for (int ks = 0; ks < KS; ++ks) {
+        kfr[0][ks] = rd0(K, 16 * ks + 8 * h);
+        kfr[1][ks] = rd1(K, 16 * ks + 8 * h);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32(lds_row8<D>(K, 32 * kt + rho(n), 16 * ks + 8 * h), qf[ks], s[kt]);
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32(kfr[kt][ks], qf[ks], s[kt]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
     }
-    // Scale, mask, tile maximum.  Element r of subtile kt is key 32kt + out_row(r, h).
+    // Mask (only the own chunk and a partial last group tile need it), then the
+    // online softmax in the log2 domain: max of the raw scores, scaled once
+    // (scale > 0), and exp2(score * c2 - m) as one FMA per key.
     const bool local = t == n_sel_tiles;
-    const int kv_lim = local ? pos : 8 * (n_valid - 8 * t) - 1;   // last valid key index in the tile
+    const bool full = !local && 8 * (t + 1) <= n_valid;
+    if (!full) {
+      const int kv_lim = local ? pos : 8 * (n_valid - 8 * t) - 1;   // last valid key index
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kt + out_row(r, h) > kv_lim) s[kt][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + out_row(r, h);
-        const float x = key <= kv_lim ? s[kt][r] * c2 : -INFINITY;
-        s[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = wave_max32(mx);
-    const float m_new = fmaxf(m2, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m2 - m_new);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    const float m_new = fmaxf(m2, wave_max32(mx) * c2);   // finite: every row has a valid key
+    const float alpha = fast_exp2(m2 - m_new);
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = m_new == -INFINITY ? 0.f : exp2f(s[kt][r] - m_new);
+        const float p = fast_exp2(fmaf(s[kt][r], c2, -m_new));
         s[kt][r] = p;
         rs += p;
       }
@@ -127,19 +163,29 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
     m2 = m_new;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-
-    // O^T += V^T P^T over 4 k-steps of 16 keys.
+    // O^T += V^T P^T over 4 k-steps of 16 keys (V^T fragments read as two batches).
+    const ColReader<D> colrd;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float pv[8];
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 vfr[2][DT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = s[ks >> 1][8 * (ks & 1) + e];
-      const bf16x8 pf = f32x8_to_bf16x8(pv);
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(lds_col8<D>(V, 16 * ks, 32 * dt), pf, oacc[dt]);
+        for (int dt = 0; dt < DT; ++dt) vfr[k2][dt] = colrd(V, 16 * (2 * half + k2), 32 * dt);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int ks = 2 * half + k2;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = s[ks >> 1][8 * (ks & 1) + e];
+        const bf16x8 pf = f32x8_to_bf16x8(pv);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(vfr[k2][dt], pf, oacc[dt]);
+      }
     }
-    if (t + 1 < n_tiles) ld.store(tk[buf ^ 1], tv[buf ^ 1]);
-  }
+  };
+
+  pipeline<kStages, 2 * dma_per_wave<D, NW>()>(n_tiles, issue, compute);
 
   // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
   const float inv = 1.f / lsum;
@@ -149,9 +195,8 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int col = 32 * dt + 8 * g + 4 * h;
-      *reinterpret_cast<uint2*>(op + col) =
-          make_uint2(pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
-                     pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv));
+      *reinterpret_cast<uint2*>(op + col) = f32x4_to_bf16x4_bits(
+          oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
     }
   if (h == 0) a.lse[qrow] = (m2 + log2f(lsum)) * kLn2;
 }

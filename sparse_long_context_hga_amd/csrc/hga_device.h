@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hga {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -31,14 +33,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Hardware round-to-nearest-even conversions (v_cvt_pk_bf16_f32), for the hot loops.
 __device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const float* x) {
-  uint4 u;
-  u.x = pack_bf16x2(x[0], x[1]);
-  u.y = pack_bf16x2(x[2], x[3]);
-  u.z = pack_bf16x2(x[4], x[5]);
-  u.w = pack_bf16x2(x[6], x[7]);
-  return __builtin_bit_cast(bf16x8, u);
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
 }
+__device__ __forceinline__ uint2 f32x4_to_bf16x4_bits(float a, float b, float c, float d) {
+  const f32x4v v = {a, b, c, d};
+  return __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
+}
+// 2^x on the transcendental unit (inputs are softmax exponents <= 0; -inf gives 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------- orderable score keys
 // Monotone map float -> uint32 (larger float -> larger key); -0 and +0 share a key.
@@ -135,6 +144,62 @@ __device__ __forceinline__ bf16x8 lds_col8(const uint16_t* tile, int row0, int c
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Swizzle term of tile row r (depends on r % 16 only).
+template <int D>
+__device__ __forceinline__ int swz_f(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+
+// A per-lane value the compiler must treat as freshly computed: addresses derived
+// from it are rebuilt where they are used instead of being hoisted out of the
+// tile loop, each one pinning a register for the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Row-fragment reader for one lane: rows `row` (fixed per lane) of a swizzled
+// tile, 8 columns at a time.
+template <int D>
+struct RowReader {
+  int base, f;   // element offset of the row, swizzle term
+  __device__ __forceinline__ RowReader(int row) {
+    const int r = opaque(row);
+    base = r * D;
+    f = swz_f<D>(r);
+  }
+  __device__ __forceinline__ bf16x8 operator()(const uint16_t* tile, int col) const {
+    return *reinterpret_cast<const bf16x8*>(tile + base + 8 * ((col >> 3) ^ f));
+  }
+};
+
+// Transposing fragment reader (see lds_col8) for row blocks starting at a multiple
+// of 16: lane-constant parts precomputed once per use site.
+template <int D>
+struct ColReader {
+  int rr, cc, f0, f1;
+  __device__ __forceinline__ ColReader() {
+    const int l = opaque(threadIdx.x & 63);
+    const int grp = l >> 4, s = l & 15;
+    rr = 8 * (grp >> 1) + (s >> 2);
+    cc = 16 * (grp & 1) + 4 * (s & 3);
+    f0 = swz_f<D>(rr);
+    f1 = swz_f<D>(rr + 4);
+  }
+  // column col0 + (l % 32) of rows row0 + 8 (l / 32) .. +7; row0 % 16 == 0, col0 % 32 == 0
+  __device__ __forceinline__ bf16x8 operator()(const uint16_t* tile, int row0, int col0) const {
+    const int c = (col0 + cc) >> 3, sub = cc & 7;
+    const uint16_t* p0 = tile + (row0 + rr) * D + 8 * (c ^ f0) + sub;
+    const uint16_t* p1 = tile + (row0 + rr + 4) * D + 8 * (c ^ f1) + sub;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -167,50 +232,89 @@ __device__ __forceinline__ int count_valid(const int32_t* g, int kg, int* sgid) 
   return nv;
 }
 
-// Global -> register -> LDS staging of one 64-token K (and V) tile.
-template <int D, int NT>
-struct TileLoader {
-  static constexpr int CH = D / 8;                 // 16-byte chunks per row
-  static constexpr int NCH = 64 * CH;               // chunks per tensor tile
-  static constexpr int LPT = (NCH + NT - 1) / NT;   // chunks per thread per tensor
-  uint4 rk[LPT], rv[LPT];
+// Copies per wave of one dma_tile call when NW waves share it (waves beyond the
+// tile's D/8 blocks issue none).
+template <int D, int NW>
+constexpr int dma_per_wave() { return (D / 8) >= NW ? (D / 8) / NW : 1; }
 
-  // Token of tile row r: selected tiles map 8 groups, the last tile is the own chunk.
-  __device__ __forceinline__ int64_t token(int t, int n_sel_tiles, int n_valid, const int* sgid,
-                                           int J, int r) const {
-    if (t < n_sel_tiles) {
-      const int slot = 8 * t + (r >> 3);
-      return slot < n_valid ? (int64_t)kGroup * sgid[slot] + (r & 7) : -1;
-    }
-    return (int64_t)kChunk * J + r;
-  }
-  __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb, int t, int n_sel_tiles,
-                                       int n_valid, const int* sgid, int J) {
+// Asynchronous global -> LDS copy of one 64-row tile into the swizzled layout
+// (global_load_lds_dwordx4: lane L of a wave writes the 16 bytes it loaded to
+// LDS base + 16 L).  The tile is 64*D*2 bytes = D/8 blocks of 1 KiB; the NW waves
+// split the blocks, and each lane fetches the logical chunk that belongs at its
+// physical slot (the swizzle is an involution).  row_src(r) is the global address
+// of tile row r.  Completion: s_waitcnt vmcnt(0) of the issuing wave, then a barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int D, int NW, typename RowSrc>
+__device__ __forceinline__ void dma_tile(uint16_t* tile, const RowSrc& row_src) {
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int RPB = 64 / CH;       // rows per 1 KiB block
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      const int r = idx / CH, c = idx % CH;
-      const int64_t tok = idx < NCH ? token(t, n_sel_tiles, n_valid, sgid, J, r) : -1;
-      if (tok >= 0) {
-        rk[i] = *reinterpret_cast<const uint4*>(kb + tok * D + 8 * c);
-        rv[i] = *reinterpret_cast<const uint4*>(vb + tok * D + 8 * c);
-      } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
+  for (int bi = w; bi < CH; bi += NW) {
+    const int r = RPB * bi + l / CH;
+    const int c = swz_chunk<D>(r, l % CH);
+    __builtin_amdgcn_global_load_lds((const void*)(row_src(r) + 8 * c), (lds_void_t*)(tile + 512 * bi), 16, 0, 0);
+  }
+}
+
+// Wait until every global->LDS copy issued by this wave has landed.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+// s_waitcnt vmcnt(N) for a compile-time N (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Software pipeline over n tiles with NBUF buffer sets and NBUF-1 tiles in flight.
+// issue(t, ic<B>) starts the asynchronous copies of tile t into buffer set B;
+// compute(t, ic<B>) consumes buffer set B.  Every wave issues exactly L copies
+// per tile (or none at all), so "tile t has landed" is vmcnt(L * tiles issued
+// after t).  Buffer sets must be distinct LDS arrays chosen at compile time: the
+// compiler then knows that reading one set never aliases copies into another
+// and adds no wait of its own.  One barrier per tile: before tile t+NBUF-1 is
+// issued into the set of tile t-1, every wave has finished computing tile t-1.
+template <int NBUF, int L, typename Issue, typename Compute>
+__device__ __forceinline__ void pipeline(int n, Issue&& issue, Compute&& compute) {
+  static_assert(NBUF >= 2 && NBUF <= 4, "2 to 4 buffer sets");
+  constexpr int P = NBUF - 1;
+  static_for<0, P>([&](auto B) {
+    if (B() < n) issue(B(), B);
+  });
+  for (int t0 = 0; t0 < n; t0 += NBUF) {
+    static_for<0, NBUF>([&](auto B) {
+      const int t = t0 + B();
+      if (t < n) {
+        const int ahead = min(P - 1, n - 1 - t);       // tiles already issued after t
+        if constexpr (P >= 3) {
+          if (ahead >= 2) wait_vmcnt<2 * L>();
+          else if (ahead == 1) wait_vmcnt<L>();
+          else wait_vmcnt<0>();
+        } else if constexpr (P == 2) {
+          if (ahead >= 1) wait_vmcnt<L>();
+          else wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (t + P < n) issue(t + P, ic<(B() + P) % NBUF>{});
+        compute(t, B);
       }
-    }
+    });
   }
-  __device__ __forceinline__ void store(uint16_t* tk, uint16_t* tv) const {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      if (NCH % NT != 0 && idx >= NCH) continue;
-      const int r = idx / CH, c = idx % CH;
-      const int off = r * D + 8 * swz_chunk<D>(r, c);
-      *reinterpret_cast<uint4*>(tk + off) = rk[i];
-      *reinterpret_cast<uint4*>(tv + off) = rv[i];
-    }
-  }
-};
+}
 
 }  // namespace hga

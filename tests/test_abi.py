@@ -102,7 +102,7 @@ def test_attend_validation(L):
     assert fw(ctypes.byref(s), A, A, A, 16384, 14336, 4096, A, A, A, None) == -4
     assert fw(ctypes.byref(s), A, A, M, 16384, 14336, 2048, A, A, A, None) == -5
     need = hga.hga_attend_bwd_workspace_size(s, 14336, 2048)
-    assert need == 32 * 2048 * 4
+    assert need >= 32 * 2048 * 4 and need % 256 == 0
     bw = L.hga_attend_bwd
     args = [A, A, A, A, A, A, 16384, 14336, 2048, A, A, A, A]
     assert bw(ctypes.byref(s), *args, A, need - 1, None) == -6
