@@ -70,10 +70,12 @@ __device__ __forceinline__ float dot8_bf16(bf16x8 x, bf16x8 y) {
 }
 
 // ---------------------------------------------------------------- dQ (bf16)
-template <int D, int G>
-__global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) {
-  constexpr int NT = 128 * G;
-  constexpr int NW = 2 * G;
+// HPW query heads of the G sharing a KV head per work-group (as in the forward).
+template <int D, int G, int HPW>
+__global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1)
+void attend_bwd_dq_bf16_kernel(BwdArgs a) {
+  constexpr int NT = 128 * HPW;
+  constexpr int NW = 2 * HPW;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
@@ -88,14 +90,15 @@ __global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) 
     else if constexpr (B() == 2) return v2; else return v3;
   };
 
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  if (unit >= a.n_units) return;
+  const int item = xcd_unit(blockIdx.x, gridDim.x);
+  if (item >= a.n_units * (G / HPW)) return;
+  const int unit = item / (G / HPW);
   const int j = unit % a.nb;
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int J = (int)(a.t_hist / kChunk) + j;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
-  const int hh = w >> 1;
+  const int hh = (item % (G / HPW)) * HPW + (w >> 1);
   const int pos = 32 * (w & 1) + n;
   const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
   const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bh * a.t_cap * D;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) 
   }
   const float Dr = wave_sum32(dpart);
   if (h == 0) a.dvec[qrow] = Dr;
-  if (unit == 0 && tid < kBuckets) a.bcount[tid] = 0;   // work-list counters for the plan kernel
+  if (item == 0 && tid < kBuckets) a.bcount[tid] = 0;   // work-list counters for the plan kernel
   const float lse2 = a.lse[qrow] * kLog2e;
 
   const int n_valid = count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid);
@@ -173,6 +176,7 @@ __global__ __launch_bounds__(128 * G) void attend_bwd_dq_bf16_kernel(BwdArgs a) 
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) kt_fr[half][dt] = colrd(K, 32 * kt + 16 * half, 32 * dt);
+
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -624,7 +628,9 @@ __global__ __launch_bounds__(256) void attend_bwd_dkdv_f32_kernel(BwdArgs a, int
 
 template <int D, int G>
 void launch_bf16(const BwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attend_bwd_dq_bf16_kernel<D, G>), dim3(grid), dim3(128 * G), 0, s, a);
+  constexpr int HPW = G >= 8 ? 4 : G;   // query heads per dQ work-group
+  hipLaunchKernelGGL((attend_bwd_dq_bf16_kernel<D, G, HPW>), dim3(xcd_grid(a.n_units * (G / HPW))),
+                     dim3(128 * HPW), 0, s, a);
   hipLaunchKernelGGL((attend_bwd_plan_kernel<G>), dim3(a.n_units), dim3(64), 0, s, a);
   hipLaunchKernelGGL((attend_bwd_dkdv_bf16_kernel<D, G>), dim3(a.n_units * kMaxParts), dim3(256), 0, s, a);
   hipLaunchKernelGGL((attend_bwd_dkdv_finalize_kernel<D>), dim3(a.n_units * kFinalizeSlices), dim3(256), 0, s, a);

@@ -40,10 +40,15 @@ struct FwdArgs {
   float scale;
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NT = 128 * G;
-  constexpr int NW = 2 * G;
+// HPW query heads of the G sharing a KV head per work-group (2 waves of 32 rows each);
+// the G / HPW work-groups of a unit gather the same tiles (the repeats hit L2: their
+// ids are consecutive, hence on one XCD) but run unsynchronised, so one group's
+// softmax overlaps another's MFMAs on the same CU.
+template <int D, int G, int HPW>
+__global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) void attend_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NT = 128 * HPW;
+  constexpr int NW = 2 * HPW;
+  constexpr int kStagesHere = HPW == G ? kStages : 2;
   constexpr int KS = D / 16;       // k-steps over the head dimension
   constexpr int DT = D / 32;       // 32-wide column tiles of O^T
   // Four tile buffer sets as distinct arrays: the compiler can then see that reads
@@ -60,14 +65,15 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
     else if constexpr (B() == 2) return v2; else return v3;
   };
 
-  const int unit = xcd_unit(blockIdx.x, gridDim.x);
-  if (unit >= a.n_units) return;
+  const int item = xcd_unit(blockIdx.x, gridDim.x);
+  if (item >= a.n_units * (G / HPW)) return;
+  const int unit = item / (G / HPW);
   const int j = unit % a.nb;
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int J = (int)(a.t_hist / kChunk) + j;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
-  const int hh = w >> 1;                  // query head within the KV group
+  const int hh = (item % (G / HPW)) * HPW + (w >> 1);   // query head within the KV group
   const int pos = 32 * (w & 1) + n;       // this lane's query position in the block
   const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
 
@@ -147,22 +153,29 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    const float m_new = fmaxf(m2, wave_max32(mx) * c2);   // finite: every row has a valid key
-    const float alpha = fast_exp2(m2 - m_new);
+    mx = wave_max32(mx) * c2;   // finite: every row has a valid key in every tile
+    // The running maximum only moves when a tile exceeds it by more than 2^8: P stays
+    // below 256 and the rescale of O (64 multiplies) is skipped in almost every tile.
+    // O and the normaliser share the maximum, so the result is unchanged.
+    const bool grow = mx > m2 + 8.f;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mx : m2;
+      const float alpha = fast_exp2(m2 - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m2 = m_new;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kt][r], c2, -m_new));
+        const float p = fast_exp2(fmaf(s[kt][r], c2, -m2));
         s[kt][r] = p;
         rs += p;
       }
-    rs = wave_sum32(rs);
-    lsum = lsum * alpha + rs;
-    m2 = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    lsum += wave_sum32(rs);
     // O^T += V^T P^T over 4 k-steps of 16 keys (V^T fragments read as two batches).
     const ColReader<D> colrd;
 #pragma unroll
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(128 * G) void attend_fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  pipeline<kStages, 2 * dma_per_wave<D, NW>()>(n_tiles, issue, compute);
+  pipeline<kStagesHere, 2 * dma_per_wave<D, NW>()>(n_tiles, issue, compute);
 
   // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
   const float inv = 1.f / lsum;
@@ -250,7 +263,10 @@ __global__ __launch_bounds__(512) void attend_fwd_f32_kernel(FwdArgs a, int G) {
 
 template <int D, int G>
 void launch_bf16(const FwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attend_fwd_bf16_kernel<D, G>), dim3(grid), dim3(128 * G), 0, s, a);
+  constexpr int HPW = G >= 8 ? 4 : G;   // query heads per work-group
+  (void)grid;
+  hipLaunchKernelGGL((attend_fwd_bf16_kernel<D, G, HPW>), dim3(xcd_grid(a.n_units * (G / HPW))),
+                     dim3(128 * HPW), 0, s, a);
 }
 template <int D>
 void launch_bf16_g(const FwdArgs& a, int G, int grid, hipStream_t s) {
