@@ -39,9 +39,14 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
                    choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k"])
+    p.add_argument("--mark-every", type=int, default=8,
+                   help="put per-kernel timing marks on every N-th timed step (default 8)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
-                   help="also run one device copy of this size first (reference for HBM counters)")
+                   help="first run a fill and a scale-copy kernel of this size (reference for HBM counters)")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                        "WRITE_SIZE) of a --copy-calibration-mib run into the traffic summary under profiles/")
     return p.parse_args()
 
 
@@ -92,7 +97,91 @@ def algorithmic_work(w, gidx):
         "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops},
         "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops},
         "attend_bwd_dkdv": {"bytes": dkdv_bytes, "flops": dkdv_flops},
+        # the selection inverse reads group_idx; the partial sums are not part of the method
+        "attend_bwd_plan": {"bytes": float(gidx.size * 4), "flops": 0.0},
+        "attend_bwd_finalize": {"bytes": 0.0, "flops": 0.0},
     }
+
+
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "hga_step_ctx16k_hbm_traffic.json")
+CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
+# kernel-name prefix -> step kernel (first match wins)
+KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_", "route"), ("attend_fwd_", "attend_fwd"),
+               ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_plan_", "attend_bwd_plan"),
+               ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv")]
+
+
+def _short_name(name):
+    import re
+    name = name.replace("void ", "").replace("hga::(anonymous namespace)::", "")
+    return re.split(r"\((?!anonymous)", name, maxsplit=1)[0]
+
+
+def traffic_summary(fetch_csv, write_csv, calib_mib, workload):
+    """Per-launch HBM bytes of each step kernel from two counter passes.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by the factor
+    that makes the calibration scale-copy kernel (torch.mul of `calib_mib` MiB
+    of fp32; reads and writes exactly that many bytes) read its known size.
+    For each kernel the count over the step dispatches is averaged (the history
+    summaries, built once outside the step, are a different grid and dropped)."""
+    import csv
+    import collections
+    n = calib_mib * (1 << 20)
+    out = {"workload": workload, "source_sha256": kernel_source_digest(), "calibration_bytes": n,
+           "kernels": {}}
+    per = {}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = list(csv.DictReader(open(path)))
+        calib = [float(r["Counter_Value"]) * 1024 for r in rows if "AUnaryFunctor" in r["Kernel_Name"]]
+        if len(calib) != 1:
+            raise SystemExit(f"{path}: expected one calibration scale-copy dispatch, found {len(calib)}")
+        factor = n / calib[0]
+        out[f"{label}_factor"] = round(factor, 5)
+        groups = collections.defaultdict(list)
+        for r in rows:
+            short = _short_name(r["Kernel_Name"])
+            key = next((k for pre, k in KERNEL_KEYS if short.startswith(pre)), None)
+            if key is not None:
+                groups[(key, r["Grid_Size"])].append(float(r["Counter_Value"]) * 1024 * factor)
+        for (key, _grid), vals in groups.items():
+            prev = per.get((key, label))
+            if prev is None or len(vals) > len(prev):          # the step's dispatches are the most frequent
+                per[(key, label)] = vals
+    for (key, label), vals in sorted(per.items()):
+        k = out["kernels"].setdefault(key, {})
+        k[f"{label}_bytes_per_launch"] = round(statistics.mean(vals))
+        k["launches"] = len(vals)
+    for k in out["kernels"].values():
+        k["hbm_bytes_per_launch"] = k.get("fetch_bytes_per_launch", 0) + k.get("write_bytes_per_launch", 0)
+    return out
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources: counter figures are only valid for this exact code."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if not name.endswith((".hip", ".h")):
+            continue
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when no
+    summary exists for this workload or the kernels changed since it was taken."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            summ = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if summ.get("workload") != workload or summ.get("source_sha256") != kernel_source_digest():
+        return None
+    k = summ.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def make_workload(name):
@@ -135,6 +224,14 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=5):
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.traffic_summary:
+        if not args.copy_calibration_mib:
+            raise SystemExit("--traffic-summary needs the --copy-calibration-mib of the profiled run")
+        summ = traffic_summary(*args.traffic_summary, args.copy_calibration_mib, args.workload)
+        with open(PMC_SUMMARY, "w") as f:
+            json.dump(summ, f, indent=1)
+        print(json.dumps(summ, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the HGA layer path has no multi-GPU mode "
               "(sharding is by sequence and KV head, see the design notes).", file=sys.stderr)
@@ -159,57 +256,82 @@ def main():
                         dev(w.d_o) if w.d_o is not None else None)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20)
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")   # fill kernel: writes n bytes
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)                                     # reads n bytes, writes n bytes
         torch.cuda.synchronize()
+        print(f"[bench] calibration: fill then scale-copy of {n} bytes", file=sys.stderr, flush=True)
         del src, dst
     L.summaries(0, w.t_hist)                                  # history summaries: built once, untimed
     torch.cuda.synchronize()
 
-    calls = [
-        ("summaries", lambda: L.summaries(w.t_hist, w.t_hist + w.seg_len)),
-        ("route", L.route),
-        ("attend_fwd", L.fwd),
-        ("attend_bwd", L.bwd),
-    ]
-    for _ in range(args.warmup):
-        for _, f in calls:
-            f()
+    # Timed region: K steps.  Every `--mark-every`-th step carries HIP timing marks on the
+    # stream the library launches on: events between the calls, and the backward's own
+    # kernels timed from their dispatches.  Marks cost GPU time, so the other steps carry none.
+    stream = torch.cuda.current_stream()
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    n_bwd = hga.HGA_BWD_KERNELS
+    marked = list(range(0, args.steps, max(1, args.mark_every)))
+    ev = {i: [mk() for _ in range(4)] for i in marked}             # summaries | route | fwd | end
+    bev = {i: [mk() for _ in range(2 * n_bwd)] for i in marked}    # backward kernels
+    for e in [x for i in marked for x in ev[i] + bev[i]]:
+        e.record(stream)                                            # torch creates the HIP event here
     torch.cuda.synchronize()
 
-    # Timed region: K steps; events between the calls on the stream the library launches on.
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    def step(i):
+        se, be = ev.get(i), bev.get(i)
+        if se: se[0].record(stream)
+        L.summaries(w.t_hist, w.t_hist + w.seg_len)
+        if se: se[1].record(stream)
+        L.route()
+        if se: se[2].record(stream)
+        L.fwd()
+        if se: se[3].record(stream)
+        if L.do is not None:
+            L.bwd(events=be)
+
+    for i in range(args.warmup):
+        step(-1 - i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, (_, f) in enumerate(calls):
-            f()
-            ev[s][i + 1].record(stream)
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call = {name: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps))
-                for i, (name, _) in enumerate(calls)}
-    step_ms_events = statistics.mean(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps))
     ms_per_step = wall * 1e3 / args.steps
+    avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
+    kern_ms = {
+        "summaries": avg((ev[i][0], ev[i][1]) for i in marked),
+        "route": avg((ev[i][1], ev[i][2]) for i in marked),
+        "attend_fwd": avg((ev[i][2], ev[i][3]) for i in marked),
+    }
+    if L.do is not None:
+        for k, name in enumerate(("attend_bwd_dq", "attend_bwd_plan", "attend_bwd_dkdv", "attend_bwd_finalize")):
+            kern_ms[name] = avg((bev[i][2 * k], bev[i][2 * k + 1]) for i in marked)
 
     gidx = L.gidx.cpu().numpy()
     work = algorithmic_work(w, gidx)
-    kern_ms = {"summaries": per_call["summaries"], "route": per_call["route"],
-               "attend_fwd": per_call["attend_fwd"], "attend_bwd": per_call["attend_bwd"]}
-    work["attend_bwd"] = {"bytes": work["attend_bwd_dq"]["bytes"] + work["attend_bwd_dkdv"]["bytes"],
-                          "flops": work["attend_bwd_dq"]["flops"] + work["attend_bwd_dkdv"]["flops"]}
     kernels = {}
     for k, ms in kern_ms.items():
-        wk = work[k]
-        kernels[k] = {"ms": round(ms, 5), "GB/s": round(wk["bytes"] / (ms * 1e-3) / 1e9, 1),
-                      "TFLOP/s": round(wk["flops"] / (ms * 1e-3) / 1e12, 2)}
-    dom = max(("attend_fwd", "attend_bwd", "route"), key=lambda k: kern_ms[k])
-    ach = work[dom]["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+        wk = work.get(k, {"bytes": 0.0, "flops": 0.0})
+        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+        tfl = wk["flops"] / (ms * 1e-3) / 1e12
+        kernels[k] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "TFLOP/s": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
+    dom = max(kern_ms, key=lambda k: kern_ms[k])
+    wk = work.get(dom, {"bytes": 0.0, "flops": 0.0})
+    intensity = wk["flops"] / max(wk["bytes"], 1.0)
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity >= ridge:
+        ach = wk["flops"] / (kern_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = wk["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roofline["traffic"] = measured_traffic(dom, w.name)
+    roofline["kernel"] = dom
 
     tokens = w.batch * w.seg_len
     out = {
@@ -223,7 +345,8 @@ def main():
                    "top_groups": w.top_groups, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
-        "step_ms_events": round(step_ms_events, 5),
+        "kernel_timing": f"HIP events on {len(marked)} of the {args.steps} timed steps; backward kernels "
+                         f"timed from their dispatches, the other calls between events on the stream",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

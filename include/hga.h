@@ -172,6 +172,23 @@ int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache,
                    void* dq, void* dk_active, void* dv_active, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/*
+ * hga_attend_bwd_timed -- hga_attend_bwd, plus per-kernel timing marks: for
+ * kernel i of the backward (HGA_BWD_KERNELS of them, in launch order: 0 dQ and
+ * rowsum(dO*O), 1 selection inverse / work list, 2 dK/dV, 3 dK/dV partial sums)
+ * events[2i] is recorded on `stream` just before its launch and events[2i+1] just
+ * after; a kernel that a dtype's path does not launch (the fp32 path has no
+ * work list and no partial sums) gets its two marks back to back.  events:
+ * 2*HGA_BWD_KERNELS hipEvent_t handles created by the caller (NULL entries are
+ * skipped).  Everything else as hga_attend_bwd.
+ */
+#define HGA_BWD_KERNELS 4
+int hga_attend_bwd_timed(const hga_shape* shape, const void* q, const void* k_cache,
+                         const void* v_cache, const void* o, const float* lse, const void* d_o,
+                         int64_t t_cap, int64_t t_hist, int64_t seg_len, const int32_t* group_idx,
+                         void* dq, void* dk_active, void* dv_active, void* workspace,
+                         size_t workspace_bytes, void* const* events, void* stream);
+
 /* Static description of a status code. */
 const char* hga_status_string(int status);
 

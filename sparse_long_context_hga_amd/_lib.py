@@ -59,6 +59,8 @@ SIGNATURES = {
     "hga_attend_bwd_workspace_size": (ctypes.c_size_t, [_SHAPE, _I64, _I64]),
     "hga_attend_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                       _P, ctypes.c_size_t, _P]),
+    "hga_attend_bwd_timed": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
+                                            _P, ctypes.c_size_t, _P, _P]),
     "hga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -130,6 +132,27 @@ def hga_attend_bwd(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_cap: int
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(d_o),
         t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(dq), _ptr(dk_active), _ptr(dv_active),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+HGA_BWD_KERNELS = 4
+
+
+def hga_attend_bwd_timed(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_cap: int, t_hist: int,
+                         seg_len: int, group_idx, dq, dk_active, dv_active, workspace: torch.Tensor,
+                         events, stream=None) -> None:
+    """hga_attend_bwd with torch.cuda.Event pairs recorded around each of its kernels
+    (events[2i], events[2i+1] for kernel i; None entries are skipped)."""
+    if len(events) != 2 * HGA_BWD_KERNELS:
+        raise ValueError(f"need {2 * HGA_BWD_KERNELS} events, got {len(events)}")
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record(stream if stream is not None else torch.cuda.current_stream())  # creates it
+    handles = (ctypes.c_void_p * (2 * HGA_BWD_KERNELS))(
+        *[None if e is None else ctypes.c_void_p(e.cuda_event) for e in events])
+    _check("hga_attend_bwd_timed", lib().hga_attend_bwd_timed(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(d_o),
+        t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(dq), _ptr(dk_active), _ptr(dv_active),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), handles, _stream(stream)))
 
 
 def hga_status_string(status: int) -> str:

@@ -19,6 +19,8 @@
 //    block's Q / dO rows per query head in swizzled LDS, and accumulates dK, dV
 //    in fp32 registers (dV^T += dO^T P, dK^T += Q^T dS, with the transposing
 //    LDS reads supplying the k-contiguous operands).
+#include <hip/hip_ext.h>
+
 #include "hga_device.h"
 #include "hga_internal.h"
 
@@ -626,22 +628,40 @@ __global__ __launch_bounds__(256) void attend_bwd_dkdv_f32_kernel(BwdArgs a, int
   for (int e = 0; e < DQ; ++e) { dko[e] = dk[e] * a.scale; dvo[e] = dv[e]; }
 }
 
+// Launches kernel i of the backward; with timing events, its start and stop
+// timestamps are taken from the dispatch itself (no extra packets in the stream).
+struct Launcher {
+  const hipEvent_t* ev;
+  hipStream_t s;
+  template <typename... KA, typename... A>
+  void operator()(int i, void (*kernel)(KA...), dim3 grid, dim3 block, A... args) const {
+    if (ev && (ev[2 * i] || ev[2 * i + 1]))
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev[2 * i], ev[2 * i + 1], 0, args...);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+  // a kernel that this path does not need: both marks back to back
+  void skip(int i) const {
+    if (ev && ev[2 * i]) hipEventRecord(ev[2 * i], s);
+    if (ev && ev[2 * i + 1]) hipEventRecord(ev[2 * i + 1], s);
+  }
+};
+
 template <int D, int G>
-void launch_bf16(const BwdArgs& a, int grid, hipStream_t s) {
+void launch_bf16(const BwdArgs& a, const Launcher& run) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per dQ work-group
-  hipLaunchKernelGGL((attend_bwd_dq_bf16_kernel<D, G, HPW>), dim3(xcd_grid(a.n_units * (G / HPW))),
-                     dim3(128 * HPW), 0, s, a);
-  hipLaunchKernelGGL((attend_bwd_plan_kernel<G>), dim3(a.n_units), dim3(64), 0, s, a);
-  hipLaunchKernelGGL((attend_bwd_dkdv_bf16_kernel<D, G>), dim3(a.n_units * kMaxParts), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((attend_bwd_dkdv_finalize_kernel<D>), dim3(a.n_units * kFinalizeSlices), dim3(256), 0, s, a);
+  run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))), dim3(128 * HPW), a);
+  run(1, attend_bwd_plan_kernel<G>, dim3(a.n_units), dim3(64), a);
+  run(2, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
+  run(3, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
 }
 template <int D>
-void launch_bf16_g(const BwdArgs& a, int G, int grid, hipStream_t s) {
+void launch_bf16_g(const BwdArgs& a, int G, const Launcher& run) {
   switch (G) {
-    case 1: launch_bf16<D, 1>(a, grid, s); break;
-    case 2: launch_bf16<D, 2>(a, grid, s); break;
-    case 4: launch_bf16<D, 4>(a, grid, s); break;
-    default: launch_bf16<D, 8>(a, grid, s); break;
+    case 1: launch_bf16<D, 1>(a, run); break;
+    case 2: launch_bf16<D, 2>(a, run); break;
+    case 4: launch_bf16<D, 4>(a, run); break;
+    default: launch_bf16<D, 8>(a, run); break;
   }
 }
 
@@ -659,7 +679,8 @@ size_t bwd_workspace_bytes(const Dims& d) {
 hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* d_o,
                              const int32_t* group_idx, void* dq, void* dk, void* dv,
-                             void* workspace, hipStream_t s) {
+                             void* workspace, hipStream_t s, const hipEvent_t* events) {
+  const Launcher run{events, s};
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o; a.lse = lse; a.gidx = group_idx;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dvec = (float*)workspace;
@@ -678,16 +699,16 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   a.scale = d.scale;
   const int grid = xcd_grid(a.n_units);
   if (bf16) {
-    if (d.D == 128) launch_bf16_g<128>(a, d.G, grid, s);
-    else launch_bf16_g<64>(a, d.G, grid, s);
+    if (d.D == 128) launch_bf16_g<128>(a, d.G, run);
+    else launch_bf16_g<64>(a, d.G, run);
   } else {
-    if (d.D == 128) {
-      hipLaunchKernelGGL((attend_bwd_dq_f32_kernel<128>), dim3(grid), dim3(64 * d.G), 0, s, a, d.G);
-      hipLaunchKernelGGL((attend_bwd_dkdv_f32_kernel<128>), dim3(grid), dim3(256), 0, s, a, d.G);
-    } else {
-      hipLaunchKernelGGL((attend_bwd_dq_f32_kernel<64>), dim3(grid), dim3(64 * d.G), 0, s, a, d.G);
-      hipLaunchKernelGGL((attend_bwd_dkdv_f32_kernel<64>), dim3(grid), dim3(256), 0, s, a, d.G);
-    }
+    // fp32: dQ and dK/dV each in one kernel, no work list and no partial sums
+    if (d.D == 128) run(0, attend_bwd_dq_f32_kernel<128>, dim3(grid), dim3(64 * d.G), a, d.G);
+    else run(0, attend_bwd_dq_f32_kernel<64>, dim3(grid), dim3(64 * d.G), a, d.G);
+    run.skip(1);
+    if (d.D == 128) run(2, attend_bwd_dkdv_f32_kernel<128>, dim3(grid), dim3(256), a, d.G);
+    else run(2, attend_bwd_dkdv_f32_kernel<64>, dim3(grid), dim3(256), a, d.G);
+    run.skip(3);
   }
   return hipGetLastError();
 }

@@ -106,10 +106,10 @@ size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int
   return hga::bwd_workspace_bytes(d);
 }
 
-int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+static int attend_bwd_impl(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                    const void* o, const float* lse, const void* d_o, int64_t t_cap, int64_t t_hist,
                    int64_t seg_len, const int32_t* group_idx, void* dq, void* dk_active, void* dv_active,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   void* workspace, size_t workspace_bytes, void* const* events, void* stream) {
   hga::Dims d;
   int st = resolve(shape, t_cap, t_hist, seg_len, d);
   if (st != HGA_OK) return st;
@@ -125,7 +125,25 @@ int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, c
     return HGA_ERR_ALIGN;
   return hip_status(hga::launch_attend_bwd(d, shape->dtype == HGA_BF16, q, k_cache, v_cache, o, lse, d_o,
                                            group_idx, dq, dk_active, dv_active, workspace,
-                                           (hipStream_t)stream));
+                                           (hipStream_t)stream, (const hipEvent_t*)events));
+}
+
+int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                   const void* o, const float* lse, const void* d_o, int64_t t_cap, int64_t t_hist,
+                   int64_t seg_len, const int32_t* group_idx, void* dq, void* dk_active, void* dv_active,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return attend_bwd_impl(shape, q, k_cache, v_cache, o, lse, d_o, t_cap, t_hist, seg_len, group_idx, dq,
+                         dk_active, dv_active, workspace, workspace_bytes, nullptr, stream);
+}
+
+int hga_attend_bwd_timed(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                         const void* o, const float* lse, const void* d_o, int64_t t_cap, int64_t t_hist,
+                         int64_t seg_len, const int32_t* group_idx, void* dq, void* dk_active,
+                         void* dv_active, void* workspace, size_t workspace_bytes, void* const* events,
+                         void* stream) {
+  if (!events) return HGA_ERR_NULL;
+  return attend_bwd_impl(shape, q, k_cache, v_cache, o, lse, d_o, t_cap, t_hist, seg_len, group_idx, dq,
+                         dk_active, dv_active, workspace, workspace_bytes, events, stream);
 }
 
 const char* hga_status_string(int status) {

@@ -31,6 +31,6 @@ size_t bwd_workspace_bytes(const Dims& d);
 hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* d_o,
                              const int32_t* group_idx, void* dq, void* dk, void* dv,
-                             void* workspace, hipStream_t s);
+                             void* workspace, hipStream_t s, const hipEvent_t* events = nullptr);
 
 }  // namespace hga

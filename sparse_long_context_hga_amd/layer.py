@@ -77,10 +77,14 @@ class HGALayerBuffers:
         L.hga_attend_fwd(self.shape, self.q, self.k, self.v, self.t_cap, self.t_hist, self.seg_len,
                          self.gidx if gidx is None else gidx, self.o, self.lse)
 
-    def bwd(self, gidx: Optional[torch.Tensor] = None):
-        L.hga_attend_bwd(self.shape, self.q, self.k, self.v, self.o, self.lse, self.do, self.t_cap,
-                         self.t_hist, self.seg_len, self.gidx if gidx is None else gidx, self.dq, self.dk,
-                         self.dv, self.ws)
+    def bwd(self, gidx: Optional[torch.Tensor] = None, events=None):
+        g = self.gidx if gidx is None else gidx
+        if events is None:
+            L.hga_attend_bwd(self.shape, self.q, self.k, self.v, self.o, self.lse, self.do, self.t_cap,
+                             self.t_hist, self.seg_len, g, self.dq, self.dk, self.dv, self.ws)
+        else:
+            L.hga_attend_bwd_timed(self.shape, self.q, self.k, self.v, self.o, self.lse, self.do, self.t_cap,
+                                   self.t_hist, self.seg_len, g, self.dq, self.dk, self.dv, self.ws, events)
 
     def step(self):
         """One pass of the hot path: active-segment summaries, route, forward, backward."""

@@ -29,7 +29,8 @@ def _declared():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert set(names) == {"hga_build_summaries", "hga_route", "hga_attend_fwd",
-                          "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_status_string"}
+                          "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_attend_bwd_timed",
+                          "hga_status_string"}
     for n in names:
         assert hasattr(L, n), n
         assert n in hga._lib.SIGNATURES
@@ -114,3 +115,7 @@ def test_attend_validation(L):
     big = hga.hga_attend_bwd_workspace_size(s, 0, 64 * 1025)
     assert bw(ctypes.byref(s), A, A, A, A, A, A, 1 << 17, 0, 64 * 1025, A, A, A, A, A, big, None) == -3
     assert hga.hga_attend_bwd_workspace_size(_shape(head_dim=80), 0, 64) == 0
+    tw = L.hga_attend_bwd_timed
+    assert tw(ctypes.byref(s), *args, A, need, None, None) == -1                # events required
+    ev = (ctypes.c_void_p * 8)()
+    assert tw(ctypes.byref(s), *args, A, need - 1, ev, None) == -6

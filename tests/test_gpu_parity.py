@@ -169,3 +169,34 @@ def test_full_chain_and_determinism(chk, cases, name):
         again = [chk.to_np(t) for t in (L.gidx, L.o, L.lse, L.dq, L.dk, L.dv)]
         for a, b_ in zip(first, again):
             assert np.array_equal(a, b_)
+
+
+@pytest.mark.parametrize("name", ["bf16_g4_d128_ragged", "f32_g4_d128"])
+def test_timed_backward_matches(chk, cases, name):
+    """hga_attend_bwd_timed writes the same bits as hga_attend_bwd and records its
+    events in launch order (dQ, plan, dK/dV, finalize)."""
+    import sparse_long_context_hga_amd as hga
+    w, _, _, _, gidx = cases[name]
+    print(f"case {name}", flush=True)
+    L = chk.DeviceLayer(w)
+    g = torch.from_numpy(gidx).cuda()
+    L.fwd(g)
+    L.bwd(g)
+    torch.cuda.synchronize()
+    ref = [chk.to_np(t).copy() for t in (L.dq, L.dk, L.dv)]
+    for t in (L.dq, L.dk, L.dv):
+        t.zero_()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * hga.HGA_BWD_KERNELS)]
+    start = torch.cuda.Event(enable_timing=True)
+    for e in ev:
+        e.record()                       # torch creates the HIP event at its first record
+    torch.cuda.synchronize()
+    start.record()
+    L.bwd(g, events=ev)
+    torch.cuda.synchronize()
+    for a, b_ in zip(ref, (L.dq, L.dk, L.dv)):
+        assert np.array_equal(a, chk.to_np(b_))
+    marks = [start] + ev                 # every mark re-recorded after `start`, in launch order
+    for e0, e1 in zip(marks, marks[1:]):
+        assert e0.elapsed_time(e1) >= 0.0
+    assert ev[0].elapsed_time(ev[1]) > 0.0 and ev[4].elapsed_time(ev[5]) > 0.0
