@@ -9,16 +9,22 @@
 //   dQ = scale sum_t dS k_t;   for active t:  dV_t = sum P dO,  dK_t = scale sum dS q
 // History tokens (< t_hist) receive nothing.
 //
-// Two kernels, both deterministic (no floating-point atomics):
-//  * dq  (query-major, one work-group per (sequence, KV head, query block)):
-//    same gathered tiles as the forward; recomputes P from LSE; writes dQ and
-//    D = rowsum(dO * O) (workspace) for the second kernel;
-//  * dkdv (key-major, one work-group per (sequence, KV head, active chunk)): the
-//    chunk's 64 keys stay in registers; it visits its own block (causal) and
-//    every later block whose selection contains one of its groups, staging that
-//    block's Q / dO rows per query head in swizzled LDS, and accumulates dK, dV
-//    in fp32 registers (dV^T += dO^T P, dK^T += Q^T dS, with the transposing
-//    LDS reads supplying the k-contiguous operands).
+// bf16 path: four kernels, deterministic (no floating-point atomics):
+//  * dq (query-major, one work-group per (sequence, KV head, query block) and
+//    query-head slice): the forward's gathered tiles again; recomputes P from
+//    LSE; writes dQ and D = rowsum(dO * O) (workspace) for the dK/dV kernel;
+//  * plan (one wave per (sequence, KV head, active chunk)): inverts the
+//    selection -- the ascending list of query blocks that attend the chunk --
+//    and cuts the chunk's work into 1..8 items of about 8 "rounds" (one round =
+//    the 64 rows of one query head of one attending block), filed into buckets
+//    by size so that the dK/dV grid starts with the heaviest items;
+//  * dkdv (one work-group per item): the chunk's 64 keys and values stay in
+//    registers; the item's rounds stream Q / dO rows through swizzled LDS; dK,
+//    dV accumulate in fp32 registers (dV^T += dO^T P, dK^T += Q^T dS, the
+//    transposing LDS reads supplying the k-contiguous operands); a chunk done
+//    by one item writes bf16 dK/dV, otherwise each item writes an fp32 partial;
+//  * finalize: sums a chunk's partials in item order and writes bf16 dK/dV.
+// fp32 path: two plain SIMT kernels (dQ, dK/dV), fp32 throughout.
 #include <hip/hip_ext.h>
 
 #include "hga_device.h"
@@ -213,10 +219,10 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 // Work item (sequence, KV head, active chunk, part).  A chunk is attended by its
 // own block (causally) and by every later block whose selection holds one of its
 // groups; each such block contributes G "rounds" (64 rows of one query head).
-// Lightly visited chunks (<= kDirectVisits visits) are done by part 0 alone, which
-// writes bf16 dK/dV; popular chunks are split by query head over G work-groups
-// that write fp32 partials, summed in part order by the finalize kernel
-// (deterministic; no atomics).
+// The plan kernel cuts a chunk's rounds into np = min(kMaxParts, ceil(rounds /
+// kTargetRounds)) contiguous slices.  With np = 1 the item writes bf16 dK/dV
+// itself; otherwise every item writes an fp32 partial, summed in part order by
+// the finalize kernel (deterministic; no atomics).
 // Inside a work-group: 4 waves; wave w owns keys 32*(w&1) .. +31 of the chunk
 // and rows 32*(w>>1) .. +31 of every round; the next round's Q/dO rows are
 // prefetched into registers while the current round is computed.
