@@ -648,8 +648,8 @@ struct Launcher {
   }
   // a kernel that this path does not need: both marks back to back
   void skip(int i) const {
-    if (ev && ev[2 * i]) hipEventRecord(ev[2 * i], s);
-    if (ev && ev[2 * i + 1]) hipEventRecord(ev[2 * i + 1], s);
+    if (ev && ev[2 * i]) (void)hipEventRecord(ev[2 * i], s);
+    if (ev && ev[2 * i + 1]) (void)hipEventRecord(ev[2 * i + 1], s);
   }
 };
 

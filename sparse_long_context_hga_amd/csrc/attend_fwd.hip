@@ -46,16 +46,14 @@ struct FwdArgs {
 // softmax overlaps another's MFMAs on the same CU.
 template <int D, int G, int HPW>
 __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) void attend_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NT = 128 * HPW;
   constexpr int NW = 2 * HPW;
   constexpr int kStagesHere = HPW == G ? kStages : 2;
   constexpr int KS = D / 16;       // k-steps over the head dimension
   constexpr int DT = D / 32;       // 32-wide column tiles of O^T
-  // Four tile buffer sets as distinct arrays: the compiler can then see that reads
-  // of one never alias the asynchronous copies into another (3 tiles in flight).
+  // Tile buffer sets as distinct arrays: the compiler can then see that reads of one
+  // never alias the asynchronous copies into another.
   __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
   __shared__ __align__(16) uint16_t k2[64 * D], v2[64 * D], k3[64 * D], v3[64 * D];
-  __shared__ int sgid[512];
   auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (B() == 0) return k0; else if constexpr (B() == 1) return k1;
     else if constexpr (B() == 2) return k2; else return k3;
@@ -77,8 +75,8 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
   const int pos = 32 * (w & 1) + n;       // this lane's query position in the block
   const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
 
-  const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bh * a.t_cap * D;
-  const uint16_t* vb = (const uint16_t*)a.v + (int64_t)bh * a.t_cap * D;
+  const char* kb = (const char*)a.k + (int64_t)bh * a.t_cap * D * 2;
+  const char* vb = (const char*)a.v + (int64_t)bh * a.t_cap * D * 2;
 
   bf16x8 qf[KS];
   {
@@ -87,26 +85,46 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
   }
 
-  const int n_valid = count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid);
+  // The group list (k_g <= 512) goes to LDS once; its valid entries (ascending, -1
+  // only trails) are counted on the way.
+  __shared__ int sgid[512];
+  const int n_valid = __builtin_amdgcn_readfirstlane(
+      count_valid<128 * HPW>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
 
-  // Token of row r of tile t: selected tiles hold 8 groups, the last tile is the own
-  // chunk.  Rows past the selection read the own chunk's first token (masked later).
-  auto token = [&](int t, int r) __attribute__((always_inline)) -> int64_t {
-    if (t < n_sel_tiles) {
-      const int slot = 8 * t + (r >> 3);
-      return slot < n_valid ? (int64_t)kGroup * sgid[slot] + (r & 7) : (int64_t)kChunk * J;
-    }
-    return (int64_t)kChunk * J + r;
+  // Group of slot s (0..7) of tile t (wave-uniform): the selection, then the own
+  // chunk as the last tile.  Slots past the selection repeat the own chunk's first
+  // group (masked later).
+  GroupCopier<D, NW> copier;
+  auto prepare = [&](int t_) __attribute__((always_inline)) {
+    const int t = __builtin_amdgcn_readfirstlane(t_);
+    copier.fetch([&](int s) __attribute__((always_inline)) -> int {
+      if (t < n_sel_tiles) {
+        const int i = 8 * t + s;
+        const int v = __builtin_amdgcn_readfirstlane(sgid[min(i, n_valid - 1)]);   // n_valid >= 1 here
+        return i < n_valid ? v : 8 * J;
+      }
+      return 8 * J + s;
+    });
   };
+  // Tiles are copied in order 0, 1, 2, ...: this wave's K blocks, then its V blocks;
+  // then the next tile's groups are fetched.
+  constexpr int BPW = GroupCopier<D, NW>::BPW;
   auto issue = [&](int t, auto B) __attribute__((always_inline)) {
-    dma_tile<D, NW>(KB(B), [&](int r) { return kb + token(t, r) * D; });
-    dma_tile<D, NW>(VB(B), [&](int r) { return vb + token(t, r) * D; });
+    static_for<0, BPW>([&](auto K) { copier.template copy_one<K()>(KB(B), kb); });
+    static_for<0, BPW>([&](auto K) { copier.template copy_one<K()>(VB(B), vb); });
+    if (t + 1 < n_tiles) prepare(t + 1);
   };
+  prepare(0);
+
+  RowOffsets<D> kro;      // K rows rho(n) (and 32 + rho(n): +32 rows as an immediate)
+  kro.init(rho(n), h);
+  ColOffsets<D> vco;      // V^T fragments
+  vco.init(l);
 
   const float c2 = a.scale * kLog2e;
-  float m2 = -INFINITY, lsum = 0.f;
+  float m2 = -INFINITY, lsum = 0.f;   // running maximum (log2 domain); this lane's share of the row sum
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
@@ -114,17 +132,18 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
   auto compute = [&](int t, auto B) __attribute__((always_inline)) {
     const uint16_t* K = KB(B);
     const uint16_t* V = VB(B);
+    kro.refresh();
+    vco.refresh();
     // S^T for 64 keys: two 32-key subtiles.  All K fragments are read in one batch,
     // then the MFMAs run (while copies into LDS are in flight the compiler can only
     // wait for all outstanding LDS reads at once).
     f32x16 s[2];
     {
-      const RowReader<D> rd0(rho(n)), rd1(32 + rho(n));
       bf16x8 kfr[2][KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        kfr[0][ks] = rd0(K, 16 * ks + 8 * h);
-        kfr[1][ks] = rd1(K, 16 * ks + 8 * h);
+        kfr[0][ks] = kro.read(K, ks);
+        kfr[1][ks] = kro.template read<32 * D * 2>(K, ks);
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = wave_max32(mx) * c2;   // finite: every row has a valid key in every tile
+    mx = half_max(mx) * c2;   // finite: every row has a valid key in every tile
     // The running maximum only moves when a tile exceeds it by more than 2^8: P stays
     // below 256 and the rescale of O (64 multiplies) is skipped in almost every tile.
     // O and the normaliser share the maximum, so the result is unchanged.
@@ -166,42 +185,40 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
       m2 = m_new;
     }
-    float rs = 0.f;
+    // P as bf16 operand fragments; the row sum adds the rounded values that the
+    // P V product uses (two per v_dot2).
+    bf16x8 pf[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ks = 0; ks < 4; ++ks) {
+      float pv[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kt][r], c2, -m2));
-        s[kt][r] = p;
-        rs += p;
-      }
-    lsum += wave_sum32(rs);
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + e], c2, -m2));
+      pf[ks] = f32x8_to_bf16x8(pv);
+      const uint4 u = __builtin_bit_cast(uint4, pf[ks]);
+      lsum = add_bf16x2(u.x, lsum);
+      lsum = add_bf16x2(u.y, lsum);
+      lsum = add_bf16x2(u.z, lsum);
+      lsum = add_bf16x2(u.w, lsum);
+    }
     // O^T += V^T P^T over 4 k-steps of 16 keys (V^T fragments read as two batches).
-    const ColReader<D> colrd;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    static_for<0, 2>([&](auto HALF) {
       bf16x8 vfr[2][DT];
+      static_for<0, 2>([&](auto K2) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vfr[K2()][dt] = vco.template read<2 * HALF() + K2()>(V, dt);
+      });
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vfr[k2][dt] = colrd(V, 16 * (2 * half + k2), 32 * dt);
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int ks = 2 * half + k2;
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[ks >> 1][8 * (ks & 1) + e];
-        const bf16x8 pf = f32x8_to_bf16x8(pv);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(vfr[k2][dt], pf, oacc[dt]);
-      }
-    }
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(vfr[k2][dt], pf[2 * HALF() + k2], oacc[dt]);
+    });
   };
 
-  pipeline<kStagesHere, 2 * dma_per_wave<D, NW>()>(n_tiles, issue, compute);
+  pipeline<kStagesHere, 2 * BPW>(n_tiles, issue, compute);
 
   // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
-  const float inv = 1.f / lsum;
+  const float ltot = half_sum(lsum);
+  const float inv = 1.f / ltot;
   uint16_t* op = (uint16_t*)a.o + qrow * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -211,7 +228,7 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
       *reinterpret_cast<uint2*>(op + col) = f32x4_to_bf16x4_bits(
           oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
     }
-  if (h == 0) a.lse[qrow] = (m2 + log2f(lsum)) * kLn2;
+  if (h == 0) a.lse[qrow] = (m2 + log2f(ltot)) * kLn2;
 }
 
 // ---------------------------------------------------------------- fp32 (SIMT)

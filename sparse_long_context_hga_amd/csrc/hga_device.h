@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kChunk = 64;    // tokens per chunk
 constexpr int kGroup = 8;     // tokens per group
@@ -111,38 +112,11 @@ __device__ __forceinline__ int swz_chunk(int r, int c) {
     return c ^ (((r & 3) << 1) | ((r >> 2) & 1));
   }
 }
-// Element offset of (row r, column col) in a swizzled tile.
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int col) {
-  return r * D + 8 * swz_chunk<D>(r, col >> 3) + (col & 7);
-}
-
-// 16-byte read of 8 consecutive columns (col multiple of 8) of row r.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* tile, int r, int col) {
-  return *reinterpret_cast<const bf16x8*>(tile + tile_off<D>(r, col));
-}
-
-// Transposing read: an MFMA operand fragment holding, for lane l, the column
-// `col0 + (l % 32)` of the 8 consecutive rows `row0 + 8*(l/32) .. +7`
-// (the k-contiguous operand layout of v_mfma_*_32x32x16_bf16) out of a
-// row-major tile.  Uses ds_read_b64_tr_b16: within each 16-lane group, lane s
-// supplies the address of 4 columns of one row and lane i receives column i of
-// 4 consecutive rows.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_col8(const uint16_t* tile, int row0, int col0) {
-  const int l = threadIdx.x & 63;
-  const int grp = l >> 4, s = l & 15;
-  const int r = row0 + 8 * (grp >> 1) + (s >> 2);
-  const int c = col0 + 16 * (grp & 1) + 4 * (s & 3);
-  const uint16_t* p0 = tile + tile_off<D>(r, c);
-  const uint16_t* p1 = tile + tile_off<D>(r + 4, c);
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
+// Transposing reads (ds_read_b64_tr_b16) produce the k-contiguous operand layout of
+// v_mfma_*_32x32x16_bf16 out of a row-major tile: within each 16-lane group, lane s
+// supplies the address of 4 columns of one row and lane i receives column i of 4
+// consecutive rows; two such reads give a lane the column `col0 + (l % 32)` of the 8
+// rows `row0 + 8*(l/32) .. +7`.
 
 // Swizzle term of tile row r (depends on r % 16 only).
 template <int D>
@@ -174,7 +148,7 @@ struct RowReader {
   }
 };
 
-// Transposing fragment reader (see lds_col8) for row blocks starting at a multiple
+// Transposing fragment reader (see above) for row blocks starting at a multiple
 // of 16: lane-constant parts precomputed once per use site.
 template <int D>
 struct ColReader {
@@ -200,6 +174,94 @@ struct ColReader {
   }
 };
 
+// Per-lane LDS byte offsets of a wave's fragment reads, computed once per kernel.
+// refresh() passes them through an empty asm in place before each tile: the compiler
+// then neither hoists one address per (buffer, fragment) out of the tile loop nor
+// recomputes them, and the constant part of every address (buffer, k-step) folds
+// into the instruction's immediate offset.
+template <int N>
+struct LaneOffsets {
+  int o[N];
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(o[i]));
+  }
+};
+
+// Row reads (operand A/B layout): row `row` of a swizzled tile, 8 columns at
+// 16 ks + 8 h for k-step ks; `extra` (bytes, compile-time) moves to another row block.
+template <int D>
+struct RowOffsets : LaneOffsets<D / 16> {
+  __device__ __forceinline__ void init(int row, int h) {
+    const int f = swz_f<D>(row);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) this->o[ks] = 2 * (row * D + 8 * ((2 * ks + h) ^ f));
+  }
+  template <int EXTRA = 0>
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + EXTRA + this->o[ks]);
+  }
+};
+
+// Transposing reads (see above): the fragment of rows 16 ks .. +15 and columns
+// 32 dt .. +31; the row block moves by an immediate, the column tile picks an offset.
+template <int D>
+struct ColOffsets : LaneOffsets<D / 16> {   // [2 dt + 0/1]: the two 4-row halves
+  __device__ __forceinline__ void init(int l) {
+    const int grp = l >> 4, s = l & 15;
+    const int rr = 8 * (grp >> 1) + (s >> 2), cc = 16 * (grp & 1) + 4 * (s & 3);
+    const int f0 = swz_f<D>(rr), f1 = swz_f<D>(rr + 4);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int c = (32 * dt + cc) >> 3;
+      this->o[2 * dt] = 2 * (rr * D + 8 * (c ^ f0) + (cc & 7));
+      this->o[2 * dt + 1] = 2 * ((rr + 4) * D + 8 * (c ^ f1) + (cc & 7));
+    }
+  }
+  template <int KS>
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int dt) const {
+    const char* t = reinterpret_cast<const char*>(tile) + 2 * 16 * KS * D;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + this->o[2 * dt]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + this->o[2 * dt + 1]));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// Copies of gathered 64-row tiles into the swizzled layout, wave by wave.  Copy
+// block bi (1 KiB, rows RPB*bi ..) lies inside group slot (RPB*bi)/8, so its source
+// is one contiguous run: the slot's group (wave-uniform) plus a per-lane offset.
+// NW waves share a tile's D/8 blocks; wave w copies blocks w, w + NW, ...
+// The group offsets of the next tile to copy are fetched (scalar loads) one tile
+// ahead, so their latency stays off the critical path.
+template <int D, int NW>
+struct GroupCopier {
+  static constexpr int CH = D / 8, RPB = 64 / CH, NBLK = D / 8, BPW = NBLK / NW;
+  static_assert(NBLK % NW == 0, "copy blocks split evenly over the waves");
+  int64_t next[BPW];   // byte offset of the source group of each of this wave's blocks
+
+  __device__ __forceinline__ static int slot(int k) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    return (RPB * (w + NW * k)) >> 3;
+  }
+  // group_of(slot) -> group id (wave-uniform) of the tile being prepared.
+  template <typename GroupOf>
+  __device__ __forceinline__ void fetch(const GroupOf& group_of) {
+#pragma unroll
+    for (int k = 0; k < BPW; ++k) next[k] = (int64_t)group_of(slot(k)) * (8 * D * 2);
+  }
+  // Copy of this wave's block number k (0 .. BPW-1) of the prepared tile.
+  template <int K>
+  __device__ __forceinline__ void copy_one(uint16_t* tile, const char* base) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const int bi = w + NW * K;
+    const int r = RPB * bi + l / CH;
+    const uint32_t lane_off = 2u * (uint32_t)((((RPB * bi) & 7) + l / CH) * D + 8 * swz_chunk<D>(r, l % CH));
+    __builtin_amdgcn_global_load_lds((const void*)(base + next[K] + lane_off), (lds_void_t*)(tile + 512 * bi), 16, 0, 0);
+  }
+};
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -217,6 +279,25 @@ __device__ __forceinline__ int out_row(int r, int h) { return 16 * (r >> 3) + 8 
 
 __device__ __forceinline__ float wave_max32(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float wave_sum32(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// The same reductions over lanes l and l ^ 32 with v_permlane32_swap (a VALU op, no
+// LDS round trip): swapping a value with itself leaves the lower half's values in
+// the first result and the upper half's in the second, in every lane.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc + x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
 
 // ------------------------------------------------------ gathered key tiles
 // Number of valid (>= 0) entries of a group list; -1 entries only trail.
@@ -243,7 +324,6 @@ constexpr int dma_per_wave() { return (D / 8) >= NW ? (D / 8) / NW : 1; }
 // split the blocks, and each lane fetches the logical chunk that belongs at its
 // physical slot (the swizzle is an involution).  row_src(r) is the global address
 // of tile row r.  Completion: s_waitcnt vmcnt(0) of the issuing wave, then a barrier.
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int D, int NW, typename RowSrc>
 __device__ __forceinline__ void dma_tile(uint16_t* tile, const RowSrc& row_src) {
@@ -279,6 +359,20 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Work-group barrier for the tile pipelines.  __syncthreads() carries a release
+// fence that makes the compiler wait for every outstanding vector-memory operation
+// (s_waitcnt vmcnt(0)), which would drain the copies of the tiles still in flight.
+// Here each wave has already waited for its own copies of the tile about to be read
+// (vmcnt(N) with the later tiles still pending), and its reads of the buffer about to
+// be overwritten have been consumed; LDS is coherent within the work-group, so a bare
+// s_barrier suffices.  The signal fences only stop the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Software pipeline over n tiles with NBUF buffer sets and NBUF-1 tiles in flight.
 // issue(t, ic<B>) starts the asynchronous copies of tile t into buffer set B;
 // compute(t, ic<B>) consumes buffer set B.  Every wave issues exactly L copies
@@ -309,7 +403,7 @@ __device__ __forceinline__ void pipeline(int n, Issue&& issue, Compute&& compute
         } else {
           wait_vmcnt<0>();
         }
-        __syncthreads();
+        tile_barrier();
         if (t + P < n) issue(t + P, ic<(B() + P) % NBUF>{});
         compute(t, B);
       }
