@@ -114,19 +114,81 @@ __device__ int block_topk(const uint32_t* keys, int n, int k, int* out, SelectSh
   return k;
 }
 
+// The same selection for small candidate sets (n <= kRankMax): candidate i is taken
+// iff fewer than k candidates beat it.  With v = key << 32 | (2^32 - 1 - index),
+// "j beats i" (a larger key, or an equal key at a lower index) is v_j > v_i: one
+// 64-bit compare per pair.  Thread t owns the contiguous candidates [t*per, t*per +
+// per), so an exclusive scan of the per-thread counts places the selected ids in
+// ascending order.  pk: LDS scratch of at least n + 1 entries.
+constexpr int kRankMax = 1024;
+__device__ int block_topk_rank(const uint32_t* keys, int n, int k, int* out, SelectShared& sh, uint64_t* pk) {
+  const int tid = threadIdx.x;
+  if (k <= 0 || n <= 0) return 0;
+  const int n16 = (n + 15) & ~15;   // zero padding never beats a real candidate (key > 0)
+  for (int i = tid; i < n16; i += kRouteThreads)
+    pk[i] = i < n ? ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
+  __syncthreads();
+  const int per = (n + kRouteThreads - 1) / kRouteThreads;   // 1 .. 4
+  const int lo = tid * per, hi = min(n, lo + per);
+  uint64_t mine[4];
+  int beat[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mine[u] = lo + u < hi ? pk[lo + u] : ~0ull;
+  const uint4* pk4 = reinterpret_cast<const uint4*>(pk);
+  // 16 candidates per step: 8 broadcast reads in flight, then the compares.
+  for (int j = 0; j < n16 / 2; j += 8) {
+    uint4 kv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kv[e] = pk4[j + e];
+    if (per == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        beat[0] += ((((uint64_t)kv[e].y << 32) | kv[e].x) > mine[0]) + ((((uint64_t)kv[e].w << 32) | kv[e].z) > mine[0]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint64_t a0 = ((uint64_t)kv[e].y << 32) | kv[e].x, a1 = ((uint64_t)kv[e].w << 32) | kv[e].z;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) beat[u] += (a0 > mine[u]) + (a1 > mine[u]);
+      }
+    }
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cnt += (lo + u < hi) && beat[u] < k;
+  int tot;
+  int o = block_exclusive_scan<kRouteThreads>(cnt, sh.scan, tot);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if ((lo + u < hi) && beat[u] < k) out[o++] = lo + u;
+  __syncthreads();
+  return tot;
+}
+
 // ---------------------------------------------------------------- bf16 / MFMA
 // Rows of the block: row = hh * 64 + pos (hh = query head within the KV group).
-// Row tile rt (32 rows) belongs to wave rt % 4.
+// Row tile rt (32 rows) belongs to wave rt % 4.  Candidate summaries are copied
+// into swizzled LDS tiles in batches of 128 rows (double-buffered) and scored
+// from there: each batch is read from memory once per work-group.
+constexpr int kBatch = 128;   // summary rows per batch (two 64-row tiles)
+
 template <int D, int G>
 __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) {
   constexpr int KS = D / 16;
   constexpr int NRT = 2 * G;                      // 32-row tiles in the block
   constexpr int RPW = (NRT + 3) / 4;              // row tiles per wave
-  __shared__ uint32_t ckeys[kMaxChunks];
-  __shared__ uint32_t gkeys[kMaxGroupCand];
+  constexpr int NW = kRouteThreads / 64;
+  constexpr int L = 2 * dma_per_wave<D, NW>();    // copies per wave per batch
+  __shared__ __align__(16) uint16_t sb0[kBatch * D], sb1[kBatch * D];
+  __shared__ __align__(16) uint32_t ckeys[kMaxChunks + 4];
+  __shared__ __align__(16) uint32_t gkeys[kMaxGroupCand + 4];
   __shared__ int csel[64];
   __shared__ int gsel[kMaxGroupCand];
   __shared__ SelectShared sh;
+  __shared__ __align__(16) uint64_t pk[kRankMax + 16];
+  auto SB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return sb0; else return sb1;
+  };
 
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   if (unit >= a.n_units) return;
@@ -139,6 +201,58 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* cs = (const uint16_t*)a.csum + (int64_t)bh * (a.t_cap / kChunk) * D;
   const uint16_t* gs = (const uint16_t*)a.gsum + (int64_t)bh * (a.t_cap / kGroup) * D;
+
+  // Score rows [0, n_rows) given row_src(r) (global address of summary row r, r < n_rows):
+  // the block maximum of q . row goes to keys[r] as an orderable key.
+  RowOffsets<D> ro;
+  ro.init(n, h);
+  // Copies of batch bt of rows [0, n_rows) into buffer set B.
+  auto issue_rows = [&](int n_rows, auto&& row_src, int bt, auto B) __attribute__((always_inline)) {
+    const int r0 = bt * kBatch;
+    static_for<0, 2>([&](auto T) {
+      dma_tile<D, NW>(SB(B) + T() * 64 * D, [&](int r) { return row_src(min(r0 + 64 * T() + r, n_rows - 1)); });
+    });
+  };
+  // Batch 0 must already be in flight (issue_rows(n_rows, row_src, 0, ic<0>)).
+  auto score_rows = [&](int n_rows, auto&& row_src, uint32_t* keys, const bf16x8 (&qf)[RPW][KS]) __attribute__((always_inline)) {
+    auto issue = [&](int bt, auto B) __attribute__((always_inline)) { issue_rows(n_rows, row_src, bt, B); };
+    const int n_batches = (n_rows + kBatch - 1) / kBatch;
+    for (int bt0 = 0; bt0 < n_batches; bt0 += 2) {
+      static_for<0, 2>([&](auto B) {
+        const int bt = bt0 + B();
+        if (bt < n_batches) {
+          wait_vmcnt<0>();
+          tile_barrier();   // batch bt visible; every wave is done with batch bt-1's buffer
+          if (bt + 1 < n_batches) issue(bt + 1, ic<1 - B()>{});
+          ro.refresh();
+          const uint16_t* tb = SB(B);
+          static_for<0, 4>([&](auto ST) {        // 32-row subtiles of the batch
+            const int r = bt * kBatch + 32 * ST() + n;
+            bf16x8 bfr[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              bfr[ks] = ro.template read<(ST() & 1) * 32 * D * 2>(tb + (ST() >> 1) * 64 * D, ks);
+            float best = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+              if (w + 4 * i < NRT) {
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) acc = mfma32(qf[i][ks], bfr[ks], acc);
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) best = fmaxf(best, acc[rr]);
+              }
+            }
+            best = half_max(best);
+            if (h == 0 && r < n_rows && w < NRT) atomicMax(&keys[r], score_key(best));
+          });
+        }
+      });
+    }
+  };
+
+  auto chunk_row = [&](int r) __attribute__((always_inline)) { return cs + (int64_t)r * D; };
+  if (J > 0) issue_rows(J, chunk_row, 0, ic<0>{});   // the first summaries travel while Q loads
 
   // Query fragments (MFMA operand A): lane holds row n of each of its row tiles.
   bf16x8 qf[RPW][KS];
@@ -153,62 +267,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
     }
   }
 
-  for (int i = tid; i < J; i += kRouteThreads) ckeys[i] = 0u;
+  // ---- chunk scores and top-k_c over the candidate chunks [0, J)
+  for (int i = tid; i < ((J + 3) & ~3); i += kRouteThreads) ckeys[i] = 0u;
   __syncthreads();
-
-  // ---- chunk scores: candidate tiles of 32 chunks
-  for (int ct = 0; ct * 32 < J; ++ct) {
-    const int c = ct * 32 + n;
-    const int cl = min(c, J - 1);
-    bf16x8 bfr[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8*>(cs + (int64_t)cl * D + 16 * ks + 8 * h);
-    float best = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      if (w + 4 * i < NRT) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma32(qf[i][ks], bfr[ks], acc);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
-      }
-    }
-    best = wave_max32(best);
-    if (h == 0 && c < J && w < NRT) atomicMax(&ckeys[c], score_key(best));
-  }
+  if (J > 0) score_rows(J, chunk_row, ckeys, qf);
   __syncthreads();
+  const int nc = J <= kRankMax ? block_topk_rank(ckeys, J, a.kc, csel, sh, pk)
+                               : block_topk(ckeys, J, a.kc, csel, sh);   // ascending chunk ids
 
-  const int nc = block_topk(ckeys, J, a.kc, csel, sh);   // ascending chunk ids
-
-  // ---- group scores over the 8 groups of each selected chunk
+  // ---- group scores over the 8 groups of each selected chunk, then top-k_g
   const int ng_cand = 8 * nc;
-  for (int i = tid; i < ng_cand; i += kRouteThreads) gkeys[i] = 0u;
+  for (int i = tid; i < ((ng_cand + 3) & ~3); i += kRouteThreads) gkeys[i] = 0u;
   __syncthreads();
-  for (int gt = 0; gt * 32 < ng_cand; ++gt) {
-    const int slot = gt * 32 + n;
-    const int sl = min(slot, ng_cand - 1);
-    const int gid = 8 * csel[sl >> 3] + (sl & 7);
-    bf16x8 bfr[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8*>(gs + (int64_t)gid * D + 16 * ks + 8 * h);
-    float best = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      if (w + 4 * i < NRT) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma32(qf[i][ks], bfr[ks], acc);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
-      }
-    }
-    best = wave_max32(best);
-    if (h == 0 && slot < ng_cand && w < NRT) atomicMax(&gkeys[slot], score_key(best));
+  if (ng_cand > 0) {
+    auto group_row = [&](int r) __attribute__((always_inline)) { return gs + (int64_t)(8 * csel[r >> 3] + (r & 7)) * D; };
+    issue_rows(ng_cand, group_row, 0, ic<0>{});
+    score_rows(ng_cand, group_row, gkeys, qf);
   }
   __syncthreads();
-
-  const int ng = block_topk(gkeys, ng_cand, a.kg, gsel, sh);   // ascending slots == ascending ids
+  const int ng = block_topk_rank(gkeys, ng_cand, a.kg, gsel, sh, pk);   // ascending slots == ascending ids
 
   // ---- outputs
   int32_t* co = a.cidx + (int64_t)unit * a.kc;
