@@ -105,7 +105,7 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int J = (int)(a.t_hist / kChunk) + j;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n = l & 31;
   const int hh = (item % (G / HPW)) * HPW + (w >> 1);
   const int pos = 32 * (w & 1) + n;
   const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
@@ -125,25 +125,40 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
       dpart += dot8_bf16(dof[ks], *reinterpret_cast<const bf16x8*>(op + 16 * ks + 8 * h));
     }
   }
-  const float Dr = wave_sum32(dpart);
+  const float Dr = half_sum(dpart);
   if (h == 0) a.dvec[qrow] = Dr;
   if (item == 0 && tid < kBuckets) a.bcount[tid] = 0;   // work-list counters for the plan kernel
   const float lse2 = a.lse[qrow] * kLog2e;
 
-  const int n_valid = count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid);
+  const int n_valid = __builtin_amdgcn_readfirstlane(
+      count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
-  auto token = [&](int t, int r) __attribute__((always_inline)) -> int64_t {
-    if (t < n_sel_tiles) {
-      const int slot = 8 * t + (r >> 3);
-      return slot < n_valid ? (int64_t)kGroup * sgid[slot] + (r & 7) : (int64_t)kChunk * J;
-    }
-    return (int64_t)kChunk * J + r;
+  // Tile t: 8 selected groups, or the own chunk as the last tile; slots past the
+  // selection repeat the own chunk's first group (masked).
+  GroupCopier<D, NW> copier;
+  auto prepare = [&](int t_) __attribute__((always_inline)) {
+    const int t = __builtin_amdgcn_readfirstlane(t_);
+    copier.fetch([&](int s) __attribute__((always_inline)) -> int {
+      if (t < n_sel_tiles) {
+        const int i = 8 * t + s;
+        const int v = __builtin_amdgcn_readfirstlane(sgid[min(i, n_valid - 1)]);   // n_valid >= 1 here
+        return i < n_valid ? v : 8 * J;
+      }
+      return 8 * J + s;
+    });
   };
+  constexpr int BPW = GroupCopier<D, NW>::BPW;
   auto issue = [&](int t, auto B) __attribute__((always_inline)) {
-    dma_tile<D, NW>(KB(B), [&](int r) { return kb + token(t, r) * D; });
-    dma_tile<D, NW>(VB(B), [&](int r) { return vb + token(t, r) * D; });
+    static_for<0, BPW>([&](auto K) { copier.template copy_one<K()>(KB(B), (const char*)kb); });
+    static_for<0, BPW>([&](auto K) { copier.template copy_one<K()>(VB(B), (const char*)vb); });
+    if (t + 1 < n_tiles) prepare(t + 1);
   };
+  prepare(0);
+  RowOffsets<D> kro;      // K / V rows rho(n) (+32 rows for the second subtile as an immediate)
+  kro.init(rho(n), h);
+  ColOffsets<D> kco;      // K^T fragments
+  kco.init(l);
 
   const float c2 = a.scale * kLog2e;
   f32x16 dqacc[DT];
@@ -153,22 +168,22 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   auto compute = [&](int t, auto B) __attribute__((always_inline)) {
     const uint16_t* K = KB(B);
     const uint16_t* V = VB(B);
+    kro.refresh();
+    kco.refresh();
     const bool local = t == n_sel_tiles;
     const bool full = !local && 8 * (t + 1) <= n_valid;
     const int kv_lim = full ? 63 : local ? pos : 8 * (n_valid - 8 * t) - 1;
     // One 32-key subtile at a time keeps the live score registers to 2 x 16.
-    const ColReader<D> colrd;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const RowReader<D> rowrd(32 * kt + rho(n));
+    static_for<0, 2>([&](auto KT) {
+      constexpr int kt = KT();
       f32x16 s = {}, dpv = {};
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {               // two batches of KS/2 k-steps
         bf16x8 ka[KS / 2], va[KS / 2];
 #pragma unroll
         for (int i = 0; i < KS / 2; ++i) {
-          ka[i] = rowrd(K, 16 * (hb * KS / 2 + i) + 8 * h);
-          va[i] = rowrd(V, 16 * (hb * KS / 2 + i) + 8 * h);
+          ka[i] = kro.template read<kt * 32 * D * 2>(K, hb * KS / 2 + i);
+          va[i] = kro.template read<kt * 32 * D * 2>(V, hb * KS / 2 + i);
         }
 #pragma unroll
         for (int i = 0; i < KS / 2; ++i) {
@@ -181,9 +196,10 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
       // K^T fragments for the dQ update (independent of dS: read before the softmax math).
       bf16x8 kt_fr[2][DT];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) kt_fr[half][dt] = colrd(K, 32 * kt + 16 * half, 32 * dt);
+      for (int dt = 0; dt < DT; ++dt) {
+        kt_fr[0][dt] = kco.template read<2 * kt>(K, dt);
+        kt_fr[1][dt] = kco.template read<2 * kt + 1>(K, dt);
+      }
 
       float ds[16];
 #pragma unroll
@@ -198,10 +214,10 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) dqacc[dt] = mfma32(kt_fr[half][dt], dsf, dqacc[dt]);
       }
-    }
+    });
   };
 
-  pipeline<kStages, 2 * dma_per_wave<D, NW>()>(n_tiles, issue, compute);
+  pipeline<kStages, 2 * BPW>(n_tiles, issue, compute);
 
   uint16_t* qo = (uint16_t*)a.dq + qrow * D;
 #pragma unroll
