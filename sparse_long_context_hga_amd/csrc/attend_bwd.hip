@@ -15,7 +15,7 @@
 //    LSE; writes dQ and D = rowsum(dO * O) (workspace) for the dK/dV kernel;
 //  * plan (one wave per (sequence, KV head, active chunk)): inverts the
 //    selection -- the ascending list of query blocks that attend the chunk --
-//    and cuts the chunk's work into 1..8 items of about 8 "rounds" (one round =
+//    and cuts the chunk's work into 1..8 items of about 12 "rounds" (one round =
 //    the 64 rows of one query head of one attending block), filed into buckets
 //    by size so that the dK/dV grid starts with the heaviest items;
 //  * dkdv (one work-group per item): the chunk's 64 keys and values stay in
@@ -38,7 +38,7 @@ namespace {
 constexpr int kStages = 2;   // K/V tile buffer sets of the dQ kernel
 
 constexpr int kMaxBlocks = 1024;   // query blocks per segment supported by the dkdv kernel
-constexpr int kTargetRounds = 8;   // dK/dV work is cut into items of about this many rounds
+constexpr int kTargetRounds = 12;  // dK/dV work is cut into items of about this many rounds
 constexpr int kMaxParts = 8;       // at most this many items per active chunk
 constexpr int kBuckets = 64;       // work-list buckets (rounds per work item, capped)
 
