@@ -258,38 +258,42 @@ struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) ve
 // Inverse of the selection for the active segment: for every active chunk, the
 // ascending list of query blocks that attend it (its own block, causally, and
 // every later block whose group list holds one of its 8 groups), with the mask of
-// the selected groups, and whether its dK/dV work is split over the query heads.
-// One wave per (sequence, KV head, active chunk); reads only group_idx.
+// the selected groups, and whether its dK/dV work is split over several items.
+// One work-group of 256 threads per (sequence, KV head, active chunk); reads only
+// group_idx.  A chunk's items differ in size by at most one round, so it files them
+// into the size buckets with at most two atomics.
+constexpr int kPlanThreads = 256;
 template <int G>
-__global__ __launch_bounds__(64) void attend_bwd_plan_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kPlanThreads) void attend_bwd_plan_kernel(BwdArgs a) {
   __shared__ uint32_t mask[kMaxBlocks];
   const int unit = blockIdx.x;
   if (unit >= a.n_units) return;
   const int cc = unit % a.nb;
   const int bh = unit / a.nb;
-  const int l = threadIdx.x;
+  const int tid = threadIdx.x, l = tid & 63;
   const int64_t g_lo = (a.t_hist / kChunk + cc) * 8;
-  for (int i = l; i < a.nb; i += 64) mask[i] = i == cc ? 0xFFu : 0u;
+  for (int i = tid; i < a.nb; i += kPlanThreads) mask[i] = i == cc ? 0xFFu : 0u;
   __syncthreads();
   const int later = a.nb - 1 - cc;
   const int32_t* g0 = a.gidx + ((int64_t)bh * a.nb + cc + 1) * a.kg;
   const int total = later * a.kg;
-  // 16 independent loads in flight per lane, then the tests.
-  for (int e0 = 0; e0 < total; e0 += 64 * 16) {
-    int32_t gv[16];
+  // 8 independent loads in flight per thread, then the tests.
+  for (int e0 = 0; e0 < total; e0 += kPlanThreads * 8) {
+    int32_t gv[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = e0 + 64 * u + l;
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + kPlanThreads * u + tid;
       gv[u] = e < total ? g0[e] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int64_t gid = gv[u];
       if (gid >= g_lo && gid < g_lo + 8)
-        atomicOr(&mask[cc + 1 + (e0 + 64 * u + l) / a.kg], 1u << (int)(gid - g_lo));
+        atomicOr(&mask[cc + 1 + (e0 + kPlanThreads * u + tid) / a.kg], 1u << (int)(gid - g_lo));
     }
   }
   __syncthreads();
+  if (tid >= 64) return;
   int n = 0;
   int* out = a.vis + (int64_t)unit * a.nb;
   for (int j0 = cc; j0 < a.nb; j0 += 64) {
@@ -300,15 +304,20 @@ __global__ __launch_bounds__(64) void attend_bwd_plan_kernel(BwdArgs a) {
     n += __popcll(bal);
   }
   if (l == 0) {
-    // G rounds (query heads) per attending block; cut into np balanced items.
+    // G rounds (query heads) per attending block; cut into np items of q or q+1 rounds.
     const int rounds = G * n;
     const int np = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
     const size_t cap = (size_t)a.n_units * kMaxParts;
+    const int q = rounds / np, n_big = rounds - q * np;     // n_big items of q+1 rounds
+    // item k has (k+1)*rounds/np - k*rounds/np rounds; file each size class with one atomic
+    int pos_small = 0, pos_big = 0;
+    const int b_small = min(q, kBuckets - 1), b_big = min(q + 1, kBuckets - 1);
+    if (np - n_big > 0) pos_small = atomicAdd(&a.bcount[b_small], np - n_big);
+    if (n_big > 0) pos_big = atomicAdd(&a.bcount[b_big], n_big);
     for (int k = 0; k < np; ++k) {
       const int rk = (k + 1) * rounds / np - k * rounds / np;
-      const int bucket = min(rk, kBuckets - 1);
-      const int pos = atomicAdd(&a.bcount[bucket], 1);
-      a.bitems[bucket * cap + pos] = unit * kMaxParts + k;
+      if (rk == q + 1 && n_big > 0) a.bitems[b_big * cap + pos_big++] = unit * kMaxParts + k;
+      else a.bitems[b_small * cap + pos_small++] = unit * kMaxParts + k;
     }
     a.nvis[unit] = n;
     a.flags[unit] = np;
@@ -673,7 +682,7 @@ template <int D, int G>
 void launch_bf16(const BwdArgs& a, const Launcher& run) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per dQ work-group
   run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))), dim3(128 * HPW), a);
-  run(1, attend_bwd_plan_kernel<G>, dim3(a.n_units), dim3(64), a);
+  run(1, attend_bwd_plan_kernel<G>, dim3(a.n_units), dim3(kPlanThreads), a);
   run(2, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
   run(3, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
 }
