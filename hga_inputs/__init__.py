@@ -115,6 +115,14 @@ def random_layer(*, seed: int, batch: int, n_q_heads: int, n_kv_heads: int, head
                     d_o=None if d_o is None else _cast(d_o, dtype))
 
 
+def prev_query_block(*, seed: int, batch: int, n_q_heads: int, head_dim: int,
+                     dtype: str = "bf16") -> np.ndarray:
+    """Queries of the last 64-token block of the previous segment, [B, Hq, 64, d],
+    N(0, 1) (the rows that route a segment's first block under causal routing)."""
+    (r,) = _streams(seed + 7000, 1)
+    return _cast(_normal(r, (batch, n_q_heads, QBLOCK, head_dim)), dtype)
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------

@@ -43,6 +43,15 @@ Where the pages leave a step open, this file takes the readings listed below
            causally (positions 64J .. its own position).
   R-scale  logits = softmax_scale * q . k;  LSE = natural log of sum exp(logits).
   R-grad   no gradient reaches history tokens, the summaries or the selection.
+  R-causal (the strictly causal variant the seventnews article, section
+           "一个真正的警告：因果泄露", says is in development; the pages give no
+           design) a block is routed by the rows of the query block just before
+           it instead of its own, with the same candidates (chunks 0 .. J-1) and
+           the same group step.  Every input of the decision then lies before the
+           block's first position, so no row can learn about later tokens from
+           which chunks were chosen.  The first block of a segment uses the last
+           query block of the previous segment; the very first block of a
+           sequence has no candidates either way.
 
 Precision: inputs are float32 arrays whose values are exact in the workload
 dtype.  Everything is computed in float64 except the two pinned rounding
@@ -137,11 +146,10 @@ def select_topk(scores: np.ndarray, ids: Sequence[int], k: int) -> List[int]:
     return sorted(int(ids[i]) for i in order[:max(0, min(k, len(ids)))])
 
 
-def route_unit(q, chunk_sum, group_sum, t_hist, b, kvh, j, top_chunks, top_groups, group_size):
-    """One (sequence, KV head, query block): returns
+def route_rows(rows, chunk_sum, group_sum, J, b, kvh, top_chunks, top_groups):
+    """Two-level selection for one (sequence b, KV head kvh) over candidate chunks
+    [0, J), scored by the given query rows [R, d]: returns
     (chunk_sel, group_sel, chunk_scores[J], group_ids, group_scores)."""
-    J = t_hist // CHUNK + j
-    rows = block_rows(q, b, kvh, j, group_size)
     sig = block_scores(rows, chunk_sum[b, kvh, :J])
     chunk_sel = select_topk(sig, list(range(J)), top_chunks)
     gids = [c * GROUPS_PER_CHUNK + u for c in chunk_sel for u in range(GROUPS_PER_CHUNK)]
@@ -150,10 +158,34 @@ def route_unit(q, chunk_sum, group_sum, t_hist, b, kvh, j, top_chunks, top_group
     return chunk_sel, group_sel, sig, gids, tau
 
 
-def route(q, chunk_sum, group_sum, t_hist, seg_len, top_chunks, top_groups, group_size):
-    """All units.  Returns chunk_idx [B,Hkv,nb,k_c], group_idx [B,Hkv,nb,k_g] (int32,
-    ascending, -1 padded) and a dict of per-unit score tables."""
-    B, Hkv = chunk_sum.shape[:2]
+def route_unit(q, chunk_sum, group_sum, t_hist, b, kvh, j, top_chunks, top_groups, group_size):
+    """One (sequence, KV head, query block), routed by the block's own rows."""
+    J = t_hist // CHUNK + j
+    return route_rows(block_rows(q, b, kvh, j, group_size), chunk_sum, group_sum, J, b, kvh,
+                      top_chunks, top_groups)
+
+
+def causal_routing_rows(q, q_prev, b, kvh, j, group_size):
+    """R-causal: the rows that route block j are those of the query block just
+    before it -- block j-1 of this segment, or for j = 0 the last block of the
+    previous segment, q_prev [B, Hq, 64, d]."""
+    if j > 0:
+        return block_rows(q, b, kvh, j - 1, group_size)
+    return block_rows(q_prev, b, kvh, 0, group_size)
+
+
+def route_unit_causal(q, q_prev, chunk_sum, group_sum, t_hist, b, kvh, j, top_chunks, top_groups,
+                      group_size):
+    """One unit under strictly causal routing (R-causal).  With no earlier chunk
+    (J = 0) there is nothing to select and no routing rows are needed."""
+    J = t_hist // CHUNK + j
+    if J == 0:
+        return [], [], np.zeros((0,), np.float32), [], np.zeros((0,), np.float32)
+    rows = causal_routing_rows(q, q_prev, b, kvh, j, group_size)
+    return route_rows(rows, chunk_sum, group_sum, J, b, kvh, top_chunks, top_groups)
+
+
+def _route_all(unit_fn, B, Hkv, seg_len, top_chunks, top_groups):
     nb = seg_len // QBLOCK
     cidx = np.full((B, Hkv, nb, top_chunks), -1, np.int32)
     gidx = np.full((B, Hkv, nb, top_groups), -1, np.int32)
@@ -161,12 +193,30 @@ def route(q, chunk_sum, group_sum, t_hist, seg_len, top_chunks, top_groups, grou
     for b in range(B):
         for kvh in range(Hkv):
             for j in range(nb):
-                cs, gs, sig, gids, tau = route_unit(q, chunk_sum, group_sum, t_hist, b, kvh, j,
-                                                    top_chunks, top_groups, group_size)
+                cs, gs, sig, gids, tau = unit_fn(b, kvh, j)
                 cidx[b, kvh, j, :len(cs)] = cs
                 gidx[b, kvh, j, :len(gs)] = gs
                 tables[(b, kvh, j)] = (sig, gids, tau)
     return cidx, gidx, tables
+
+
+def route(q, chunk_sum, group_sum, t_hist, seg_len, top_chunks, top_groups, group_size):
+    """All units.  Returns chunk_idx [B,Hkv,nb,k_c], group_idx [B,Hkv,nb,k_g] (int32,
+    ascending, -1 padded) and a dict of per-unit score tables."""
+    B, Hkv = chunk_sum.shape[:2]
+    return _route_all(lambda b, kvh, j: route_unit(q, chunk_sum, group_sum, t_hist, b, kvh, j, top_chunks,
+                                                   top_groups, group_size),
+                      B, Hkv, seg_len, top_chunks, top_groups)
+
+
+def route_causal(q, q_prev, chunk_sum, group_sum, t_hist, seg_len, top_chunks, top_groups, group_size):
+    """All units under strictly causal routing (R-causal); outputs as route().
+    q_prev [B, Hq, 64, d]: the last query block of the previous segment (needed
+    when t_hist > 0, ignored otherwise)."""
+    B, Hkv = chunk_sum.shape[:2]
+    return _route_all(lambda b, kvh, j: route_unit_causal(q, q_prev, chunk_sum, group_sum, t_hist, b, kvh, j,
+                                                          top_chunks, top_groups, group_size),
+                      B, Hkv, seg_len, top_chunks, top_groups)
 
 
 def selection_accepted(sel: Sequence[int], ids: Sequence[int], scores: np.ndarray, k: int,

@@ -141,3 +141,121 @@ def test_planted_chunks_are_recalled():
             assert planted <= set(int(c) for c in cidx[0, kvh, j])
             pg = {8 * c + u for c in planted for u in range(8)}
             assert pg <= set(int(g) for g in gidx[0, kvh, j])
+
+
+# ---------------------------------------------------------------------------
+# Strictly causal routing (R-causal): a block is routed by the query block before it.
+# ---------------------------------------------------------------------------
+
+def _causal_layer(seed=21, t_hist=256, seg_len=256, dtype="f32", kc=2, kg=6):
+    w = hi.random_layer(seed=seed, batch=1, n_q_heads=4, n_kv_heads=2, head_dim=32, t_hist=t_hist,
+                        seg_len=seg_len, top_chunks=kc, top_groups=kg, dtype=dtype)
+    q_prev = hi.prev_query_block(seed=seed, batch=1, n_q_heads=4, head_dim=32, dtype=dtype)
+    return w, q_prev
+
+
+def test_causal_route_scores_use_the_previous_block_rows():
+    """Chunk and group scores of block j equal the mean raw logit of the rows of the
+    block before it (q_prev for the first block) against each candidate's tokens,
+    computed from the keys without forming a summary; the selections equal the
+    exhaustive k-subset answer on those scores."""
+    w, q_prev = _causal_layer()
+    gs, cs = _summaries(w)
+    q_all = np.concatenate([q_prev, w.q], axis=2)      # block j of the segment routes with q_all block j
+    kk = w.k_cache.astype(np.float64)
+    for kvh in range(2):
+        for j in range(4):
+            J = w.t_hist // 64 + j
+            c_sel, g_sel, sig, gids, tau = ora.route_unit_causal(w.q, q_prev, cs, gs, w.t_hist, 0, kvh, j,
+                                                                 w.top_chunks, w.top_groups, 2)
+            rows = q_all[0, 2 * kvh:2 * kvh + 2, 64 * j:64 * j + 64].reshape(-1, 32).astype(np.float64)
+            brute = np.array([max(float(np.mean(kk[0, kvh, 64 * c:64 * c + 64] @ r)) for r in rows)
+                              for c in range(J)])
+            assert np.max(np.abs(sig - brute)) <= 1e-5 * (1 + np.max(np.abs(brute)))
+            assert c_sel == _brute_topk(sig, list(range(J)), w.top_chunks)
+            gbrute = np.array([max(float(np.mean(kk[0, kvh, 8 * g:8 * g + 8] @ r)) for r in rows) for g in gids])
+            assert np.max(np.abs(tau - gbrute)) <= 1e-5 * (1 + np.max(np.abs(gbrute)))
+            assert g_sel == _brute_topk(tau, gids, w.top_groups)
+
+
+def test_causal_route_is_blind_to_the_block_and_everything_after_it():
+    """Replacing every query at or after block j's first position and every key at
+    or after it leaves block j's causal selection unchanged; replacing the rows of
+    the block before it does change selections (the decision really reads them)."""
+    w, q_prev = _causal_layer(seed=22)
+    gs, cs = _summaries(w)
+    base_c, base_g, _ = ora.route_causal(w.q, q_prev, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, 2)
+    rng = np.random.default_rng(5)
+    moved = 0
+    for j in range(4):
+        q2 = w.q.copy()
+        q2[:, :, 64 * j:] = rng.standard_normal(q2[:, :, 64 * j:].shape).astype(np.float32) * 3
+        w2 = hi.random_layer(seed=22, batch=1, n_q_heads=4, n_kv_heads=2, head_dim=32, t_hist=w.t_hist,
+                             seg_len=w.seg_len, top_chunks=2, top_groups=6, dtype="f32")
+        w2.k_cache[:, :, w.t_hist + 64 * j:] = rng.standard_normal(
+            w2.k_cache[:, :, w.t_hist + 64 * j:].shape).astype(np.float32) * 3
+        gs2, cs2 = _summaries(w2)
+        c2, g2, _ = ora.route_causal(q2, q_prev, cs2, gs2, w.t_hist, w.seg_len, 2, 6, 2)
+        np.testing.assert_array_equal(c2[:, :, j], base_c[:, :, j])
+        np.testing.assert_array_equal(g2[:, :, j], base_g[:, :, j])
+        # the rows that do route block j: the block before it
+        q3, qp3 = w.q.copy(), q_prev.copy()
+        if j > 0:
+            q3[:, :, 64 * (j - 1):64 * j] = rng.standard_normal((1, 4, 64, 32)).astype(np.float32) * 3
+        else:
+            qp3 = rng.standard_normal(q_prev.shape).astype(np.float32) * 3
+        c3, g3, _ = ora.route_causal(q3, qp3, cs, gs, w.t_hist, w.seg_len, 2, 6, 2)
+        moved += int(not np.array_equal(g3[:, :, j], base_g[:, :, j]))
+    assert moved >= 2
+
+
+def test_causal_route_is_segmentation_invariant():
+    """One 512-token segment with no history, or the same tokens as two 256-token
+    segments where the second gets the first one's last query block: identical
+    selections.  The first block of the sequence selects nothing."""
+    w, _ = _causal_layer(seed=23, t_hist=0, seg_len=512)
+    gs, cs = _summaries(w)
+    c_one, g_one, _ = ora.route_causal(w.q, None, cs, gs, 0, 512, 2, 6, 2)
+    c_a, g_a, _ = ora.route_causal(w.q[:, :, :256], None, cs, gs, 0, 256, 2, 6, 2)
+    c_b, g_b, _ = ora.route_causal(w.q[:, :, 256:], w.q[:, :, 192:256], cs, gs, 256, 256, 2, 6, 2)
+    np.testing.assert_array_equal(np.concatenate([c_a, c_b], axis=2), c_one)
+    np.testing.assert_array_equal(np.concatenate([g_a, g_b], axis=2), g_one)
+    assert np.all(c_one[:, :, 0] == -1) and np.all(g_one[:, :, 0] == -1)
+    assert np.all(c_one[:, :, 1, 0] == 0) and np.all(c_one[:, :, 1, 1] == -1)   # only chunk 0 exists
+
+
+def _layer_out(w, q, k, v, q_prev, causal):
+    """Summaries, routing (block or causal) and forward of a one-sequence layer."""
+    B, H, T, d = k.shape
+    gs = np.zeros((B, H, T // 8, d), np.float32)
+    cs = np.zeros((B, H, T // 64, d), np.float32)
+    ora.build_summaries(k, 0, w.t_hist + w.seg_len, w.dtype, gs, cs)
+    if causal:
+        _, gidx, _ = ora.route_causal(q, q_prev, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, 2)
+    else:
+        _, gidx, _ = ora.route(q, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, 2)
+    return ora.attend_fwd(q, k, v, w.t_hist, gidx, w.softmax_scale, 2)[0]
+
+
+def test_causal_routing_removes_the_in_block_leak():
+    """The leak: under block routing, later queries of a block can change which
+    groups its earlier rows attend, so an earlier output depends on a later token.
+    Steering the rows after position p of block 2 toward an unselected chunk's
+    summary changes outputs at positions <= p under block routing, and changes
+    nothing at positions <= p under causal routing."""
+    w, q_prev = _causal_layer(seed=24, kc=1, kg=3)
+    gs, cs = _summaries(w)
+    j, p = 2, 10                                       # row positions 64j .. 64j+p stay fixed
+    c_blk, _, _ = ora.route(w.q, cs, gs, w.t_hist, w.seg_len, 1, 3, 2)
+    q2 = w.q.copy()
+    for kvh in range(2):
+        J = w.t_hist // 64 + j
+        target = next(c for c in range(J) if c not in set(c_blk[0, kvh, j].tolist()))
+        q2[0, 2 * kvh:2 * kvh + 2, 64 * j + p + 1:64 * j + 64] = 50.0 * cs[0, kvh, target]
+    lo = 64 * j + p + 1
+    o_blk = _layer_out(w, w.q, w.k_cache, w.v_cache, q_prev, False)
+    o_blk2 = _layer_out(w, q2, w.k_cache, w.v_cache, q_prev, False)
+    assert np.max(np.abs(o_blk2[:, :, 64 * j:lo] - o_blk[:, :, 64 * j:lo])) > 1e-3     # leak present
+    o_c = _layer_out(w, w.q, w.k_cache, w.v_cache, q_prev, True)
+    o_c2 = _layer_out(w, q2, w.k_cache, w.v_cache, q_prev, True)
+    np.testing.assert_array_equal(o_c2[:, :, :lo], o_c[:, :, :lo])                     # and gone
