@@ -12,7 +12,11 @@ head_dim 128, bf16) at 16,384 tokens of context: 14,336 detached history tokens
 plus a 2,048-token active segment, top-16 chunks / top-64 groups, block-structured
 keys.  Prints one JSON line (tokens/s of the active segment, whole job).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--routing block|causal]
+                    [--no-cpu-baseline]
+
+--routing causal times the strictly causal variant (each block routed by the
+block before it, hga_route_causal); the default is block routing.
 """
 from __future__ import annotations
 
@@ -39,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
                    choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k"])
+    p.add_argument("--routing", default="block", choices=["block", "causal"],
+                   help="block: each block routes itself (hga_route); causal: the block before it routes it")
     p.add_argument("--mark-every", type=int, default=8,
                    help="put per-kernel timing marks on every N-th timed step (default 8)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
@@ -191,7 +197,7 @@ def make_workload(name):
 
 
 # ------------------------------------------------------------------ CPU oracle leg
-def cpu_baseline(w, min_seconds=10.0, max_reps=5):
+def cpu_baseline(w, q_prev=None, min_seconds=10.0, max_reps=5):
     """The CPU oracle, as it stands, on the same step (all of it), repeated until
     about `min_seconds` of work; returns tokens/s from the median repetition."""
     import numpy as np
@@ -210,7 +216,11 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=5):
     while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
         t0 = time.perf_counter()
         ora.build_summaries(w.k_cache, w.t_hist, w.t_hist + w.seg_len, w.dtype, gs, cs)
-        _, gidx, _ = ora.route(w.q, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, w.group_size)
+        if q_prev is None:
+            _, gidx, _ = ora.route(w.q, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups, w.group_size)
+        else:
+            _, gidx, _ = ora.route_causal(w.q, q_prev, cs, gs, w.t_hist, w.seg_len, w.top_chunks, w.top_groups,
+                                          w.group_size)
         ora.attend_fwd(w.q, w.k_cache, w.v_cache, w.t_hist, gidx, w.softmax_scale, w.group_size)
         if w.d_o is not None:
             ora.attend_bwd(w.q, w.k_cache, w.v_cache, w.d_o, w.t_hist, gidx, w.softmax_scale, w.group_size)
@@ -262,6 +272,15 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] calibration: fill then scale-copy of {n} bytes", file=sys.stderr, flush=True)
         del src, dst
+    q_prev_np = None
+    if args.routing == "causal":
+        import hga_inputs as hi
+        q_prev_np = hi.prev_query_block(seed=1, batch=w.batch, n_q_heads=w.n_q_heads, head_dim=w.head_dim,
+                                        dtype=w.dtype)
+        q_prev = dev(q_prev_np)
+        route = lambda: L.route_causal(q_prev)   # noqa: E731
+    else:
+        route = L.route
     L.summaries(0, w.t_hist)                                  # history summaries: built once, untimed
     torch.cuda.synchronize()
 
@@ -283,7 +302,7 @@ def main():
         if se: se[0].record(stream)
         L.summaries(w.t_hist, w.t_hist + w.seg_len)
         if se: se[1].record(stream)
-        L.route()
+        route()
         if se: se[2].record(stream)
         L.fwd()
         if se: se[3].record(stream)
@@ -330,7 +349,7 @@ def main():
         ach = wk["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roofline["traffic"] = measured_traffic(dom, w.name)
+    roofline["traffic"] = measured_traffic(dom, w.name) if args.routing == "block" else None
     roofline["kernel"] = dom
 
     tokens = w.batch * w.seg_len
@@ -342,14 +361,14 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "t_hist": w.t_hist,
                    "seg_len": w.seg_len, "context": w.t_hist + w.seg_len, "top_chunks": w.top_chunks,
-                   "top_groups": w.top_groups, "parallelism": "none (1 GPU)"},
+                   "top_groups": w.top_groups, "routing": args.routing, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
         "kernel_timing": f"HIP events on {len(marked)} of the {args.steps} timed steps; backward kernels "
                          f"timed from their dispatches, the other calls between events on the stream",
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, q_prev_np)
     print(json.dumps(out), flush=True)
 
 

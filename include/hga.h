@@ -125,6 +125,27 @@ int hga_route(const hga_shape* shape, const void* q, const void* chunk_sum,
               void* stream);
 
 /*
+ * hga_route_causal -- strictly causal routing.  With hga_route a block's
+ * decision reads all of its rows, so an earlier position can learn which chunks
+ * its later positions favour (the side channel described in the seventnews
+ * article, section "一个真正的警告：因果泄露", which names a strictly causal
+ * variant as in development without giving one).  This library's variant routes
+ * block j with the rows of the query block just before it, everything else as in
+ * hga_route (candidates chunks 0 .. J-1, the group step, ties, output format):
+ *   rows(j) = block j-1 of q                      for j >= 1
+ *           = q_prev, the last 64-position block of the previous segment, for j = 0
+ * Every input of the decision then lies before the block's first position.
+ *   q_prev  [B, Hq, 64, d] read; required when t_hist > 0 (HGA_ERR_NULL if NULL),
+ *           ignored when t_hist == 0 (the first block has no candidates).
+ * Other arguments, requirements and errors as hga_route.  hga_attend_fwd and
+ * hga_attend_bwd take the group_idx it writes unchanged.
+ */
+int hga_route_causal(const hga_shape* shape, const void* q, const void* q_prev,
+                     const void* chunk_sum, const void* group_sum, int64_t t_cap, int64_t t_hist,
+                     int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx, float* chunk_score,
+                     float* group_score, void* stream);
+
+/*
  * hga_attend_fwd -- exact attention of every active query over the exact
  * tokens of its block's selected groups plus its own chunk up to and including
  * its own position (summaries never act as values: seventnews, "HGA的不同之处";

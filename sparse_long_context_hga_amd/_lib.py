@@ -55,6 +55,7 @@ _SHAPE = ctypes.POINTER(HgaShape)
 SIGNATURES = {
     "hga_build_summaries": (ctypes.c_int, [_SHAPE, _P, _I64, _I64, _I64, _P, _P, _P]),
     "hga_route": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "hga_route_causal": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "hga_attend_fwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "hga_attend_bwd_workspace_size": (ctypes.c_size_t, [_SHAPE, _I64, _I64]),
     "hga_attend_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
@@ -110,6 +111,15 @@ def hga_route(shape: HgaShape, q: torch.Tensor, chunk_sum: torch.Tensor, group_s
               stream=None) -> None:
     _check("hga_route", lib().hga_route(
         ctypes.byref(shape), _ptr(q), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist, seg_len,
+        _ptr(chunk_idx), _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _stream(stream)))
+
+
+def hga_route_causal(shape: HgaShape, q: torch.Tensor, q_prev: Optional[torch.Tensor], chunk_sum: torch.Tensor,
+                     group_sum: torch.Tensor, t_cap: int, t_hist: int, seg_len: int, chunk_idx: torch.Tensor,
+                     group_idx: torch.Tensor, chunk_score: Optional[torch.Tensor] = None,
+                     group_score: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check("hga_route_causal", lib().hga_route_causal(
+        ctypes.byref(shape), _ptr(q), _ptr(q_prev), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist, seg_len,
         _ptr(chunk_idx), _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _stream(stream)))
 
 

@@ -66,9 +66,10 @@ int hga_build_summaries(const hga_shape* shape, const void* k_cache, int64_t t_c
                                           chunk_sum, (hipStream_t)stream));
 }
 
-int hga_route(const hga_shape* shape, const void* q, const void* chunk_sum, const void* group_sum,
-              int64_t t_cap, int64_t t_hist, int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx,
-              float* chunk_score, float* group_score, void* stream) {
+static int route_impl(const hga_shape* shape, const void* q, const void* q_prev, bool causal,
+                      const void* chunk_sum, const void* group_sum, int64_t t_cap, int64_t t_hist,
+                      int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx, float* chunk_score,
+                      float* group_score, void* stream) {
   hga::Dims d;
   int st = resolve(shape, t_cap, t_hist, seg_len, d);
   if (st != HGA_OK) return st;
@@ -76,13 +77,30 @@ int hga_route(const hga_shape* shape, const void* q, const void* chunk_sum, cons
   if ((t_hist + seg_len) / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
   if (!q || !chunk_sum || !group_sum || (d.kc > 0 && !chunk_idx) || (d.kg > 0 && !group_idx))
     return HGA_ERR_NULL;
+  if (causal && t_hist > 0 && !q_prev) return HGA_ERR_NULL;
   if (!aligned16(q) || !aligned16(chunk_sum) || !aligned16(group_sum) ||
       (chunk_idx && !aligned16(chunk_idx)) || (group_idx && !aligned16(group_idx)) ||
       (chunk_score && !aligned16(chunk_score)) ||
-      (group_score && !aligned16(group_score)))
+      (group_score && !aligned16(group_score)) || (causal && q_prev && !aligned16(q_prev)))
     return HGA_ERR_ALIGN;
-  return hip_status(hga::launch_route(d, shape->dtype == HGA_BF16, q, chunk_sum, group_sum, chunk_idx,
-                                      group_idx, chunk_score, group_score, (hipStream_t)stream));
+  return hip_status(hga::launch_route(d, shape->dtype == HGA_BF16, q, causal ? q_prev : nullptr, causal,
+                                      chunk_sum, group_sum, chunk_idx, group_idx, chunk_score, group_score,
+                                      (hipStream_t)stream));
+}
+
+int hga_route(const hga_shape* shape, const void* q, const void* chunk_sum, const void* group_sum,
+              int64_t t_cap, int64_t t_hist, int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx,
+              float* chunk_score, float* group_score, void* stream) {
+  return route_impl(shape, q, nullptr, false, chunk_sum, group_sum, t_cap, t_hist, seg_len, chunk_idx,
+                    group_idx, chunk_score, group_score, stream);
+}
+
+int hga_route_causal(const hga_shape* shape, const void* q, const void* q_prev, const void* chunk_sum,
+                     const void* group_sum, int64_t t_cap, int64_t t_hist, int64_t seg_len,
+                     int32_t* chunk_idx, int32_t* group_idx, float* chunk_score, float* group_score,
+                     void* stream) {
+  return route_impl(shape, q, q_prev, true, chunk_sum, group_sum, t_cap, t_hist, seg_len, chunk_idx,
+                    group_idx, chunk_score, group_score, stream);
 }
 
 int hga_attend_fwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,

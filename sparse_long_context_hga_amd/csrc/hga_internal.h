@@ -18,9 +18,10 @@ struct Dims {
 hipError_t launch_summaries(const Dims& d, bool bf16, const void* k, int64_t t_begin, int64_t t_end,
                             void* group_sum, void* chunk_sum, hipStream_t s);
 
-hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* chunk_sum,
-                        const void* group_sum, int32_t* chunk_idx, int32_t* group_idx,
-                        float* chunk_score, float* group_score, hipStream_t s);
+// causal: block j is routed by the rows of block j-1 (q_prev [B,Hq,64,d] for j = 0).
+hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* q_prev, bool causal,
+                        const void* chunk_sum, const void* group_sum, int32_t* chunk_idx,
+                        int32_t* group_idx, float* chunk_score, float* group_score, hipStream_t s);
 
 hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
                              const int32_t* group_idx, void* o, float* lse, hipStream_t s);

@@ -10,6 +10,13 @@
 // the 8 groups of every selected chunk; ties go to the lower index; outputs are
 // ascending and padded with -1.
 //
+// Strictly causal variant (the same article, "因果泄露", says one is in development
+// and gives no design; this library's reading): a block is routed by the rows of
+// the query block before it -- block j-1 of the segment, or for j = 0 the last
+// block of the previous segment (q_prev) -- with the same candidates, so no input
+// of the decision lies at or after the block's first position.  Only the source
+// of the query rows differs (RouteArgs::lag).
+//
 // One work-group (256 threads) per (sequence, KV head, query block).  The bf16
 // path scores with v_mfma_f32_32x32x16_bf16: operand A = 32 query rows (held in
 // registers for the whole kernel), operand B = 32 summary rows, so each lane
@@ -32,6 +39,7 @@ constexpr int kMaxGroupCand = 512;    // 8 * max top_chunks
 
 struct RouteArgs {
   const void* q;
+  const void* q_prev;   // [B, Hq, 64, d]: routes block 0 when lag == 1
   const void* csum;
   const void* gsum;
   int32_t* cidx;
@@ -40,7 +48,17 @@ struct RouteArgs {
   float* gscore;
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kc, kg, nb, n_units;
+  int lag;              // 0: a block routes itself; 1: the block before it routes it
 };
+
+// Start of query row `pos` of head `head` in the block that routes block j.
+template <typename T>
+__device__ __forceinline__ const T* routing_row(const RouteArgs& a, int b, int head, int j, int pos, int D) {
+  const int qb = j - a.lag;
+  if (qb >= 0)
+    return (const T*)a.q + ((((int64_t)b * a.Hq + head) * a.seg_len) + qb * kQBlock + pos) * D;
+  return (const T*)a.q_prev + ((((int64_t)b * a.Hq + head) * kQBlock) + pos) * D;
+}
 
 struct SelectShared {
   uint32_t hist[256];
@@ -198,7 +216,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   const int J = (int)(a.t_hist / kChunk) + j;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
 
-  const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* cs = (const uint16_t*)a.csum + (int64_t)bh * (a.t_cap / kChunk) * D;
   const uint16_t* gs = (const uint16_t*)a.gsum + (int64_t)bh * (a.t_cap / kGroup) * D;
 
@@ -255,15 +272,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   if (J > 0) issue_rows(J, chunk_row, 0, ic<0>{});   // the first summaries travel while Q loads
 
   // Query fragments (MFMA operand A): lane holds row n of each of its row tiles.
+  // Nothing is scored when J == 0 (and q_prev may then be absent).
   bf16x8 qf[RPW][KS];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int rt = w + 4 * i;
-    if (rt < NRT) {
+    if (rt < NRT && J > 0) {
       const int hh = rt >> 1, pos = 32 * (rt & 1) + n;
-      const uint16_t* qp = q + ((((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + j * kQBlock + pos) * D;
+      const uint16_t* qp = routing_row<uint16_t>(a, b, kvh * G + hh, j, pos, D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[i][ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[i][ks] = bf16x8{};
     }
   }
 
@@ -318,7 +339,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a, i
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int J = (int)(a.t_hist / kChunk) + j;
   const int tid = threadIdx.x;
-  const float* q = (const float*)a.q;
   const float* cs = (const float*)a.csum + (int64_t)bh * (a.t_cap / kChunk) * D;
   const float* gs = (const float*)a.gsum + (int64_t)bh * (a.t_cap / kGroup) * D;
   const int R = G * kQBlock;
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a, i
     float best = -INFINITY;
     for (int r = 0; r < R; ++r) {
       const int hh = r / kQBlock, pos = r % kQBlock;
-      const float* qp = q + ((((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + j * kQBlock + pos) * D;
+      const float* qp = routing_row<float>(a, b, kvh * G + hh, j, pos, D);
       float acc = 0.f;
       for (int e = 0; e < D; ++e) acc = fmaf(qp[e], srow[e], acc);
       best = fmaxf(best, acc);
@@ -374,11 +394,12 @@ void launch_bf16_g(const RouteArgs& a, int G, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* chunk_sum,
-                        const void* group_sum, int32_t* chunk_idx, int32_t* group_idx,
-                        float* chunk_score, float* group_score, hipStream_t s) {
+hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* q_prev, bool causal,
+                        const void* chunk_sum, const void* group_sum, int32_t* chunk_idx,
+                        int32_t* group_idx, float* chunk_score, float* group_score, hipStream_t s) {
   RouteArgs a;
-  a.q = q; a.csum = chunk_sum; a.gsum = group_sum;
+  a.q = q; a.q_prev = q_prev; a.lag = causal ? 1 : 0;
+  a.csum = chunk_sum; a.gsum = group_sum;
   a.cidx = chunk_idx; a.gidx = group_idx; a.cscore = chunk_score; a.gscore = group_score;
   a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kc = d.kc; a.kg = d.kg; a.nb = d.nb;

@@ -73,6 +73,13 @@ class HGALayerBuffers:
                     self.gsum if gsum is None else gsum, self.t_cap, self.t_hist, self.seg_len,
                     self.cidx, self.gidx, self.cscore, self.gscore)
 
+    def route_causal(self, q_prev: Optional[torch.Tensor], csum: Optional[torch.Tensor] = None,
+                     gsum: Optional[torch.Tensor] = None):
+        """Strictly causal routing: block j routed by block j-1 (q_prev for the first block)."""
+        L.hga_route_causal(self.shape, self.q, q_prev, self.csum if csum is None else csum,
+                           self.gsum if gsum is None else gsum, self.t_cap, self.t_hist, self.seg_len,
+                           self.cidx, self.gidx, self.cscore, self.gscore)
+
     def fwd(self, gidx: Optional[torch.Tensor] = None):
         L.hga_attend_fwd(self.shape, self.q, self.k, self.v, self.t_cap, self.t_hist, self.seg_len,
                          self.gidx if gidx is None else gidx, self.o, self.lse)
@@ -100,7 +107,9 @@ class HGAKVCache:
 
     Positions [0, length) are written; appending a segment writes its K/V and
     summaries.  Gradients never flow into the cache: a segment's K/V become
-    detached history once the next segment starts.
+    detached history once the next segment starts.  For strictly causal routing
+    the cache also keeps the last query block of the latest committed segment
+    (it routes the next segment's first block).
     """
 
     def __init__(self, batch: int, n_kv_heads: int, head_dim: int, t_cap: int,
@@ -114,6 +123,8 @@ class HGAKVCache:
         self.gsum = torch.zeros(batch, n_kv_heads, t_cap // 8, head_dim, dtype=dtype, device=device)
         self.csum = torch.zeros(batch, n_kv_heads, t_cap // 64, head_dim, dtype=dtype, device=device)
         self.length = 0
+        self.q_last: Optional[torch.Tensor] = None      # [B, Hq, 64, d] of the committed history
+        self._q_pending: Optional[torch.Tensor] = None
 
     def write(self, k_seg: torch.Tensor, v_seg: torch.Tensor, shape: L.HgaShape) -> int:
         """Place a segment's K/V at [length, length+S) and build its summaries.
@@ -127,22 +138,36 @@ class HGAKVCache:
         L.hga_build_summaries(shape, self.k, self.t_cap, t0, t0 + S, self.gsum, self.csum)
         return t0
 
+    def keep_last_query_block(self, q: torch.Tensor):
+        """Remember the written segment's last 64 query rows (taken over by commit)."""
+        self._q_pending = q[:, :, -64:].detach().contiguous().clone()
+
     def commit(self, seg_len: int):
         """The written segment becomes history."""
         self.length += seg_len
+        self.q_last, self._q_pending = self._q_pending, None
 
 
 class _HGAAttentionFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k_seg, v_seg, cache: HGAKVCache, top_chunks: int, top_groups: int, scale: float):
+    def forward(ctx, q, k_seg, v_seg, cache: HGAKVCache, top_chunks: int, top_groups: int, scale: float,
+                causal_routing: bool):
         B, Hq, S, d = q.shape
         shape = L.make_shape(B, Hq, cache.n_kv_heads, d, top_chunks, top_groups, _dtype_name(q.dtype), scale)
         q = q.contiguous()
+        if causal_routing and cache.length > 0 and (cache.q_last is None or cache.q_last.shape[1] != Hq):
+            raise ValueError("causal routing over history needs the previous segment's last query block "
+                             "(route every segment of the cache causally)")
         t_hist = cache.write(k_seg, v_seg, shape)
         nb = S // 64
         cidx = torch.empty(B, cache.n_kv_heads, nb, top_chunks, dtype=torch.int32, device=q.device)
         gidx = torch.empty(B, cache.n_kv_heads, nb, top_groups, dtype=torch.int32, device=q.device)
-        L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
+        if causal_routing:
+            L.hga_route_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.csum, cache.gsum,
+                               cache.t_cap, t_hist, S, cidx, gidx)
+        else:
+            L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
+        cache.keep_last_query_block(q)
         o = torch.empty_like(q)
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
         L.hga_attend_fwd(shape, q, cache.k, cache.v, cache.t_cap, t_hist, S, gidx, o, lse)
@@ -163,16 +188,19 @@ class _HGAAttentionFn(torch.autograd.Function):
                          device=q.device)
         L.hga_attend_bwd(shape, q, cache.k, cache.v, o, lse, d_o.contiguous(), cache.t_cap, t_hist, S, gidx,
                          dq, dk, dv, ws)
-        return dq, dk, dv, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None
 
 
 def hga_attention(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cache: HGAKVCache,
-                  top_chunks: int = 16, top_groups: int = 64, softmax_scale: Optional[float] = None):
+                  top_chunks: int = 16, top_groups: int = 64, softmax_scale: Optional[float] = None,
+                  causal_routing: bool = False):
     """Routed attention of one active segment against the cache's history plus itself.
 
     q [B,Hq,S,d], k_seg/v_seg [B,Hkv,S,d] (the segment's keys/values, written into
     the cache at its current length).  Returns (o [B,Hq,S,d], group_idx).  Call
     cache.commit(S) once the segment's backward is done to turn it into history.
+    causal_routing: route each block with the block before it (hga_route_causal);
+    then every segment written to the cache must be routed that way.
     """
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    return _HGAAttentionFn.apply(q, k_seg, v_seg, cache, top_chunks, top_groups, scale)
+    return _HGAAttentionFn.apply(q, k_seg, v_seg, cache, top_chunks, top_groups, scale, causal_routing)

@@ -63,11 +63,16 @@ def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm((got - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
 
 
-def check_route_unit(w, gs, cs, b, kvh, j, cidx_row, gidx_row) -> int:
-    """Acceptance of the GPU selection of one unit against oracle scores.
+def check_route_unit(w, gs, cs, b, kvh, j, cidx_row, gidx_row, causal=False, q_prev=None) -> int:
+    """Acceptance of the GPU selection of one unit against oracle scores (block
+    routing, or causal routing with the previous segment's last block q_prev).
     Returns the number of near-tie exemptions; raises AssertionError on failure."""
     J = w.t_hist // 64 + j
-    rows = ora.block_rows(w.q, b, kvh, j, w.group_size)
+    if causal and J == 0:
+        assert all(x == -1 for x in cidx_row) and all(x == -1 for x in gidx_row)
+        return 0
+    rows = (ora.causal_routing_rows(w.q, q_prev, b, kvh, j, w.group_size) if causal
+            else ora.block_rows(w.q, b, kvh, j, w.group_size))
     sig = ora.block_scores(rows, cs[b, kvh, :J])
     csel = [int(x) for x in cidx_row if x >= 0]
     assert all(x == -1 for x in cidx_row[len(csel):]), "chunk list not -1 padded at the end"

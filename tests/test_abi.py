@@ -28,7 +28,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert set(names) == {"hga_build_summaries", "hga_route", "hga_attend_fwd",
+    assert set(names) == {"hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd",
                           "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_attend_bwd_timed",
                           "hga_status_string"}
     for n in names:
@@ -82,6 +82,20 @@ def test_route_validation(L):
     s = _shape()
     s.softmax_scale = float("nan")
     assert _route(L, s) == -2
+
+
+def test_route_causal_validation(L):
+    s = _shape()
+    f = L.hga_route_causal
+
+    def call(q_prev=A, t_hist=14336, q=A, shape=s):
+        return f(ctypes.byref(shape), q, q_prev, A, A, 16384, t_hist, 2048, A, A, None, None, None)
+    assert call(q_prev=None) == -1                    # history present: the previous block is needed
+    assert call(q_prev=M) == -5
+    assert call(q=None) == -1
+    assert call(t_hist=100) == -2
+    assert call(shape=_shape(n_q_heads=24)) == -3
+    assert f(None, A, A, A, A, 16384, 0, 2048, A, A, None, None, None) == -1
 
 
 def test_summaries_validation(L):
