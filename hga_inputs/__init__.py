@@ -123,6 +123,58 @@ def prev_query_block(*, seed: int, batch: int, n_q_heads: int, head_dim: int,
     return _cast(_normal(r, (batch, n_q_heads, QBLOCK, head_dim)), dtype)
 
 
+@dataclasses.dataclass
+class DecodeWorkload:
+    """One generation step: every sequence adds one token at its own position."""
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    t_cap: int
+    top_chunks: int
+    top_groups: int
+    dtype: str
+    softmax_scale: float
+    pos: np.ndarray               # [B] int64: the new token's position (negative: idle slot)
+    q: np.ndarray                 # [B,Hq,d] the new tokens' queries
+    k_cache: np.ndarray           # [B,Hkv,t_cap,d] (holds the new tokens' keys at pos)
+    v_cache: np.ndarray
+
+    @property
+    def group_size(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+def decode_batch(*, seed: int, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, t_cap: int,
+                 pos, top_chunks: int, top_groups: int, dtype: str = "bf16", chunk_mean_var: float = 0.0,
+                 name: str = "decode") -> DecodeWorkload:
+    """Q, K, V ~ N(0, 1) over the whole cache (positions after a sequence's pos are
+    filled too: they must not matter); optional per-(sequence, KV head, chunk) key
+    means ~ N(0, chunk_mean_var * I)."""
+    rq, rk, rv, rs = _streams(seed, 4)
+    q = _normal(rq, (batch, n_q_heads, head_dim))
+    k = _normal(rk, (batch, n_kv_heads, t_cap, head_dim))
+    v = _normal(rv, (batch, n_kv_heads, t_cap, head_dim))
+    if chunk_mean_var > 0.0:
+        mu = _normal(rs, (batch, n_kv_heads, t_cap // CHUNK, head_dim)) * np.float32(math.sqrt(chunk_mean_var))
+        k += np.repeat(mu, CHUNK, axis=2)
+    return DecodeWorkload(name=name, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                          head_dim=head_dim, t_cap=t_cap, top_chunks=top_chunks, top_groups=top_groups,
+                          dtype=dtype, softmax_scale=1.0 / math.sqrt(head_dim),
+                          pos=np.asarray(pos, np.int64), q=_cast(q, dtype), k_cache=_cast(k, dtype),
+                          v_cache=_cast(v, dtype))
+
+
+def decode_b8_ctx32k(seed: int = 66) -> DecodeWorkload:
+    """Generation at 32K context: 8 sequences of the Qwen3-8B layer shape, each adding
+    one token at a position in the last chunk of the 32,768-token cache (ragged
+    own-chunk lengths, the last one completes its chunk), block-structured keys."""
+    pos = [32767 - 9 * b for b in range(8)]
+    return decode_batch(seed=seed, batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, t_cap=32768, pos=pos,
+                        top_chunks=16, top_groups=64, chunk_mean_var=0.5, name="decode_b8_ctx32k")
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------

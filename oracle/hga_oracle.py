@@ -52,6 +52,18 @@ Where the pages leave a step open, this file takes the readings listed below
            which chunks were chosen.  The first block of a segment uses the last
            query block of the previous segment; the very first block of a
            sequence has no candidates either way.
+  R-decode (generation: the abstract on the adnankhan.ai note, "Raw Abstract /
+           Excerpt", and the seventnews section "检索：密集基线无退化" say HGA can
+           generate and that a serving implementation is in development; the
+           pages give no design) one new token per sequence at position pos:
+           its query block is that single position, so its rows are the G query
+           heads of the token; candidates are chunks 0 .. J-1 with J = pos // 64;
+           it attends the selected groups plus its own chunk up to and including
+           itself (positions 64J .. pos).  The routing is per token, so it is
+           strictly causal by construction.  When pos is the last position of a
+           chunk, that chunk's group and chunk summaries are built (R-sum) so the
+           next tokens can select it.  A negative pos marks an idle batch slot:
+           nothing selected, O = 0, LSE = -inf.
 
 Precision: inputs are float32 arrays whose values are exact in the workload
 dtype.  Everything is computed in float64 except the two pinned rounding
@@ -380,3 +392,77 @@ def dkdv_active_chunk(q, k_cache, v_cache, d_o, t_hist, group_idx, b, kvh, cc, s
         np.add.at(dk, tokens[m] - lo, dku[m])
         np.add.at(dv, tokens[m] - lo, dvu[m])
     return dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Generation: one new token per sequence (reading R-decode).  HGA can be used
+# for generation (adnankhan.ai note, "Raw Abstract / Excerpt"; seventnews,
+# "检索：密集基线无退化"); the pages give no design for it.
+# ---------------------------------------------------------------------------
+
+def decode_route_unit(q_tok, chunk_sum, group_sum, pos, b, kvh, top_chunks, top_groups, group_size):
+    """Routing of the token at position pos of sequence b for KV head kvh.
+    q_tok [B, Hq, d]: the new tokens' queries.  Returns route_rows' tuple."""
+    J = pos // CHUNK
+    h0 = kvh * group_size
+    rows = q_tok[b, h0:h0 + group_size].astype(np.float64)          # [G, d]
+    return route_rows(rows, chunk_sum, group_sum, J, b, kvh, top_chunks, top_groups)
+
+
+def decode_route(q_tok, chunk_sum, group_sum, pos, top_chunks, top_groups, group_size):
+    """chunk_idx [B, Hkv, k_c], group_idx [B, Hkv, k_g] (int32, ascending, -1 padded)
+    and the per-unit score tables; pos [B] (negative: idle slot)."""
+    B, Hkv = chunk_sum.shape[:2]
+    cidx = np.full((B, Hkv, top_chunks), -1, np.int32)
+    gidx = np.full((B, Hkv, top_groups), -1, np.int32)
+    tables = {}
+    for b in range(B):
+        if pos[b] < 0:
+            continue
+        for kvh in range(Hkv):
+            cs, gs, sig, gids, tau = decode_route_unit(q_tok, chunk_sum, group_sum, int(pos[b]), b, kvh,
+                                                       top_chunks, top_groups, group_size)
+            cidx[b, kvh, :len(cs)] = cs
+            gidx[b, kvh, :len(gs)] = gs
+            tables[(b, kvh)] = (sig, gids, tau)
+    return cidx, gidx, tables
+
+
+def decode_key_tokens(group_sel, pos):
+    """Positions the token at pos attends: the selected groups' tokens, then its own
+    chunk up to and including itself."""
+    J = pos // CHUNK
+    return np.concatenate([key_tokens(group_sel), np.arange(J * CHUNK, pos + 1)])
+
+
+def decode_attend(q_tok, k_cache, v_cache, pos, group_idx, scale, group_size):
+    """O [B, Hq, d] and LSE [B, Hq] (float64) of the new tokens."""
+    B, Hq, d = q_tok.shape
+    Hkv = k_cache.shape[1]
+    o = np.zeros((B, Hq, d), np.float64)
+    lse = np.full((B, Hq), -np.inf, np.float64)
+    for b in range(B):
+        if pos[b] < 0:
+            continue
+        for kvh in range(Hkv):
+            tok = decode_key_tokens(group_idx[b, kvh], int(pos[b]))
+            keys = k_cache[b, kvh][tok].astype(np.float64)
+            vals = v_cache[b, kvh][tok].astype(np.float64)
+            h0 = kvh * group_size
+            rows = q_tok[b, h0:h0 + group_size].astype(np.float64)
+            L = scale * (rows @ keys.T)
+            m = L.max(axis=1, keepdims=True)
+            lu = m[:, 0] + np.log(np.exp(L - m).sum(axis=1))
+            o[b, h0:h0 + group_size] = np.exp(L - lu[:, None]) @ vals
+            lse[b, h0:h0 + group_size] = lu
+    return o, lse
+
+
+def decode_summaries(k_cache, pos, dtype, group_sum, chunk_sum):
+    """Incremental summary update: for every sequence whose new token completes a
+    chunk ((pos + 1) % 64 == 0), build that chunk's group and chunk summaries."""
+    for b in range(k_cache.shape[0]):
+        p = int(pos[b])
+        if p >= 0 and (p + 1) % CHUNK == 0:
+            c0 = p + 1 - CHUNK
+            build_summaries(k_cache[b:b + 1], c0, c0 + CHUNK, dtype, group_sum[b:b + 1], chunk_sum[b:b + 1])
