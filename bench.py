@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
-                   choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k"])
+                   choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k",
+                            "decode_b8_ctx32k"],
+                   help="decode_b8_ctx32k times the generation path (hga_decode_route + hga_decode_attend)")
     p.add_argument("--routing", default="block", choices=["block", "causal"],
                    help="block: each block routes itself (hga_route); causal: the block before it routes it")
     p.add_argument("--mark-every", type=int, default=8,
@@ -109,12 +111,14 @@ def algorithmic_work(w, gidx):
     }
 
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "hga_step_ctx16k_hbm_traffic.json")
+PMC_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_hbm_traffic.json"),
+                 "decode_b8_ctx32k": os.path.join(ROOT, "profiles", "hga_decode_ctx32k_hbm_traffic.json")}
 CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 # kernel-name prefix -> step kernel (first match wins)
 KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_", "route"), ("attend_fwd_", "attend_fwd"),
                ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_plan_", "attend_bwd_plan"),
-               ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv")]
+               ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv"),
+               ("decode_kernel", "decode_step")]
 
 
 def _short_name(name):
@@ -180,9 +184,9 @@ def measured_traffic(kernel, workload):
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when no
     summary exists for this workload or the kernels changed since it was taken."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(PMC_SUMMARIES[workload]) as f:
             summ = json.load(f)
-    except (OSError, ValueError):
+    except (KeyError, OSError, ValueError):
         return None
     if summ.get("workload") != workload or summ.get("source_sha256") != kernel_source_digest():
         return None
@@ -231,6 +235,143 @@ def cpu_baseline(w, q_prev=None, min_seconds=10.0, max_reps=5):
                       f"{len(times)} repetitions, median {t:.2f} s"}
 
 
+# ------------------------------------------------------------------ generation
+DECODE_METRIC = "HGA decode tokens/s at 32K ctx (one new token per sequence per step); % of HBM roofline"
+
+
+def decode_work(w, cidx, gidx):
+    """Algorithmic HBM bytes of one generation step (one launch): the query heads,
+    every candidate chunk summary, the selected chunks' group summaries, the K and V
+    rows of every attended token, O and LSE, the selection, and the summaries of
+    each chunk a new token completes."""
+    import numpy as np
+    B, Hq, Hkv, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    el = 2 if w.dtype == "bf16" else 4
+    pos = np.asarray(w.pos)
+    live = pos >= 0
+    J = np.where(live, pos // 64, 0)
+    q_bytes = int(live.sum()) * Hq * d * el
+    nc = (cidx >= 0).sum(axis=-1)                     # [B, Hkv]
+    ng = (gidx >= 0).sum(axis=-1)
+    summ = Hkv * int(J.sum()) * d * el + int((8 * nc).sum()) * d * el
+    local = np.where(live, pos - 64 * J + 1, 0)
+    tokens = int((8 * ng).sum()) + Hkv * int(local.sum())
+    done = int(((pos + 1) % 64 == 0)[live].sum()) * Hkv * 9 * d * el
+    total = 2 * q_bytes + summ + tokens * d * el * 2 + int(live.sum()) * Hq * 4 + (cidx.size + gidx.size) * 4 + done
+    return {"decode_step": {"bytes": float(total), "flops": 0.0}}
+
+
+def cpu_baseline_decode(w, min_seconds=10.0, max_reps=50):
+    """The CPU oracle on the same generation step (route, attention, summary update)."""
+    import numpy as np
+    from oracle import hga_oracle as ora
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, H, T, d = w.k_cache.shape
+    gs = np.zeros((B, H, T // 8, d), np.float32)
+    cs = np.zeros((B, H, T // 64, d), np.float32)
+    ora.build_summaries(w.k_cache, 0, T, w.dtype, gs, cs)            # the prompt: untimed, as on the GPU
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
+        t0 = time.perf_counter()
+        _, gidx, _ = ora.decode_route(w.q, cs, gs, w.pos, w.top_chunks, w.top_groups, w.group_size)
+        ora.decode_attend(w.q, w.k_cache, w.v_cache, w.pos, gidx, w.softmax_scale, w.group_size)
+        ora.decode_summaries(w.k_cache, w.pos, w.dtype, gs, cs)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    n_tok = int((np.asarray(w.pos) >= 0).sum())
+    return {"value": n_tok / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full generation step of this workload ({n_tok} tokens: route, attention, summary "
+                      f"update), {len(times)} repetitions, median {t * 1e3:.1f} ms"}
+
+
+def main_decode(args):
+    import numpy as np
+    import torch
+    import hga_inputs as hi
+    import sparse_long_context_hga_amd as hga
+
+    w = hi.decode_b8_ctx32k()
+    print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
+          f"t_cap={w.t_cap} pos={list(w.pos)} k_c={w.top_chunks} k_g={w.top_groups}", file=sys.stderr, flush=True)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda x: torch.from_numpy(x).to("cuda").to(dt).contiguous()   # noqa: E731
+    shape = hga.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.top_chunks, w.top_groups,
+                           w.dtype, w.softmax_scale)
+    q, k, v = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+    B, Hkv, T, d = k.shape
+    gsum = torch.zeros(B, Hkv, T // 8, d, dtype=dt, device="cuda")
+    csum = torch.zeros(B, Hkv, T // 64, d, dtype=dt, device="cuda")
+    pos = torch.tensor(w.pos, dtype=torch.int32, device="cuda")
+    cidx = torch.empty(B, Hkv, w.top_chunks, dtype=torch.int32, device="cuda")
+    gidx = torch.empty(B, Hkv, w.top_groups, dtype=torch.int32, device="cuda")
+    o = torch.empty(B, w.n_q_heads, d, dtype=dt, device="cuda")
+    lse = torch.empty(B, w.n_q_heads, dtype=torch.float32, device="cuda")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration: fill then scale-copy of {n} bytes", file=sys.stderr, flush=True)
+        del src, dst
+    hga.hga_build_summaries(shape, k, T, 0, T, gsum, csum)    # the prompt's summaries: untimed
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    marked = list(range(0, args.steps, max(1, args.mark_every)))
+    ev = {i: [mk() for _ in range(2)] for i in marked}
+    for e in [x for i in marked for x in ev[i]]:
+        e.record(stream)
+    torch.cuda.synchronize()
+
+    def step(i):
+        se = ev.get(i)
+        if se: se[0].record(stream)
+        hga.hga_decode_step(shape, q, k, v, csum, gsum, T, pos, cidx, gidx, o, lse)
+        if se: se[1].record(stream)
+
+    for i in range(args.warmup):
+        step(-1 - i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
+    kern_ms = {"decode_step": avg((ev[i][0], ev[i][1]) for i in marked)}
+    work = decode_work(w, cidx.cpu().numpy(), gidx.cpu().numpy())
+    kernels = {}
+    for kname, ms in kern_ms.items():
+        gbs = work[kname]["bytes"] / (ms * 1e-3) / 1e9
+        kernels[kname] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(kern_ms, key=lambda kk: kern_ms[kk])
+    ach = work[dom]["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, w.name), "kernel": dom}
+    n_tok = int((np.asarray(w.pos) >= 0).sum())
+    out = {
+        "metric": DECODE_METRIC, "value": round(n_tok / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "t_cap": w.t_cap, "positions": [int(x) for x in w.pos],
+                   "top_chunks": w.top_chunks, "top_groups": w.top_groups, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "kernel_timing": f"HIP events around the step's one launch on {len(marked)} of the {args.steps} timed steps",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -238,7 +379,7 @@ def main():
         if not args.copy_calibration_mib:
             raise SystemExit("--traffic-summary needs the --copy-calibration-mib of the profiled run")
         summ = traffic_summary(*args.traffic_summary, args.copy_calibration_mib, args.workload)
-        with open(PMC_SUMMARY, "w") as f:
+        with open(PMC_SUMMARIES[args.workload], "w") as f:
             json.dump(summ, f, indent=1)
         print(json.dumps(summ, indent=1))
         return
@@ -255,6 +396,8 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     hga.lib()
+    if args.workload.startswith("decode"):
+        return main_decode(args)
     w = make_workload(args.workload)
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
           f"t_hist={w.t_hist} S={w.seg_len} k_c={w.top_chunks} k_g={w.top_groups}", file=sys.stderr, flush=True)

@@ -210,6 +210,59 @@ int hga_attend_bwd_timed(const hga_shape* shape, const void* q, const void* k_ca
                          void* dq, void* dk_active, void* dv_active, void* workspace,
                          size_t workspace_bytes, void* const* events, void* stream);
 
+/*
+ * Generation: one new token per sequence per call.  The pages say HGA can be
+ * used for generation and that a serving implementation is in development
+ * (adnankhan.ai note, "Raw Abstract / Excerpt"; seventnews, "检索：密集基线无退化"),
+ * without a design.  This library treats the new token at position pos[b] of
+ * sequence b as a query block of one position:
+ *   rows       = its Hq/Hkv query heads of KV head g
+ *   candidates = chunks 0 .. J-1, J = pos[b] / 64 (every complete earlier chunk)
+ *   selection  = as hga_route (max over the rows, top-k_c chunks, their groups,
+ *                top-k_g groups, ties to the lower id, ascending, -1 padded)
+ *   keys       = the selected groups' tokens plus its own chunk up to and
+ *                including itself (positions 64J .. pos[b])
+ *   summaries  = when pos[b] is the last position of its chunk (pos % 64 == 63),
+ *                that chunk's group and chunk summaries are written exactly as
+ *                hga_build_summaries would, so the next tokens can select it
+ * Per-token routing depends on nothing after the token (strictly causal).
+ *
+ *   q          [B, Hq, d]               the new tokens' queries
+ *   pos        [B] int32, DEVICE memory  position of each sequence's new token; its
+ *              K/V must already be in the cache there.  An entry outside
+ *              [0, t_cap) marks an idle slot: its chunk_idx/group_idx rows are -1,
+ *              its o rows 0 and its lse -inf.
+ *   chunk_sum, group_sum, k_cache, v_cache: as for the segment calls (t_cap);
+ *              routing reads summary rows of chunks < J only.
+ *   chunk_idx  [B, Hkv, k_c], group_idx [B, Hkv, k_g] int32
+ *   o          [B, Hq, d], lse [B, Hq] float32
+ * No workspace.  Requires t_cap a multiple of 64 with t_cap/64 <= HGA_MAX_CHUNKS.
+ */
+
+/* hga_decode_step -- routing, attention and the summary update in one launch.
+ * chunk_sum / group_sum are read (rows of chunks < J) and updated (row J of a
+ * completed chunk).  chunk_idx / group_idx may be NULL (then not written). */
+int hga_decode_step(const hga_shape* shape, const void* q, const void* k_cache,
+                    const void* v_cache, void* chunk_sum, void* group_sum, int64_t t_cap,
+                    const int32_t* pos, int32_t* chunk_idx, int32_t* group_idx, void* o,
+                    float* lse, void* stream);
+
+/* hga_decode_route -- the selection alone (chunk_score / group_score optional, as
+ * in hga_route). */
+int hga_decode_route(const hga_shape* shape, const void* q, const void* chunk_sum,
+                     const void* group_sum, int64_t t_cap, const int32_t* pos,
+                     int32_t* chunk_idx, int32_t* group_idx, float* chunk_score,
+                     float* group_score, void* stream);
+
+/* hga_decode_attend -- the attention alone, over a given selection (group_idx as
+ * hga_decode_route writes it: valid ids below 8J first, then -1; an id outside
+ * that range ends the list).  group_sum and chunk_sum (both or neither) receive
+ * the summaries of completed chunks as in hga_decode_step. */
+int hga_decode_attend(const hga_shape* shape, const void* q, const void* k_cache,
+                      const void* v_cache, int64_t t_cap, const int32_t* pos,
+                      const int32_t* group_idx, void* o, float* lse, void* group_sum,
+                      void* chunk_sum, void* stream);
+
 /* Static description of a status code. */
 const char* hga_status_string(int status);
 

@@ -62,6 +62,9 @@ SIGNATURES = {
                                       _P, ctypes.c_size_t, _P]),
     "hga_attend_bwd_timed": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                             _P, ctypes.c_size_t, _P, _P]),
+    "hga_decode_step": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
+    "hga_decode_route": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
+    "hga_decode_attend": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "hga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -163,6 +166,33 @@ def hga_attend_bwd_timed(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_ca
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(d_o),
         t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(dq), _ptr(dk_active), _ptr(dv_active),
         _ptr(workspace), workspace.numel() * workspace.element_size(), handles, _stream(stream)))
+
+
+def hga_decode_step(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    chunk_sum: torch.Tensor, group_sum: torch.Tensor, t_cap: int, pos: torch.Tensor,
+                    chunk_idx: Optional[torch.Tensor], group_idx: Optional[torch.Tensor], o: torch.Tensor,
+                    lse: torch.Tensor, stream=None) -> None:
+    _check("hga_decode_step", lib().hga_decode_step(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap,
+        _ptr(pos), _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def hga_decode_route(shape: HgaShape, q: torch.Tensor, chunk_sum: torch.Tensor, group_sum: torch.Tensor,
+                     t_cap: int, pos: torch.Tensor, chunk_idx: torch.Tensor, group_idx: torch.Tensor,
+                     chunk_score: Optional[torch.Tensor] = None, group_score: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    _check("hga_decode_route", lib().hga_decode_route(
+        ctypes.byref(shape), _ptr(q), _ptr(chunk_sum), _ptr(group_sum), t_cap, _ptr(pos), _ptr(chunk_idx),
+        _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _stream(stream)))
+
+
+def hga_decode_attend(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      t_cap: int, pos: torch.Tensor, group_idx: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                      group_sum: Optional[torch.Tensor] = None, chunk_sum: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    _check("hga_decode_attend", lib().hga_decode_attend(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(pos), _ptr(group_idx), _ptr(o),
+        _ptr(lse), _ptr(group_sum), _ptr(chunk_sum), _stream(stream)))
 
 
 def hga_status_string(status: int) -> str:

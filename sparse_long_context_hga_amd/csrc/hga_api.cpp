@@ -146,6 +146,58 @@ static int attend_bwd_impl(const hga_shape* shape, const void* q, const void* k_
                                            (hipStream_t)stream, (const hipEvent_t*)events));
 }
 
+int hga_decode_route(const hga_shape* shape, const void* q, const void* chunk_sum, const void* group_sum,
+                     int64_t t_cap, const int32_t* pos, int32_t* chunk_idx, int32_t* group_idx,
+                     float* chunk_score, float* group_score, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, 0, 0, d);
+  if (st != HGA_OK) return st;
+  if (t_cap / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
+  if (!q || !chunk_sum || !group_sum || !pos || (d.kc > 0 && !chunk_idx) || (d.kg > 0 && !group_idx))
+    return HGA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(chunk_sum) || !aligned16(group_sum) ||
+      (chunk_idx && !aligned16(chunk_idx)) || (group_idx && !aligned16(group_idx)) ||
+      (chunk_score && !aligned16(chunk_score)) || (group_score && !aligned16(group_score)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, true, false, q, nullptr, nullptr, chunk_sum,
+                                       group_sum, pos, chunk_idx, group_idx, chunk_score, group_score, nullptr,
+                                       nullptr, nullptr, nullptr, (hipStream_t)stream));
+}
+
+int hga_decode_attend(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                      int64_t t_cap, const int32_t* pos, const int32_t* group_idx, void* o, float* lse,
+                      void* group_sum, void* chunk_sum, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, 0, 0, d);
+  if (st != HGA_OK) return st;
+  if (!q || !k_cache || !v_cache || !pos || !o || !lse || (d.kg > 0 && !group_idx)) return HGA_ERR_NULL;
+  if ((group_sum == nullptr) != (chunk_sum == nullptr)) return HGA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      (group_idx && !aligned16(group_idx)) || (group_sum && !aligned16(group_sum)) ||
+      (chunk_sum && !aligned16(chunk_sum)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, false, true, q, k_cache, v_cache, nullptr,
+                                       nullptr, pos, nullptr, const_cast<int32_t*>(group_idx), nullptr, nullptr,
+                                       o, lse, group_sum, chunk_sum, (hipStream_t)stream));
+}
+
+int hga_decode_step(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                    void* chunk_sum, void* group_sum, int64_t t_cap, const int32_t* pos, int32_t* chunk_idx,
+                    int32_t* group_idx, void* o, float* lse, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, 0, 0, d);
+  if (st != HGA_OK) return st;
+  if (t_cap / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !chunk_sum || !group_sum || !pos || !o || !lse) return HGA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(chunk_sum) || !aligned16(group_sum) || (chunk_idx && !aligned16(chunk_idx)) ||
+      (group_idx && !aligned16(group_idx)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, true, true, q, k_cache, v_cache, chunk_sum,
+                                       group_sum, pos, chunk_idx, group_idx, nullptr, nullptr, o, lse, group_sum,
+                                       chunk_sum, (hipStream_t)stream));
+}
+
 int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                    const void* o, const float* lse, const void* d_o, int64_t t_cap, int64_t t_hist,
                    int64_t seg_len, const int32_t* group_idx, void* dq, void* dk_active, void* dv_active,

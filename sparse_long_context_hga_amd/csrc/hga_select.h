@@ -1,0 +1,146 @@
+// Exact top-k selection of a work-group over orderable score keys (ties go to
+// the lower index; the result is written in ascending index order).  Used by the
+// routing kernels of the segment path and of the generation path.
+#pragma once
+
+#include "hga_device.h"
+
+namespace hga {
+namespace {
+
+constexpr int kRouteThreads = 256;   // threads of the segment path's routing work-groups
+constexpr int kMaxChunks = 8192;     // = HGA_MAX_CHUNKS
+constexpr int kMaxGroupCand = 512;   // 8 * max top_chunks
+
+// NT: threads of the calling work-group (a multiple of 64, at least 256).
+template <int NT>
+struct SelectShared {
+  uint32_t hist[256];
+  int scan[NT / 64];
+  int digit, above;
+};
+
+// Indices of the k largest keys[0..n) (ties -> lower index), written ascending to
+// out[0..min(k,n)).  Keys must be distinct from 0 for real candidates.  Returns
+// the number written.  All threads of the block must call it.
+template <int NT>
+__device__ int block_topk(const uint32_t* keys, int n, int k, int* out, SelectShared<NT>& sh) {
+  static_assert(NT >= 256 && NT % 64 == 0, "one thread per digit");
+  const int tid = threadIdx.x;
+  if (k <= 0 || n <= 0) return 0;
+  if (k >= n) {
+    for (int i = tid; i < n; i += NT) out[i] = i;
+    __syncthreads();
+    return n;
+  }
+  uint32_t prefix = 0, pmask = 0;
+  int kk = k;  // rank (1-based) of the k-th key among keys matching `prefix`
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) sh.hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = keys[i];
+      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // Suffix sums over digits: thread t looks at digit 255 - t.
+    const int hv = tid < 256 ? (int)sh.hist[255 - tid] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<NT>(hv, sh.scan, tot);  // keys in higher digits
+    if (tid < 256 && ex < kk && kk <= ex + hv) {
+      sh.digit = 255 - tid;
+      sh.above = ex;
+    }
+    __syncthreads();
+    prefix |= ((uint32_t)sh.digit) << shift;
+    pmask |= 255u << shift;
+    kk -= sh.above;
+    __syncthreads();
+  }
+  // Threshold key T = prefix: take every key > T and the kk lowest-index keys == T.
+  const int per = (n + NT - 1) / NT;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int n_eq = 0;
+  for (int i = lo; i < hi; ++i) n_eq += keys[i] == prefix;
+  int tot;
+  int eq_before = block_exclusive_scan<NT>(n_eq, sh.scan, tot);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t u = keys[i];
+      if (u > prefix) ++n_sel;
+      else if (u == prefix) { n_sel += e < kk; ++e; }
+    }
+  }
+  int sel_before = block_exclusive_scan<NT>(n_sel, sh.scan, tot);
+  {
+    int e = eq_before, o = sel_before;
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t u = keys[i];
+      bool take = false;
+      if (u > prefix) take = true;
+      else if (u == prefix) { take = e < kk; ++e; }
+      if (take) out[o++] = i;
+    }
+  }
+  __syncthreads();
+  return k;
+}
+
+// The same selection for small candidate sets (n <= kRankMax): candidate i is taken
+// iff fewer than k candidates beat it.  With v = key << 32 | (2^32 - 1 - index),
+// "j beats i" (a larger key, or an equal key at a lower index) is v_j > v_i: one
+// 64-bit compare per pair.  Thread t owns the contiguous candidates [t*per, t*per +
+// per), so an exclusive scan of the per-thread counts places the selected ids in
+// ascending order.  pk: LDS scratch of at least n + 1 entries.
+constexpr int kRankMax = 1024;
+template <int NT>
+__device__ int block_topk_rank(const uint32_t* keys, int n, int k, int* out, SelectShared<NT>& sh, uint64_t* pk) {
+  static_assert(4 * NT >= kRankMax, "at most 4 candidates per thread");
+  const int tid = threadIdx.x;
+  if (k <= 0 || n <= 0) return 0;
+  const int n16 = (n + 15) & ~15;   // zero padding never beats a real candidate (key > 0)
+  for (int i = tid; i < n16; i += NT)
+    pk[i] = i < n ? ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
+  __syncthreads();
+  const int per = (n + NT - 1) / NT;   // 1 .. 4
+  const int lo = tid * per, hi = min(n, lo + per);
+  uint64_t mine[4];
+  int beat[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mine[u] = lo + u < hi ? pk[lo + u] : ~0ull;
+  const uint4* pk4 = reinterpret_cast<const uint4*>(pk);
+  // 16 candidates per step: 8 broadcast reads in flight, then the compares (waves
+  // that own no candidate skip the loop).
+  for (int j = 0; lo < hi && j < n16 / 2; j += 8) {
+    uint4 kv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kv[e] = pk4[j + e];
+    if (per == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        beat[0] += ((((uint64_t)kv[e].y << 32) | kv[e].x) > mine[0]) + ((((uint64_t)kv[e].w << 32) | kv[e].z) > mine[0]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint64_t a0 = ((uint64_t)kv[e].y << 32) | kv[e].x, a1 = ((uint64_t)kv[e].w << 32) | kv[e].z;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) beat[u] += (a0 > mine[u]) + (a1 > mine[u]);
+      }
+    }
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cnt += (lo + u < hi) && beat[u] < k;
+  int tot;
+  int o = block_exclusive_scan<NT>(cnt, sh.scan, tot);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if ((lo + u < hi) && beat[u] < k) out[o++] = lo + u;
+  __syncthreads();
+  return tot;
+}
+
+}  // namespace
+}  // namespace hga

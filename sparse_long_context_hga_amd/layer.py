@@ -11,6 +11,9 @@ stream; every step of the computation runs in libhga.so.
   hga_attention    -- autograd op for one active segment: forward routes and
                       attends; backward returns dQ, dK, dV of the active segment
                       only (the history is detached).
+  HGADecoder       -- generation over an HGAKVCache: one new token per sequence
+                      per step (per-token routing, attention, and the summaries of
+                      a chunk once its last token is in).
 """
 from __future__ import annotations
 
@@ -204,3 +207,37 @@ def hga_attention(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cac
     """
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
     return _HGAAttentionFn.apply(q, k_seg, v_seg, cache, top_chunks, top_groups, scale, causal_routing)
+
+
+class HGADecoder:
+    """Generation steps over `cache`: every sequence adds one token per step.
+
+    step(q, k_new, v_new, pos) writes the new tokens' K/V at positions pos (a [B]
+    int32 device tensor; a negative entry marks an idle slot), routes each token
+    with its own query heads, attends, and builds the summaries of every chunk
+    whose last token this step wrote.  Returns (o [B,Hq,d], lse [B,Hq], group_idx).
+    The cache's `length` is not used: positions come from `pos`.
+    """
+
+    def __init__(self, cache: HGAKVCache, n_q_heads: int, top_chunks: int = 16, top_groups: int = 64,
+                 softmax_scale: Optional[float] = None):
+        B, Hkv, d = cache.batch, cache.n_kv_heads, cache.head_dim
+        dev = cache.k.device
+        scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d)
+        self.cache = cache
+        self.shape = L.make_shape(B, n_q_heads, Hkv, d, top_chunks, top_groups, _dtype_name(cache.dtype), scale)
+        self.cidx = torch.empty(B, Hkv, top_chunks, dtype=torch.int32, device=dev)
+        self.gidx = torch.empty(B, Hkv, top_groups, dtype=torch.int32, device=dev)
+        self.o = torch.empty(B, n_q_heads, d, dtype=cache.dtype, device=dev)
+        self.lse = torch.empty(B, n_q_heads, dtype=torch.float32, device=dev)
+        self._b = torch.arange(B, device=dev)
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor):
+        c = self.cache
+        live = pos >= 0
+        bi, p = self._b[live], pos[live].long()
+        c.k[bi, :, p] = k_new[live].to(c.dtype)
+        c.v[bi, :, p] = v_new[live].to(c.dtype)
+        L.hga_decode_step(self.shape, q.contiguous(), c.k, c.v, c.csum, c.gsum, c.t_cap, pos, self.cidx,
+                          self.gidx, self.o, self.lse)
+        return self.o, self.lse, self.gidx

@@ -73,19 +73,26 @@ def check_route_unit(w, gs, cs, b, kvh, j, cidx_row, gidx_row, causal=False, q_p
         return 0
     rows = (ora.causal_routing_rows(w.q, q_prev, b, kvh, j, w.group_size) if causal
             else ora.block_rows(w.q, b, kvh, j, w.group_size))
+    return check_selection(rows, J, gs, cs, b, kvh, cidx_row, gidx_row, w.top_chunks, w.top_groups,
+                           (b, kvh, j))
+
+
+def check_selection(rows, J, gs, cs, b, kvh, cidx_row, gidx_row, top_chunks, top_groups, where) -> int:
+    """Acceptance of a GPU selection made by the given query rows over candidate
+    chunks [0, J), against the oracle's scores.  Returns the near-tie exemptions."""
     sig = ora.block_scores(rows, cs[b, kvh, :J])
     csel = [int(x) for x in cidx_row if x >= 0]
     assert all(x == -1 for x in cidx_row[len(csel):]), "chunk list not -1 padded at the end"
     assert csel == sorted(csel), "chunk ids not ascending"
-    ok, ex1 = ora.selection_accepted(csel, list(range(J)), sig, w.top_chunks, NEAR_TIE_REL)
-    assert ok, f"chunk selection rejected at unit {(b, kvh, j)}: {csel}"
+    ok, ex1 = ora.selection_accepted(csel, list(range(J)), sig, top_chunks, NEAR_TIE_REL)
+    assert ok, f"chunk selection rejected at unit {where}: {csel}"
     gids = [8 * c + u for c in csel for u in range(8)]
     tau = ora.block_scores(rows, gs[b, kvh, gids]) if gids else np.zeros(0, np.float32)
     gsel = [int(x) for x in gidx_row if x >= 0]
     assert all(x == -1 for x in gidx_row[len(gsel):]), "group list not -1 padded at the end"
     assert gsel == sorted(gsel), "group ids not ascending"
-    ok, ex2 = ora.selection_accepted(gsel, gids, tau, w.top_groups, NEAR_TIE_REL)
-    assert ok, f"group selection rejected at unit {(b, kvh, j)}: {gsel}"
+    ok, ex2 = ora.selection_accepted(gsel, gids, tau, top_groups, NEAR_TIE_REL)
+    assert ok, f"group selection rejected at unit {where}: {gsel}"
     return ex1 + ex2
 
 

@@ -1,0 +1,256 @@
+"""GPU parity of the generation path (hga_decode_route / hga_decode_attend): one new
+token per sequence, routed by its own query heads, attending its selected groups
+plus its own chunk up to itself; summaries of a chunk built when its last token
+arrives.
+
+Cases span ragged positions (first chunk, mid-chunk, chunk-completing, idle
+slots), every GQA width, both head sizes, both dtypes, a zero budget, budgets
+above the candidate count, and a context long enough for the radix select
+(more than 1,024 candidate chunks).  Routing is checked with the near-tie
+acceptance rule; attention on the oracle's own selection; summaries bit-exactly.
+Expected values come only from the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hga_inputs as hi
+from oracle import hga_oracle as ora
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "bf16_g4_d128": dict(seed=71, batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128, t_cap=2048,
+                         pos=[2047, 1000, 63, -1], top_chunks=5, top_groups=27, chunk_mean_var=0.5),
+    "bf16_g8_d128": dict(seed=72, batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128, t_cap=4096,
+                         pos=[4078, 3007], top_chunks=16, top_groups=64),
+    "bf16_g1_d64": dict(seed=73, batch=3, n_q_heads=2, n_kv_heads=2, head_dim=64, t_cap=1024,
+                        pos=[1023, 511, 70], top_chunks=3, top_groups=13),
+    "bf16_g2_budget_exceeds": dict(seed=74, batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128, t_cap=512,
+                                   pos=[200, 130], top_chunks=8, top_groups=64),
+    "bf16_zero_budget": dict(seed=75, batch=2, n_q_heads=4, n_kv_heads=1, head_dim=128, t_cap=512,
+                             pos=[300, 447], top_chunks=0, top_groups=0),
+    "f32_g4_d64": dict(seed=76, batch=2, n_q_heads=4, n_kv_heads=1, head_dim=64, t_cap=1024,
+                       pos=[767, 900], top_chunks=4, top_groups=19, dtype="f32"),
+    "f32_g1_d128": dict(seed=77, batch=2, n_q_heads=2, n_kv_heads=2, head_dim=128, t_cap=512,
+                        pos=[5, 319], top_chunks=2, top_groups=11, dtype="f32"),
+    "bf16_long_ctx_radix": dict(seed=78, batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, t_cap=131072,
+                                pos=[131066], top_chunks=16, top_groups=64, chunk_mean_var=0.5),
+}
+
+
+@pytest.fixture(scope="module")
+def chk():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    from tests import hga_check
+    import sparse_long_context_hga_amd as hga
+    hga.lib()
+    return hga_check
+
+
+def _shape(w):
+    import sparse_long_context_hga_amd as hga
+    return hga.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.top_chunks, w.top_groups, w.dtype,
+                          w.softmax_scale)
+
+
+def _summaries(w):
+    B, H, T, d = w.k_cache.shape
+    gs = np.zeros((B, H, T // 8, d), np.float32)
+    cs = np.zeros((B, H, T // 64, d), np.float32)
+    ora.build_summaries(w.k_cache, 0, T, w.dtype, gs, cs)
+    return gs, cs
+
+
+class Dev:
+    """Device buffers of one generation step."""
+
+    def __init__(self, chk, w, gs, cs):
+        import sparse_long_context_hga_amd as hga
+        self.shape = _shape(w)
+        self.q = chk.to_dev(w.q, w.dtype)
+        self.k = chk.to_dev(w.k_cache, w.dtype)
+        self.v = chk.to_dev(w.v_cache, w.dtype)
+        self.gs = chk.to_dev(gs, w.dtype)
+        self.cs = chk.to_dev(cs, w.dtype)
+        self.pos = torch.tensor(w.pos, dtype=torch.int32, device="cuda")
+        B, Hkv = w.batch, w.n_kv_heads
+        self.cidx = torch.full((B, Hkv, w.top_chunks), 7, dtype=torch.int32, device="cuda")
+        self.gidx = torch.full((B, Hkv, w.top_groups), 7, dtype=torch.int32, device="cuda")
+        self.cscore = torch.zeros((B, Hkv, w.top_chunks), dtype=torch.float32, device="cuda")
+        self.o = torch.full((B, w.n_q_heads, w.head_dim), 5.0, dtype=self.q.dtype, device="cuda")
+        self.lse = torch.zeros((B, w.n_q_heads), dtype=torch.float32, device="cuda")
+        self.w = w
+
+    def route(self):
+        import sparse_long_context_hga_amd as hga
+        hga.hga_decode_route(self.shape, self.q, self.cs, self.gs, self.w.t_cap, self.pos, self.cidx, self.gidx,
+                             chunk_score=self.cscore)
+
+    def attend(self, gidx=None, gs=None, cs=None):
+        import sparse_long_context_hga_amd as hga
+        hga.hga_decode_attend(self.shape, self.q, self.k, self.v, self.w.t_cap, self.pos,
+                              self.gidx if gidx is None else gidx, self.o, self.lse, gs, cs)
+
+    def step(self):
+        import sparse_long_context_hga_amd as hga
+        hga.hga_decode_step(self.shape, self.q, self.k, self.v, self.cs, self.gs, self.w.t_cap, self.pos,
+                            self.cidx, self.gidx, self.o, self.lse)
+
+
+def _check_route(chk, w, gs, cs, cidx, gidx, cscore=None):
+    G = w.group_size
+    exempt = 0
+    for b in range(w.batch):
+        p = int(w.pos[b])
+        for kvh in range(w.n_kv_heads):
+            if p < 0:
+                assert np.all(cidx[b, kvh] == -1) and np.all(gidx[b, kvh] == -1)
+                continue
+            rows = w.q[b, kvh * G:(kvh + 1) * G].astype(np.float64)
+            J = p // 64
+            exempt += chk.check_selection(rows, J, gs, cs, b, kvh, cidx[b, kvh], gidx[b, kvh], w.top_chunks,
+                                          w.top_groups, (b, kvh))
+            if cscore is not None and J > 0:
+                sig = ora.block_scores(rows, cs[b, kvh, :J])
+                for i, c in enumerate(cidx[b, kvh]):
+                    if c >= 0:
+                        assert abs(cscore[b, kvh, i] - sig[c]) <= 1e-5 * max(1.0, abs(sig[c]))
+    return exempt
+
+
+def _check_attend(chk, w, o_gpu, lse_gpu, gidx):
+    o, lse = ora.decode_attend(w.q, w.k_cache, w.v_cache, w.pos, gidx, w.softmax_scale, w.group_size)
+    idle = np.asarray(w.pos) < 0
+    assert np.all(o_gpu[idle] == 0) and np.all(lse_gpu[idle] == -np.inf)
+    eo = float(np.max(np.abs(o_gpu[~idle] - o[~idle])))
+    el = float(np.max(np.abs(lse_gpu[~idle] - lse[~idle])))
+    print(f"O max-abs {eo:.3e} LSE max-abs {el:.3e}", flush=True)
+    assert eo <= chk.TOL_O[w.dtype] and el <= chk.TOL_O[w.dtype]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_route_accepted(chk, name):
+    w = hi.decode_batch(name=name, **CASES[name])
+    print(f"case {name} pos={list(w.pos)}", flush=True)
+    gs, cs = _summaries(w)
+    d = Dev(chk, w, gs, cs)
+    d.route()
+    torch.cuda.synchronize()
+    exempt = _check_route(chk, w, gs, cs, d.cidx.cpu().numpy(), d.gidx.cpu().numpy(), d.cscore.cpu().numpy())
+    print(f"near-tie exemptions: {exempt}")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_attend_on_oracle_selection_and_summaries(chk, name):
+    w = hi.decode_batch(name=name, **CASES[name])
+    print(f"case {name} pos={list(w.pos)}", flush=True)
+    gs, cs = _summaries(w)
+    _, ogidx, _ = ora.decode_route(w.q, cs, gs, w.pos, w.top_chunks, w.top_groups, w.group_size)
+    # summary tables with the rows of every chunk a new token completes cleared: the
+    # attention call must rebuild exactly those rows
+    gs_in, cs_in = gs.copy(), cs.copy()
+    done = [(b, int(w.pos[b]) // 64) for b in range(w.batch) if w.pos[b] >= 0 and (w.pos[b] + 1) % 64 == 0]
+    for b, c in done:
+        gs_in[b, :, 8 * c:8 * c + 8] = 0
+        cs_in[b, :, c] = 0
+    d = Dev(chk, w, gs_in, cs_in)
+    d.attend(torch.from_numpy(ogidx).cuda(), d.gs, d.cs)
+    torch.cuda.synchronize()
+    _check_attend(chk, w, chk.to_np(d.o), d.lse.cpu().numpy(), ogidx)
+    np.testing.assert_array_equal(chk.to_np(d.gs), gs)
+    np.testing.assert_array_equal(chk.to_np(d.cs), cs)
+    print(f"summaries rebuilt for {done}")
+
+
+@pytest.mark.parametrize("name", ["bf16_g4_d128", "bf16_g1_d64", "f32_g4_d64"])
+def test_decode_step_equals_route_then_attend(chk, name):
+    """The one-launch step gives bit-exactly what the two separate calls give (same
+    selection, output, LSE and summaries), and repeats bit-exactly."""
+    w = hi.decode_batch(name=name, **CASES[name])
+    print(f"case {name} pos={list(w.pos)}", flush=True)
+    gs, cs = _summaries(w)
+    done = [(b, int(w.pos[b]) // 64) for b in range(w.batch) if w.pos[b] >= 0 and (w.pos[b] + 1) % 64 == 0]
+    for b, c in done:                   # rows the step must rebuild
+        gs[b, :, 8 * c:8 * c + 8] = 0
+        cs[b, :, c] = 0
+    d1, d2 = Dev(chk, w, gs, cs), Dev(chk, w, gs, cs)
+    d1.route()
+    d1.attend(None, d1.gs, d1.cs)
+    d2.step()
+    torch.cuda.synchronize()
+    for x, y in ((d1.cidx, d2.cidx), (d1.gidx, d2.gidx), (d1.o, d2.o), (d1.lse, d2.lse), (d1.gs, d2.gs),
+                 (d1.cs, d2.cs)):
+        assert torch.equal(x, y)
+    first = [t.clone() for t in (d2.gidx, d2.o, d2.lse)]
+    d2.step()
+    torch.cuda.synchronize()
+    for x, y in zip(first, (d2.gidx, d2.o, d2.lse)):
+        assert torch.equal(x, y)
+    _check_route(chk, w, *_summaries(w), d2.cidx.cpu().numpy(), d2.gidx.cpu().numpy())
+    _check_attend(chk, w, chk.to_np(d2.o), d2.lse.cpu().numpy(), d2.gidx.cpu().numpy())
+
+
+def test_decode_b8_ctx32k(chk):
+    w = hi.decode_b8_ctx32k()
+    print(f"workload {w.name} pos={list(w.pos)}", flush=True)
+    gs, cs = _summaries(w)
+    d = Dev(chk, w, gs, cs)
+    d.step()
+    torch.cuda.synchronize()
+    cidx, gidx = d.cidx.cpu().numpy(), d.gidx.cpu().numpy()
+    exempt = _check_route(chk, w, gs, cs, cidx, gidx)
+    print(f"route accepted on all {w.batch * w.n_kv_heads} units, near-tie exemptions {exempt}", flush=True)
+    _check_attend(chk, w, chk.to_np(d.o), d.lse.cpu().numpy(), gidx)
+
+
+def test_generation_loop_through_the_decoder(chk):
+    """Tokens generated one by one through HGADecoder (K/V appended each step, ragged
+    positions crossing chunk boundaries): every step's selection is accepted and its
+    output matches the oracle; the summaries built on the way equal the bulk build."""
+    from sparse_long_context_hga_amd.layer import HGADecoder, HGAKVCache
+    import sparse_long_context_hga_amd as hga
+    B, Hq, Hkv, d, T = 2, 8, 2, 128, 512
+    w = hi.decode_batch(seed=79, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, t_cap=T, pos=[0, 0],
+                        top_chunks=3, top_groups=17, chunk_mean_var=0.5)
+    start = [250, 120]                       # sequence 0 crosses 255 -> 256, sequence 1 crosses 127 -> 128
+    n_steps = 10
+    cache = HGAKVCache(B, Hkv, d, T, torch.bfloat16)
+    k_dev = chk.to_dev(w.k_cache, "bf16")
+    v_dev = chk.to_dev(w.v_cache, "bf16")
+    for b in range(B):                       # the prompt: positions before start[b]
+        cache.k[b, :, :start[b]] = k_dev[b, :, :start[b]]
+        cache.v[b, :, :start[b]] = v_dev[b, :, :start[b]]
+        full = 64 * (start[b] // 64)
+        shape1 = hga.make_shape(1, Hq, Hkv, d, 3, 17, "bf16")
+        hga.hga_build_summaries(shape1, cache.k[b:b + 1], T, 0, full, cache.gsum[b:b + 1], cache.csum[b:b + 1])
+    dec = HGADecoder(cache, Hq, 3, 17)
+    rng = np.random.default_rng(5)
+    for s in range(n_steps):
+        pos = np.array([start[0] + s, start[1] + s])
+        q = hi.round_to_bf16(rng.standard_normal((B, Hq, d)).astype(np.float32))
+        k_new = np.stack([w.k_cache[b, :, pos[b]] for b in range(B)])
+        v_new = np.stack([w.v_cache[b, :, pos[b]] for b in range(B)])
+        o, lse, gidx = dec.step(chk.to_dev(q, "bf16"), chk.to_dev(k_new, "bf16"), chk.to_dev(v_new, "bf16"),
+                                torch.tensor(pos, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        # oracle view of this step: cache contents up to each sequence's position
+        ws = hi.DecodeWorkload(name="step", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, t_cap=T,
+                               top_chunks=3, top_groups=17, dtype="bf16", softmax_scale=1 / np.sqrt(d), pos=pos,
+                               q=q, k_cache=w.k_cache, v_cache=w.v_cache)
+        gs = np.zeros((B, Hkv, T // 8, d), np.float32)
+        cs = np.zeros((B, Hkv, T // 64, d), np.float32)
+        for b in range(B):
+            ora.build_summaries(w.k_cache[b:b + 1], 0, 64 * (pos[b] // 64), "bf16", gs[b:b + 1], cs[b:b + 1])
+        g_np = gidx.cpu().numpy()
+        _check_route(chk, ws, gs, cs, dec.cidx.cpu().numpy(), g_np)
+        _check_attend(chk, ws, chk.to_np(o), lse.cpu().numpy(), g_np)
+    final = [start[b] + n_steps for b in range(B)]
+    for b in range(B):
+        nf = final[b] // 64
+        gs = np.zeros((1, Hkv, T // 8, d), np.float32)
+        cs = np.zeros((1, Hkv, T // 64, d), np.float32)
+        ora.build_summaries(w.k_cache[b:b + 1], 0, 64 * nf, "bf16", gs, cs)
+        np.testing.assert_array_equal(chk.to_np(cache.gsum[b:b + 1]), gs)
+        np.testing.assert_array_equal(chk.to_np(cache.csum[b:b + 1]), cs)
