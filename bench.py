@@ -118,7 +118,7 @@ CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_", "route"), ("attend_fwd_", "attend_fwd"),
                ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_plan_", "attend_bwd_plan"),
                ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv"),
-               ("decode_kernel", "decode_step")]
+               ("decode_route_kernel", "decode_route"), ("decode_attend_kernel", "decode_attend")]
 
 
 def _short_name(name):
@@ -240,10 +240,11 @@ DECODE_METRIC = "HGA decode tokens/s at 32K ctx (one new token per sequence per 
 
 
 def decode_work(w, cidx, gidx):
-    """Algorithmic HBM bytes of one generation step (one launch): the query heads,
-    every candidate chunk summary, the selected chunks' group summaries, the K and V
-    rows of every attended token, O and LSE, the selection, and the summaries of
-    each chunk a new token completes."""
+    """Algorithmic HBM bytes of the two generation kernels for one step: routing reads
+    the query heads, every candidate chunk summary and the selected chunks' group
+    summaries and writes the selection; attention reads the query heads and the K
+    and V rows of every attended token, writes O and LSE, and the summaries of each
+    chunk that a new token completes."""
     import numpy as np
     B, Hq, Hkv, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     el = 2 if w.dtype == "bf16" else 4
@@ -253,12 +254,13 @@ def decode_work(w, cidx, gidx):
     q_bytes = int(live.sum()) * Hq * d * el
     nc = (cidx >= 0).sum(axis=-1)                     # [B, Hkv]
     ng = (gidx >= 0).sum(axis=-1)
-    summ = Hkv * int(J.sum()) * d * el + int((8 * nc).sum()) * d * el
+    route = q_bytes + Hkv * int(J.sum()) * d * el + int((8 * nc).sum()) * d * el + (cidx.size + gidx.size) * 4
     local = np.where(live, pos - 64 * J + 1, 0)
     tokens = int((8 * ng).sum()) + Hkv * int(local.sum())
     done = int(((pos + 1) % 64 == 0)[live].sum()) * Hkv * 9 * d * el
-    total = 2 * q_bytes + summ + tokens * d * el * 2 + int(live.sum()) * Hq * 4 + (cidx.size + gidx.size) * 4 + done
-    return {"decode_step": {"bytes": float(total), "flops": 0.0}}
+    attend = q_bytes + tokens * d * el * 2 + q_bytes + int(live.sum()) * Hq * 4 + gidx.size * 4 + done
+    return {"decode_route": {"bytes": float(route), "flops": 0.0},
+            "decode_attend": {"bytes": float(attend), "flops": 0.0}}
 
 
 def cpu_baseline_decode(w, min_seconds=10.0, max_reps=50):
@@ -311,6 +313,7 @@ def main_decode(args):
     gidx = torch.empty(B, Hkv, w.top_groups, dtype=torch.int32, device="cuda")
     o = torch.empty(B, w.n_q_heads, d, dtype=dt, device="cuda")
     lse = torch.empty(B, w.n_q_heads, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(hga.hga_decode_workspace_size(shape, T), dtype=torch.uint8, device="cuda")
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20)
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -324,7 +327,7 @@ def main_decode(args):
     stream = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
     marked = list(range(0, args.steps, max(1, args.mark_every)))
-    ev = {i: [mk() for _ in range(2)] for i in marked}
+    ev = {i: [mk() for _ in range(3)] for i in marked}
     for e in [x for i in marked for x in ev[i]]:
         e.record(stream)
     torch.cuda.synchronize()
@@ -332,8 +335,10 @@ def main_decode(args):
     def step(i):
         se = ev.get(i)
         if se: se[0].record(stream)
-        hga.hga_decode_step(shape, q, k, v, csum, gsum, T, pos, cidx, gidx, o, lse)
+        hga.hga_decode_route(shape, q, csum, gsum, T, pos, cidx, gidx, ws)
         if se: se[1].record(stream)
+        hga.hga_decode_attend(shape, q, k, v, T, pos, gidx, o, lse, ws, gsum, csum)
+        if se: se[2].record(stream)
 
     for i in range(args.warmup):
         step(-1 - i)
@@ -345,7 +350,8 @@ def main_decode(args):
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
-    kern_ms = {"decode_step": avg((ev[i][0], ev[i][1]) for i in marked)}
+    kern_ms = {"decode_route": avg((ev[i][0], ev[i][1]) for i in marked),
+               "decode_attend": avg((ev[i][1], ev[i][2]) for i in marked)}
     work = decode_work(w, cidx.cpu().numpy(), gidx.cpu().numpy())
     kernels = {}
     for kname, ms in kern_ms.items():
@@ -365,7 +371,7 @@ def main_decode(args):
                    "top_chunks": w.top_chunks, "top_groups": w.top_groups, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
-        "kernel_timing": f"HIP events around the step's one launch on {len(marked)} of the {args.steps} timed steps",
+        "kernel_timing": f"HIP events between the two calls on {len(marked)} of the {args.steps} timed steps",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w)

@@ -236,32 +236,38 @@ int hga_attend_bwd_timed(const hga_shape* shape, const void* q, const void* k_ca
  *              routing reads summary rows of chunks < J only.
  *   chunk_idx  [B, Hkv, k_c], group_idx [B, Hkv, k_g] int32
  *   o          [B, Hq, d], lse [B, Hq] float32
- * No workspace.  Requires t_cap a multiple of 64 with t_cap/64 <= HGA_MAX_CHUNKS.
+ *   workspace  device memory of at least hga_decode_workspace_size() bytes,
+ *              16-byte aligned and zero-filled before its first use.  Every call
+ *              leaves it ready for the next (its arrival counters return to zero),
+ *              so it is reused without clearing; calls that share a workspace
+ *              must not run concurrently.
+ * Requires t_cap a multiple of 64 with t_cap/64 <= HGA_MAX_CHUNKS.
  */
+size_t hga_decode_workspace_size(const hga_shape* shape, int64_t t_cap);
 
-/* hga_decode_step -- routing, attention and the summary update in one launch.
+/* hga_decode_step -- routing, attention and the summary update (two launches).
  * chunk_sum / group_sum are read (rows of chunks < J) and updated (row J of a
- * completed chunk).  chunk_idx / group_idx may be NULL (then not written). */
+ * completed chunk).  chunk_idx may be NULL (then not written). */
 int hga_decode_step(const hga_shape* shape, const void* q, const void* k_cache,
                     const void* v_cache, void* chunk_sum, void* group_sum, int64_t t_cap,
                     const int32_t* pos, int32_t* chunk_idx, int32_t* group_idx, void* o,
-                    float* lse, void* stream);
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* hga_decode_route -- the selection alone (chunk_score / group_score optional, as
  * in hga_route). */
 int hga_decode_route(const hga_shape* shape, const void* q, const void* chunk_sum,
                      const void* group_sum, int64_t t_cap, const int32_t* pos,
                      int32_t* chunk_idx, int32_t* group_idx, float* chunk_score,
-                     float* group_score, void* stream);
+                     float* group_score, void* workspace, size_t workspace_bytes, void* stream);
 
 /* hga_decode_attend -- the attention alone, over a given selection (group_idx as
- * hga_decode_route writes it: valid ids below 8J first, then -1; an id outside
- * that range ends the list).  group_sum and chunk_sum (both or neither) receive
+ * hga_decode_route writes it; an entry outside [0, 8J) is skipped, so no read
+ * leaves the token's history).  group_sum and chunk_sum (both or neither) receive
  * the summaries of completed chunks as in hga_decode_step. */
 int hga_decode_attend(const hga_shape* shape, const void* q, const void* k_cache,
                       const void* v_cache, int64_t t_cap, const int32_t* pos,
                       const int32_t* group_idx, void* o, float* lse, void* group_sum,
-                      void* chunk_sum, void* stream);
+                      void* chunk_sum, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* hga_status_string(int status);

@@ -62,9 +62,12 @@ SIGNATURES = {
                                       _P, ctypes.c_size_t, _P]),
     "hga_attend_bwd_timed": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                             _P, ctypes.c_size_t, _P, _P]),
-    "hga_decode_step": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
-    "hga_decode_route": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
-    "hga_decode_attend": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "hga_decode_workspace_size": (ctypes.c_size_t, [_SHAPE, _I64]),
+    "hga_decode_step": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                       _P]),
+    "hga_decode_route": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "hga_decode_attend": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                         _P]),
     "hga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -168,31 +171,41 @@ def hga_attend_bwd_timed(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_ca
         _ptr(workspace), workspace.numel() * workspace.element_size(), handles, _stream(stream)))
 
 
+def hga_decode_workspace_size(shape: HgaShape, t_cap: int) -> int:
+    return int(lib().hga_decode_workspace_size(ctypes.byref(shape), t_cap))
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def hga_decode_step(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     chunk_sum: torch.Tensor, group_sum: torch.Tensor, t_cap: int, pos: torch.Tensor,
-                    chunk_idx: Optional[torch.Tensor], group_idx: Optional[torch.Tensor], o: torch.Tensor,
-                    lse: torch.Tensor, stream=None) -> None:
+                    chunk_idx: Optional[torch.Tensor], group_idx: torch.Tensor, o: torch.Tensor,
+                    lse: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     _check("hga_decode_step", lib().hga_decode_step(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap,
-        _ptr(pos), _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), _stream(stream)))
+        _ptr(pos), _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
 
 
 def hga_decode_route(shape: HgaShape, q: torch.Tensor, chunk_sum: torch.Tensor, group_sum: torch.Tensor,
                      t_cap: int, pos: torch.Tensor, chunk_idx: torch.Tensor, group_idx: torch.Tensor,
-                     chunk_score: Optional[torch.Tensor] = None, group_score: Optional[torch.Tensor] = None,
-                     stream=None) -> None:
+                     workspace: torch.Tensor, chunk_score: Optional[torch.Tensor] = None,
+                     group_score: Optional[torch.Tensor] = None, stream=None) -> None:
     _check("hga_decode_route", lib().hga_decode_route(
         ctypes.byref(shape), _ptr(q), _ptr(chunk_sum), _ptr(group_sum), t_cap, _ptr(pos), _ptr(chunk_idx),
-        _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _stream(stream)))
+        _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
 
 
 def hga_decode_attend(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       t_cap: int, pos: torch.Tensor, group_idx: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-                      group_sum: Optional[torch.Tensor] = None, chunk_sum: Optional[torch.Tensor] = None,
-                      stream=None) -> None:
+                      workspace: torch.Tensor, group_sum: Optional[torch.Tensor] = None,
+                      chunk_sum: Optional[torch.Tensor] = None, stream=None) -> None:
     _check("hga_decode_attend", lib().hga_decode_attend(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(pos), _ptr(group_idx), _ptr(o),
-        _ptr(lse), _ptr(group_sum), _ptr(chunk_sum), _stream(stream)))
+        _ptr(lse), _ptr(group_sum), _ptr(chunk_sum), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def hga_status_string(status: int) -> str:

@@ -11,14 +11,21 @@
 // pos is the last position of a chunk, the chunk's group and chunk summaries are
 // built (same fixed fp32 tree as hga_build_summaries) so later tokens can pick it.
 //
-// One work-group of 512 threads per (sequence, KV head): a decode step has little
-// work per unit and nothing to share between units, so the unit's whole chain --
-// chunk scores, top-k_c, group scores, top-k_g, attention, summary update -- runs
-// in one work-group with its intermediate results in LDS, and a step is one
-// launch.  Rows (summaries, keys, values) are read by D/8 lanes each, 16 B per
-// lane, many rows in flight per thread; scores and attention are G-row GEMVs on
-// the vector ALUs in fp32 (not GEMM-shaped, so no MFMA).  Attention walks the key
-// list in tiles with an online softmax per head.
+// A step moves little data per (sequence, KV head) unit, and one compute unit
+// alone cannot keep enough HBM requests in flight to move it quickly, so each
+// unit is spread over many work-groups, and the last one to finish a phase
+// finishes it (an arrival counter per unit, reset by that work-group):
+//   route   work-group s scores candidate chunks 64s .. 64s+63 (16 lanes per
+//           summary row, 16 B each); the last one selects the top-k_c chunks,
+//           scores their groups and selects the top-k_g groups.
+//   attend  work-group 0 takes the own chunk, work-group s >= 1 the selected
+//           groups 8(s-1) .. 8s-1 (64 tokens, K and V rows read once); each
+//           leaves a partial (max, sum, unnormalised O); the last one merges.
+// Values that another work-group reads are written and read with device-scope
+// (agent) coherent accesses, and a work-group's own stores complete before it
+// arrives, so no cache-wide write-back or invalidation is needed.  Scores and
+// attention are G-row GEMVs on the vector ALUs in fp32 (not GEMM-shaped, so no
+// MFMA); selection uses ballot-counted bit searches on (score, index) keys.
 #include "hga_device.h"
 #include "hga_internal.h"
 #include "hga_select.h"
@@ -28,10 +35,10 @@
 namespace hga {
 namespace {
 
-constexpr int kDecThreads = 512;
+constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-
-enum : int { kRoute = 1, kAttend = 2 };
+constexpr int kSliceChunks = 64;   // candidate chunks scored per routing work-group
+constexpr int kSplitGroups = 8;    // groups (64 tokens) per attention work-group
 
 struct DecodeArgs {
   const void* q;          // [B, Hq, d]
@@ -42,17 +49,60 @@ struct DecodeArgs {
   void* csum_out;         // summary tables updated by the attention (nullable)
   void* gsum_out;
   const int32_t* pos;     // [B]
-  int32_t* cidx;          // [B, Hkv, k_c] (nullable in a fused step)
+  int32_t* cidx;          // [B, Hkv, k_c] (nullable)
   int32_t* gidx;          // [B, Hkv, k_g]
-  const int32_t* gidx_in; // attention only: the selection to attend
+  const int32_t* gidx_in; // attention: the selection to attend
   float* cscore;
   float* gscore;
   void* o;                // [B, Hq, d]
   float* lse;             // [B, Hq]
+  uint32_t* rcount;       // workspace: arrival counters [n_units]
+  uint32_t* acount;       //            [n_units]
+  uint64_t* cands;        //            best chunks of each slice [n_units][n_slices][k_c]
+  float* part;            //            partials [n_units][n_split][G*(d+2)]
   int64_t t_cap;
-  int Hq, Hkv, kc, kg, n_units;
+  int Hq, Hkv, kc, kg, n_units, n_slices, n_split;
   float scale_log2;       // softmax_scale * log2(e)
 };
+
+// ------------------------------------------------ exchange between work-groups
+// Device-scope coherent stores and loads (relaxed atomics at agent scope).
+__device__ __forceinline__ void put(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival of a work-group at its unit's counter, after its put()s; true in the last
+// of the n that arrive.  Every wave waits for its stores to complete first, so a
+// work-group that sees the final count also sees every put() of the others.  The
+// last one resets the counter for the next launch.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int n, int* flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_dma();   // s_waitcnt vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == (uint32_t)(n - 1);
+    if (*flag) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
 
 // 8 consecutive elements of a row (16 B of bf16, 32 B of fp32), widened to fp32.
 template <typename T> struct Vec8;
@@ -169,7 +219,10 @@ __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[P], int k) {
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < P; ++i) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[i] >= t));
-    if (cnt >= k) res = t;
+    if (cnt >= k) {
+      res = t;
+      if (cnt == k) break;   // exactly k at or above: any larger threshold keeps the same set
+    }
   }
   return res;
 }
@@ -210,7 +263,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int kvh, floa
   }
 }
 
-// key[r] = orderable(max over the G heads of q . row r) for rows [0, n) given by
+// key_out(r, orderable(max over the G heads of q . row r)) for rows [0, n) given by
 // row_src(r), NP rows per thread in flight per round.
 template <typename T, int D, int G, int NP, typename RowSrc, typename KeyOut>
 __device__ __forceinline__ void score_rows(const float (&qv)[G][8], int n, const RowSrc& row_src,
@@ -242,38 +295,55 @@ __device__ __forceinline__ void score_rows(const float (&qv)[G][8], int n, const
   }
 }
 
-template <typename T, int D, int G>
-struct DecodeShared {
-  static constexpr int LPR = D / 8, RPP = kDecThreads / LPR;
-  static constexpr int NPA = sizeof(T) == 2 ? 8 : 4;        // attention rows per thread per tile
-  static constexpr int TT = NPA * RPP;                       // tokens per attention tile
-  uint32_t ckeys[kMaxChunks + 4];
+struct RouteShared {
+  uint32_t ckeys[kSliceChunks];  // this work-group's chunk scores
   uint32_t gkeys[kMaxGroupCand + 4];
   int csel[64];
-  int gsel[kMaxGroupCand];      // route: selected slots; attention: the group ids to attend
-  float s[G][TT];               // logits, then probabilities, of one tile
-  float alpha[G];               // rescale of the running output per head
-  float red[kDecWaves][G][D];   // cross-wave sum of P V
-  float stat[G][2];             // running max and sum per head (log2 domain)
-  float gs[8][D];               // unscaled group sums of a completed chunk
-  uint64_t win[kDecWaves * 64]; // each wave's best chunk candidates (k_c per wave)
-  uint64_t fin[64];             // the selected chunks, best first
-  int nsel;
+  int gsel[kMaxGroupCand];
+  uint64_t win[kDecWaves * 64];  // each wave's best chunk candidates (k_c per wave)
+  uint64_t fin[64];              // the selected chunks, best first
+  uint32_t cscr[64];             // score keys of csel
+  int nsel, flag;
 };
 
-// Top-k_c (1 <= k_c <= 64) of the chunk keys[0 .. J): each wave selects the best
-// k_c of the chunks c = tid + 512 i its lanes own (P per lane), wave 0 the best k_c
-// of those (P2 per lane), stored in ascending chunk order to csel.  Returns their
-// number (all threads).
-template <int P, int P2, typename S>
-__device__ __forceinline__ int select_chunks(S& sm, int J, int kc) {
+// Wave 0: the selected chunks fin[0 .. n) (any order) to csel / cscr in ascending
+// chunk order (rank = number of selected chunks with a lower index).
+__device__ __forceinline__ void sort_selected(RouteShared& sm, int n) {
+  const int lane = threadIdx.x & 63;
+  if (lane < n) {
+    const uint64_t x = sm.fin[lane];
+    const int idx = cand_index(x);
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) rank += j < n && cand_index(sm.fin[j]) < idx;
+    sm.csel[rank] = idx;
+    sm.cscr[rank] = (uint32_t)(x >> 32);
+  }
+  if (lane == 0) sm.nsel = n;
+}
+
+// Top-k_c (1 <= k_c <= 64) of N candidates (cand_at(i), i < N): wave 0 alone
+// (P = N/64 per lane, N <= 512), or each wave over P per lane (i = tid + 256 p)
+// and then wave 0 over the waves' best (P2 per lane).  The result goes to csel in
+// ascending chunk order; returns its size (all threads).
+template <int P, typename F>
+__device__ __forceinline__ int select_one_wave(RouteShared& sm, int N, int kc, const F& cand_at) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    uint64_t v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) v[i] = lane + 64 * i < N ? cand_at(lane + 64 * i) : 0;
+    sort_selected(sm, wave_select<P>(v, kc, sm.fin));
+  }
+  __syncthreads();
+  return sm.nsel;
+}
+template <int P, int P2, typename F>
+__device__ __forceinline__ int select_two_stage(RouteShared& sm, int N, int kc, const F& cand_at) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   uint64_t v[P];
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const int c = tid + kDecThreads * i;
-    v[i] = c < J ? cand(sm.ckeys[c], c) : 0;
-  }
+  for (int i = 0; i < P; ++i) v[i] = tid + kDecThreads * i < N ? cand_at(tid + kDecThreads * i) : 0;
   uint64_t* mine = sm.win + w * kc;
   const int m = wave_select<P>(v, kc, mine);
   for (int i = m + lane; i < kc; i += 64) mine[i] = 0;
@@ -281,35 +351,29 @@ __device__ __forceinline__ int select_chunks(S& sm, int J, int kc) {
   if (w == 0) {
     uint64_t u[P2];
 #pragma unroll
-    for (int q = 0; q < P2; ++q) {
-      const int i = lane + 64 * q;
-      u[q] = i < kDecWaves * kc ? sm.win[i] : 0;
-    }
-    const int n = wave_select<P2>(u, kc, sm.fin);
-    if (lane < n) {
-      const int idx = cand_index(sm.fin[lane]);
-      int rank = 0;
-      for (int j = 0; j < n; ++j) rank += cand_index(sm.fin[j]) < idx;
-      sm.csel[rank] = idx;
-    }
-    if (lane == 0) sm.nsel = n;
+    for (int q = 0; q < P2; ++q) u[q] = lane + 64 * q < kDecWaves * kc ? sm.win[lane + 64 * q] : 0;
+    sort_selected(sm, wave_select<P2>(u, kc, sm.fin));
   }
   __syncthreads();
   return sm.nsel;
 }
-
-template <int P, typename S>
-__device__ __forceinline__ int select_chunks_p(S& sm, int J, int kc) {
-  if (kc <= 8) return select_chunks<P, 1>(sm, J, kc);
-  if (kc <= 16) return select_chunks<P, 2>(sm, J, kc);
-  if (kc <= 32) return select_chunks<P, 4>(sm, J, kc);
-  return select_chunks<P, 8>(sm, J, kc);
+template <typename F>
+__device__ __forceinline__ int select_chunks(RouteShared& sm, int N, int kc, const F& cand_at) {
+  if (N <= 64) return select_one_wave<1>(sm, N, kc, cand_at);
+  if (N <= 128) return select_one_wave<2>(sm, N, kc, cand_at);
+  if (N <= 256) return select_one_wave<4>(sm, N, kc, cand_at);
+  if (N <= 512) return select_one_wave<8>(sm, N, kc, cand_at);
+  constexpr int P2 = 4;   // 4 waves x k_c <= 256 candidates
+  if (N <= 1024) return select_two_stage<4, P2>(sm, N, kc, cand_at);
+  if (N <= 2048) return select_two_stage<8, P2>(sm, N, kc, cand_at);
+  if (N <= 4096) return select_two_stage<16, P2>(sm, N, kc, cand_at);
+  return select_two_stage<32, P2>(sm, N, kc, cand_at);
 }
 
 // Top-k_g of the group keys[0 .. n) (n <= 512) by wave 0, stored in ascending slot
 // order (= ascending group id) to out.  Returns their number (all threads).
-template <int P, typename S>
-__device__ __forceinline__ int select_groups(S& sm, int n, int kg, int* out) {
+template <int P>
+__device__ __forceinline__ int select_groups(RouteShared& sm, int n, int kg, int* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (w == 0) {
     uint64_t v[P];   // lane l holds slots P l .. P l + P - 1
@@ -335,119 +399,123 @@ __device__ __forceinline__ int select_groups(S& sm, int n, int kg, int* out) {
   return sm.nsel;
 }
 
-template <typename T, int D, int G, int MODE>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
-  using S = DecodeShared<T, D, G>;
-  constexpr int LPR = S::LPR, RPP = S::RPP, NPA = S::NPA, TT = S::TT;
-  constexpr int NPR = sizeof(T) == 2 ? 16 : 8;               // scoring rows per thread in flight
-  __shared__ __align__(16) S sm;
+// ---------------------------------------------------------------- routing
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void decode_route_kernel(DecodeArgs a) {
+  constexpr int NPR = sizeof(T) == 2 ? 4 : 2;   // rows per thread in flight (16 B each)
+  __shared__ __align__(16) RouteShared sm;
+  const int unit = blockIdx.x % a.n_units, slice = blockIdx.x / a.n_units;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int p = a.pos[b];
+  const bool active = p >= 0 && p < a.t_cap;
+  const int J = active ? p / kChunk : 0;
+  const int tid = threadIdx.x;
+  const int64_t n_chunks = a.t_cap / kChunk;
+  const T* cs = (const T*)a.csum + (int64_t)unit * n_chunks * D;
+  const T* gs = (const T*)a.gsum + (int64_t)unit * (a.t_cap / kGroup) * D;
+  uint64_t* cands = a.cands + (int64_t)unit * a.n_slices * a.kc;
 
-  const int unit = blockIdx.x;
-  if (unit >= a.n_units) return;
+  // ---- every work-group: its 64 candidate chunks, keeping their best k_c
+  float qv[G][8];
+  const int c0 = slice * kSliceChunks;
+  if (c0 < J && a.kc > 0) {
+    const int nrows = min(kSliceChunks, J - c0);
+    load_q<T, D, G>(a, b, kvh, qv, 1.0f);
+    score_rows<T, D, G, NPR>(qv, nrows, [&](int r) { return cs + (int64_t)(c0 + r) * D; },
+                             [&](int r, uint32_t key) { sm.ckeys[r] = key; });
+    __syncthreads();
+    if (tid < 64) {
+      uint64_t v[1] = {tid < nrows ? cand(sm.ckeys[tid], c0 + tid) : 0};
+      const int m = wave_select<1>(v, a.kc, sm.fin);
+      if (tid < a.kc) put(cands + slice * a.kc + tid, tid < m ? sm.fin[tid] : 0ull);
+    }
+  }
+  if (!arrive_last(a.rcount + unit, a.n_slices, &sm.flag)) return;
+
+  // ---- the last work-group of the unit: top-k_c, group scores, top-k_g
+  const int N = a.kc > 0 ? (J + kSliceChunks - 1) / kSliceChunks * a.kc : 0;
+  const int nc = N == 0 ? 0 : select_chunks(sm, N, a.kc, [&](int i) { return get(cands + i); });
+  const int ng_cand = 8 * nc;
+  if (ng_cand > 0 && a.kg > 0) {
+    load_q<T, D, G>(a, b, kvh, qv, 1.0f);
+    score_rows<T, D, G, 2 * NPR>(qv, ng_cand, [&](int r) { return gs + (int64_t)(8 * sm.csel[r >> 3] + (r & 7)) * D; },
+                           [&](int r, uint32_t key) { sm.gkeys[r] = key; });
+  }
+  __syncthreads();
+  const int ng = (ng_cand == 0 || a.kg == 0) ? 0
+                 : ng_cand <= 64            ? select_groups<1>(sm, ng_cand, a.kg, sm.gsel)
+                 : ng_cand <= 128           ? select_groups<2>(sm, ng_cand, a.kg, sm.gsel)
+                 : ng_cand <= 256           ? select_groups<4>(sm, ng_cand, a.kg, sm.gsel)
+                                            : select_groups<8>(sm, ng_cand, a.kg, sm.gsel);
+  if (a.cidx != nullptr) {
+    for (int i = tid; i < a.kc; i += kDecThreads) {
+      a.cidx[(int64_t)unit * a.kc + i] = i < nc ? sm.csel[i] : -1;
+      if (a.cscore) a.cscore[(int64_t)unit * a.kc + i] = i < nc ? key_score(sm.cscr[i]) : -INFINITY;
+    }
+  }
+  for (int i = tid; i < a.kg; i += kDecThreads) {
+    const int slot = i < ng ? sm.gsel[i] : 0;
+    a.gidx[(int64_t)unit * a.kg + i] = i < ng ? 8 * sm.csel[slot >> 3] + (slot & 7) : -1;
+    if (a.gscore) a.gscore[(int64_t)unit * a.kg + i] = i < ng ? key_score(sm.gkeys[slot]) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- attention
+template <typename T, int D, int G>
+struct AttendShared {
+  float s[G][kChunk];                 // logits, then probabilities
+  float red[kDecWaves][G][D];         // cross-wave sum of P V
+  float ml[G][2];                     // max and sum per head (log2 domain)
+  int gid[kSplitGroups];              // this split's groups
+  float wm[1 + kMaxGroupCand / kSplitGroups][G];   // merge: max, then weight, per split
+  float wl[1 + kMaxGroupCand / kSplitGroups][G];   // merge: sum per split
+  __align__(16) T ktile[kChunk][D];   // the own chunk's keys (summary update)
+  float gs[8][D];                     // unscaled group sums of a completed chunk
+  int flag;
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void decode_attend_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 8, RPP = kDecThreads / LPR, NP = kChunk / RPP;   // passes over 64 tokens
+  constexpr int PART = G * (D + 2);
+  __shared__ __align__(16) AttendShared<T, D, G> sm;
+  const int unit = blockIdx.x % a.n_units, split = blockIdx.x / a.n_units;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int p = a.pos[b];
   const bool active = p >= 0 && p < a.t_cap;
   const int J = active ? p / kChunk : 0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int e = tid % LPR, rr = tid / LPR;
-
-  // ---------------------------------------------------------------- routing
-  int ng = 0;   // groups to attend (their ids in sm.gsel[0 .. ng))
-  if constexpr ((MODE & kRoute) != 0) {
-    const int64_t n_chunks = a.t_cap / kChunk;
-    const T* cs = (const T*)a.csum + (int64_t)unit * n_chunks * D;
-    const T* gs = (const T*)a.gsum + (int64_t)unit * (a.t_cap / kGroup) * D;
-    float qv[G][8];
-    if (J > 0) {
-      load_q<T, D, G>(a, b, kvh, qv, 1.0f);
-      score_rows<T, D, G, NPR>(qv, J, [&](int r) { return cs + (int64_t)r * D; },
-                               [&](int r, uint32_t key) { sm.ckeys[r] = key; });
-    }
-    __syncthreads();
-    const int nc = (J == 0 || a.kc == 0) ? 0
-                   : J <= kDecThreads     ? select_chunks_p<1>(sm, J, a.kc)
-                   : J <= 4 * kDecThreads ? select_chunks_p<4>(sm, J, a.kc)
-                                          : select_chunks_p<16>(sm, J, a.kc);
-    const int ng_cand = 8 * nc;
-    if (ng_cand > 0)
-      score_rows<T, D, G, 4>(qv, ng_cand,
-                             [&](int r) { return gs + (int64_t)(8 * sm.csel[r >> 3] + (r & 7)) * D; },
-                             [&](int r, uint32_t key) { sm.gkeys[r] = key; });
-    __syncthreads();
-    ng = (ng_cand == 0 || a.kg == 0) ? 0
-         : ng_cand <= 64  ? select_groups<1>(sm, ng_cand, a.kg, sm.gsel)
-         : ng_cand <= 128 ? select_groups<2>(sm, ng_cand, a.kg, sm.gsel)
-         : ng_cand <= 256 ? select_groups<4>(sm, ng_cand, a.kg, sm.gsel)
-                          : select_groups<8>(sm, ng_cand, a.kg, sm.gsel);   // ascending slots = ascending ids
-    if (a.cidx != nullptr) {
-      for (int i = tid; i < a.kc; i += kDecThreads) {
-        a.cidx[(int64_t)unit * a.kc + i] = i < nc ? sm.csel[i] : -1;
-        if (a.cscore) a.cscore[(int64_t)unit * a.kc + i] = i < nc ? key_score(sm.ckeys[sm.csel[i]]) : -INFINITY;
-      }
-    }
-    // slots -> group ids, in place (each thread rewrites the entries it reads)
-    int gid[kMaxGroupCand / kDecThreads + 1];
-    float gsc[kMaxGroupCand / kDecThreads + 1];
-#pragma unroll
-    for (int u = 0; u * kDecThreads < kMaxGroupCand; ++u) {
-      const int i = tid + u * kDecThreads;
-      const int slot = i < ng ? sm.gsel[i] : 0;
-      gid[u] = 8 * sm.csel[slot >> 3] + (slot & 7);
-      gsc[u] = key_score(sm.gkeys[slot]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u * kDecThreads < kMaxGroupCand; ++u) {
-      const int i = tid + u * kDecThreads;
-      if (i < ng) sm.gsel[i] = gid[u];
-      if (i < a.kg && a.gidx != nullptr) {
-        a.gidx[(int64_t)unit * a.kg + i] = i < ng ? gid[u] : -1;
-        if (a.gscore) a.gscore[(int64_t)unit * a.kg + i] = i < ng ? gsc[u] : -INFINITY;
-      }
-    }
-    __syncthreads();
-  } else {
-    // the selection to attend, as the routing writes it: valid ids (before the own
-    // chunk) first, then -1; anything else ends the list, so no read leaves the history
-    if (active) {
-      for (int i = tid; i < a.kg; i += kDecThreads) sm.gsel[i] = a.gidx_in[(int64_t)unit * a.kg + i];
-    }
-    __syncthreads();
-    if (active) {
-      while (ng < a.kg && sm.gsel[ng] >= 0 && sm.gsel[ng] < kGroup * J) ++ng;
-    }
-  }
-  if constexpr ((MODE & kAttend) == 0) return;
-
-  // ---------------------------------------------------------------- attention
-  T* o = (T*)a.o + ((int64_t)b * a.Hq + kvh * G) * D;
-  float* lse = a.lse + (int64_t)b * a.Hq + kvh * G;
-  if (!active) {
-    for (int i = tid; i < G * D; i += kDecThreads) store_elem(o + i, 0.f);
-    if (tid < G) lse[tid] = -INFINITY;
-    return;
-  }
   const T* kb = (const T*)a.k + (int64_t)unit * a.t_cap * D;
   const T* vb = (const T*)a.v + (int64_t)unit * a.t_cap * D;
-  const int n_sel = kGroup * ng;
-  const int n_tok = n_sel + (p - kChunk * J + 1);
-  auto tok_pos = [&](int i) __attribute__((always_inline)) -> int64_t {
-    return i < n_sel ? (int64_t)kGroup * sm.gsel[i / kGroup] + (i % kGroup) : (int64_t)kChunk * J + (i - n_sel);
-  };
-  float qv[G][8];
-  load_q<T, D, G>(a, b, kvh, qv, a.scale_log2);
-  float acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;    // wave g < G keeps head g's running statistics
 
-  for (int t0 = 0; t0 < n_tok; t0 += TT) {
-    Vec8<T> kx[NPA], vx[NPA];
+  // Tokens of this split: split 0 = own chunk 64J .. p; split s = the valid ids among
+  // selected groups 8(s-1) .. 8s-1 (an id outside [0, 8J) is skipped, so no read
+  // leaves the history).
+  if (w == 0) {
+    int g = -1;
+    const int slot = kSplitGroups * (split - 1) + lane;
+    if (active && split > 0 && lane < kSplitGroups && slot < a.kg) g = a.gidx_in[(int64_t)unit * a.kg + slot];
+    const bool ok = g >= 0 && g < kGroup * J;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+    if (ok) sm.gid[lanes_below(m)] = g;
+    if (lane == 0) sm.flag = __builtin_popcountll(m);
+  }
+  __syncthreads();
+  const int n_tok = !active ? 0 : split == 0 ? p - kChunk * J + 1 : kGroup * sm.flag;
+  __syncthreads();
+  auto tok_pos = [&](int i) __attribute__((always_inline)) -> int64_t {
+    return split == 0 ? (int64_t)kChunk * J + i : (int64_t)kGroup * sm.gid[i / kGroup] + (i % kGroup);
+  };
+
+  float* part = a.part + ((int64_t)unit * a.n_split + split) * PART;
+  if (n_tok > 0) {
+    float qv[G][8];
+    load_q<T, D, G>(a, b, kvh, qv, a.scale_log2);
+    Vec8<T> kx[NP], vx[NP];
 #pragma unroll
-    for (int pp = 0; pp < NPA; ++pp) {
-      const int i = t0 + pp * RPP + rr;
+    for (int pp = 0; pp < NP; ++pp) {
+      const int i = pp * RPP + rr;
       if (i < n_tok) {
         const int64_t t = tok_pos(i);
         kx[pp].load(kb + t * D + 8 * e);
@@ -455,8 +523,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int pp = 0; pp < NPA; ++pp) {
-      const int i = t0 + pp * RPP + rr;
+    for (int pp = 0; pp < NP; ++pp) {
+      const int i = pp * RPP + rr;
       float f[8];
       kx[pp].get(f);
 #pragma unroll
@@ -465,151 +533,239 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) s = fmaf(qv[g][c], f[c], s);
         s = row_sum<LPR>(s);
-        if (e == 0) sm.s[g][pp * RPP + rr] = i < n_tok ? s : -INFINITY;
+        if (e == 0) sm.s[g][i] = i < n_tok ? s : -INFINITY;
       }
     }
     __syncthreads();
-    if (w < G) {   // online softmax of head w over this tile
-      float x[TT / 64];
-      float mt = -INFINITY;   // tile maximum
-#pragma unroll
-      for (int u = 0; u < TT / 64; ++u) {
-        x[u] = sm.s[w][u * 64 + lane];
-        mt = fmaxf(mt, x[u]);
-      }
-      mt = wave_max(mt);
-      const float m_new = fmaxf(m_run, mt);          // finite: the tile holds a valid key
-      float sum = 0.f;
-#pragma unroll
-      for (int u = 0; u < TT / 64; ++u) {
-        const float pe = x[u] == -INFINITY ? 0.f : fast_exp2(x[u] - m_new);
-        sm.s[w][u * 64 + lane] = pe;
-        sum += pe;
-      }
-      sum = wave_sum(sum);
-      const float al = fast_exp2(m_run - m_new);     // 0 on the first tile
-      l_run = l_run * al + sum;
-      m_run = m_new;
-      if (lane == 0) sm.alpha[w] = al;
+    for (int g = w; g < G; g += kDecWaves) {   // softmax pieces of head g (one token per lane)
+      const float x = sm.s[g][lane];
+      const float m = wave_max(x);              // finite: split holds a valid token
+      const float pe = x == -INFINITY ? 0.f : fast_exp2(x - m);
+      const float l = wave_sum(pe);
+      sm.s[g][lane] = pe;
+      if (lane == 0) { sm.ml[g][0] = m; sm.ml[g][1] = l; }
     }
     __syncthreads();
+    float acc[G][8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float al = sm.alpha[g];
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[g][c] *= al;
-    }
+      for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < NPA; ++pp) {
+    for (int pp = 0; pp < NP; ++pp) {
+      const int i = pp * RPP + rr;
       float f[8];
       vx[pp].get(f);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float pv = sm.s[g][pp * RPP + rr];
+        const float pv = sm.s[g][i];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(pv, f[c], acc[g][c]);
       }
     }
-    __syncthreads();   // the next tile overwrites sm.s
-  }
-  if (w < G && lane == 0) {
-    sm.stat[w][0] = m_run;
-    sm.stat[w][1] = l_run;
-  }
-  // rows -> one value per (head, column): lanes of a wave first, then the waves
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[g][c] = col_sum<LPR>(acc[g][c]);
-  if (lane < LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) sm.red[w][g][8 * e + c] = acc[g][c];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kDecThreads) {
-    const int g = idx / D, dd = idx % D;
-    float x = 0.f;
+      for (int c = 0; c < 8; ++c) acc[g][c] = col_sum<LPR>(acc[g][c]);
+    if (lane < LPR) {
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) x += sm.red[ww][g][dd];
-    store_elem(o + idx, x / sm.stat[g][1]);
-  }
-  if (tid < G) lse[tid] = (sm.stat[tid][0] + __log2f(sm.stat[tid][1])) * kLn2;
-
-  // ---------------------------------------------------------------- summaries
-  // The token completes its chunk: build the chunk's group and chunk summaries.
-  if (a.gsum_out != nullptr && p % kChunk == kChunk - 1) {
-    constexpr int TPG = D / 4;   // threads per group, 4 columns each
-    const int gg = tid / TPG, cq = tid % TPG;
-    if (gg < 8) {
-      const T* kp = kb + ((int64_t)kChunk * J + kGroup * gg) * D + 4 * cq;
-      T* gout = (T*)a.gsum_out + ((int64_t)unit * (a.t_cap / kGroup) + 8 * J + gg) * D + 4 * cq;
-      float x[8][4];
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[r][c] = widen(kp[(int64_t)r * D + c]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float col[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) col[r] = x[r][c];
-        const float s = tree8(col);
-        sm.gs[gg][4 * cq + c] = s;
-        store_elem(gout + c, s * 0.125f);
-      }
+        for (int c = 0; c < 8; ++c) sm.red[w][g][8 * e + c] = acc[g][c];
     }
     __syncthreads();
-    if (tid < D) {
-      float col[8];
+    for (int idx = tid; idx < G * D; idx += kDecThreads) {
+      const int g = idx / D, dd = idx % D;
+      float x = 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) col[u] = sm.gs[u][tid];
-      store_elem((T*)a.csum_out + ((int64_t)unit * (a.t_cap / kChunk) + J) * D + tid, tree8(col) * 0.015625f);
+      for (int ww = 0; ww < kDecWaves; ++ww) x += sm.red[ww][g][dd];
+      put(part + idx, x);
     }
+    if (tid < G) {
+      put(part + G * D + tid, sm.ml[tid][0]);
+      put(part + G * D + G + tid, sm.ml[tid][1]);
+    }
+
+    // Incremental summaries: the token completes its chunk.
+    if (split == 0 && n_tok == kChunk && a.gsum_out != nullptr) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int i = pp * RPP + rr;
+        float f[8];
+        kx[pp].get(f);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) store_elem(&sm.ktile[i][8 * e + c], f[c]);
+      }
+      __syncthreads();
+      constexpr int TPG = D / 4;   // threads per group, 4 columns each
+      const int gg = tid / TPG, cq = tid % TPG;
+      if (gg < 8) {
+        T* gout = (T*)a.gsum_out + ((int64_t)unit * (a.t_cap / kGroup) + 8 * J + gg) * D + 4 * cq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float col[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) col[r] = widen(sm.ktile[8 * gg + r][4 * cq + c]);
+          const float s = tree8(col);
+          sm.gs[gg][4 * cq + c] = s;
+          store_elem(gout + c, s * 0.125f);
+        }
+      }
+      __syncthreads();
+      if (tid < D) {
+        float col[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) col[u] = sm.gs[u][tid];
+        store_elem((T*)a.csum_out + ((int64_t)unit * (a.t_cap / kChunk) + J) * D + tid, tree8(col) * 0.015625f);
+      }
+    }
+  } else if (tid < G) {
+    put(part + G * D + tid, -INFINITY);   // empty split
+    put(part + G * D + G + tid, 0.f);
+  }
+  if (!arrive_last(a.acount + unit, a.n_split, &sm.flag)) return;
+
+  // ---- the last work-group of the unit merges the partials: per (split, head) the
+  // weight 2^(m_s - M) / L, then O = sum of weight * O_s (8 splits' loads in flight)
+  T* o = (T*)a.o + ((int64_t)b * a.Hq + kvh * G) * D;
+  float* lse = a.lse + (int64_t)b * a.Hq + kvh * G;
+  if (!active) {
+    for (int idx = tid; idx < G * D; idx += kDecThreads) store_elem(o + idx, 0.f);
+    if (tid < G) lse[tid] = -INFINITY;
+    return;
+  }
+  const float* pu = a.part + (int64_t)unit * a.n_split * PART;
+  constexpr int OPT = (G * D + kDecThreads - 1) / kDecThreads;   // outputs per thread
+  constexpr int SB = 16;                                          // splits per round of loads
+  float ov[SB][OPT];                                              // the first SB splits' O values
+#pragma unroll
+  for (int u = 0; u < SB; ++u)
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int idx = tid + j * kDecThreads;
+      ov[u][j] = u < a.n_split && idx < G * D ? get(pu + u * PART + idx) : 0.f;
+    }
+  for (int i = tid; i < a.n_split * G; i += kDecThreads) {
+    const int s2 = i / G, g = i % G;
+    sm.wm[s2][g] = get(pu + s2 * PART + G * D + g);
+    sm.wl[s2][g] = get(pu + s2 * PART + G * D + G + g);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY, L = 0.f;
+    for (int s2 = 0; s2 < a.n_split; ++s2) M = fmaxf(M, sm.wm[s2][tid]);
+    for (int s2 = 0; s2 < a.n_split; ++s2) {
+      const float l = sm.wl[s2][tid];
+      const float wgt = l > 0.f ? fast_exp2(sm.wm[s2][tid] - M) : 0.f;
+      sm.wm[s2][tid] = wgt;
+      L = fmaf(wgt, l, L);
+    }
+    for (int s2 = 0; s2 < a.n_split; ++s2) sm.wm[s2][tid] /= L;
+    lse[tid] = (M + __log2f(L)) * kLn2;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int idx = tid + j * kDecThreads;
+    if (idx >= G * D) break;
+    const int g = idx / D;
+    float x = 0.f;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) x = u < a.n_split ? fmaf(sm.wm[u][g], ov[u][j], x) : x;
+    for (int s0 = SB; s0 < a.n_split; s0 += SB) {
+      float y[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) y[u] = s0 + u < a.n_split ? get(pu + (s0 + u) * PART + idx) : 0.f;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) x = s0 + u < a.n_split ? fmaf(sm.wm[s0 + u][g], y[u], x) : x;
+    }
+    store_elem(o + idx, x);
   }
 }
 
-template <typename T, int D, int MODE>
-hipError_t launch_t(const DecodeArgs& a, int G, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_units), block(kDecThreads);
+template <typename T, int D>
+hipError_t launch_route_t(const DecodeArgs& a, int G, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n_units * a.n_slices)), block(kDecThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<T, D, 1, MODE>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<T, D, 2, MODE>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<T, D, 4, MODE>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<T, D, 8, MODE>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_route_kernel<T, D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_route_kernel<T, D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_route_kernel<T, D, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_route_kernel<T, D, 8>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_mode(const Dims& d, bool bf16, const DecodeArgs& a, hipStream_t s) {
-  if (bf16) return d.D == 128 ? launch_t<uint16_t, 128, MODE>(a, d.G, s) : launch_t<uint16_t, 64, MODE>(a, d.G, s);
-  return d.D == 128 ? launch_t<float, 128, MODE>(a, d.G, s) : launch_t<float, 64, MODE>(a, d.G, s);
+template <typename T, int D>
+hipError_t launch_attend_t(const DecodeArgs& a, int G, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n_units * a.n_split)), block(kDecThreads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_attend_kernel<T, D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_attend_kernel<T, D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_attend_kernel<T, D, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_attend_kernel<T, D, 8>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
 }
 
-DecodeArgs make_args(const Dims& d) {
+// Workspace: rcount, acount, keys, part (256-byte aligned pieces).
+struct DecodeWs {
+  size_t rcount, acount, keys, part, total;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+DecodeWs decode_ws(const Dims& d) {
+  const size_t units = (size_t)d.B * d.Hkv;
+  const size_t n_split = 1 + (d.kg + kSplitGroups - 1) / kSplitGroups;
+  DecodeWs w;
+  w.rcount = 0;
+  w.acount = align256(units * 4);
+  w.keys = w.acount + align256(units * 4);
+  const size_t n_slices = (size_t)((d.t_cap / kChunk + kSliceChunks - 1) / kSliceChunks);
+  w.part = w.keys + align256(units * n_slices * (size_t)d.kc * 8);
+  w.total = w.part + align256(units * n_split * (size_t)d.G * (d.D + 2) * 4);
+  return w;
+}
+
+DecodeArgs make_args(const Dims& d, void* ws) {
   DecodeArgs a = {};
+  const DecodeWs l = decode_ws(d);
+  char* base = (char*)ws;
+  a.rcount = (uint32_t*)(base + l.rcount);
+  a.acount = (uint32_t*)(base + l.acount);
+  a.cands = (uint64_t*)(base + l.keys);
+  a.part = (float*)(base + l.part);
   a.t_cap = d.t_cap;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kc = d.kc; a.kg = d.kg;
   a.n_units = d.B * d.Hkv;
+  a.n_slices = (int)((d.t_cap / kChunk + kSliceChunks - 1) / kSliceChunks);
+  a.n_split = 1 + (d.kg + kSplitGroups - 1) / kSplitGroups;
   a.scale_log2 = d.scale * kLog2e;
   return a;
 }
 
 }  // namespace
 
+size_t decode_workspace_bytes(const Dims& d) { return decode_ws(d).total; }
+
 hipError_t launch_decode(const Dims& d, bool bf16, bool route, bool attend, const void* q, const void* k,
                          const void* v, const void* chunk_sum, const void* group_sum, const int32_t* pos,
                          int32_t* chunk_idx, int32_t* group_idx, float* chunk_score, float* group_score,
-                         void* o, float* lse, void* group_sum_out, void* chunk_sum_out, hipStream_t s) {
-  DecodeArgs a = make_args(d);
+                         void* o, float* lse, void* group_sum_out, void* chunk_sum_out, void* ws,
+                         hipStream_t s) {
+  DecodeArgs a = make_args(d, ws);
   a.q = q; a.k = k; a.v = v; a.csum = chunk_sum; a.gsum = group_sum; a.pos = pos;
   a.cidx = chunk_idx; a.gidx = group_idx; a.gidx_in = group_idx; a.cscore = chunk_score; a.gscore = group_score;
   a.o = o; a.lse = lse; a.gsum_out = group_sum_out; a.csum_out = chunk_sum_out;
-  if (route && attend) return launch_mode<kRoute | kAttend>(d, bf16, a, s);
-  if (route) return launch_mode<kRoute>(d, bf16, a, s);
-  return launch_mode<kAttend>(d, bf16, a, s);
+  hipError_t e = hipSuccess;
+  if (route) {
+    e = bf16 ? (d.D == 128 ? launch_route_t<uint16_t, 128>(a, d.G, s) : launch_route_t<uint16_t, 64>(a, d.G, s))
+             : (d.D == 128 ? launch_route_t<float, 128>(a, d.G, s) : launch_route_t<float, 64>(a, d.G, s));
+    if (e != hipSuccess) return e;
+  }
+  if (attend) {
+    e = bf16 ? (d.D == 128 ? launch_attend_t<uint16_t, 128>(a, d.G, s) : launch_attend_t<uint16_t, 64>(a, d.G, s))
+             : (d.D == 128 ? launch_attend_t<float, 128>(a, d.G, s) : launch_attend_t<float, 64>(a, d.G, s));
+  }
+  return e;
 }
 
 }  // namespace hga

@@ -146,56 +146,74 @@ static int attend_bwd_impl(const hga_shape* shape, const void* q, const void* k_
                                            (hipStream_t)stream, (const hipEvent_t*)events));
 }
 
+size_t hga_decode_workspace_size(const hga_shape* shape, int64_t t_cap) {
+  hga::Dims d;
+  if (resolve(shape, t_cap, 0, 0, d) != HGA_OK) return 0;
+  return hga::decode_workspace_bytes(d);
+}
+
+static int decode_ws_check(const hga::Dims& d, const void* workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < hga::decode_workspace_bytes(d)) return HGA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HGA_ERR_ALIGN;
+  return HGA_OK;
+}
+
 int hga_decode_route(const hga_shape* shape, const void* q, const void* chunk_sum, const void* group_sum,
                      int64_t t_cap, const int32_t* pos, int32_t* chunk_idx, int32_t* group_idx,
-                     float* chunk_score, float* group_score, void* stream) {
+                     float* chunk_score, float* group_score, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   hga::Dims d;
   int st = resolve(shape, t_cap, 0, 0, d);
   if (st != HGA_OK) return st;
   if (t_cap / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
   if (!q || !chunk_sum || !group_sum || !pos || (d.kc > 0 && !chunk_idx) || (d.kg > 0 && !group_idx))
     return HGA_ERR_NULL;
+  if ((st = decode_ws_check(d, workspace, workspace_bytes)) != HGA_OK) return st;
   if (!aligned16(q) || !aligned16(chunk_sum) || !aligned16(group_sum) ||
       (chunk_idx && !aligned16(chunk_idx)) || (group_idx && !aligned16(group_idx)) ||
       (chunk_score && !aligned16(chunk_score)) || (group_score && !aligned16(group_score)))
     return HGA_ERR_ALIGN;
   return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, true, false, q, nullptr, nullptr, chunk_sum,
                                        group_sum, pos, chunk_idx, group_idx, chunk_score, group_score, nullptr,
-                                       nullptr, nullptr, nullptr, (hipStream_t)stream));
+                                       nullptr, nullptr, nullptr, workspace, (hipStream_t)stream));
 }
 
 int hga_decode_attend(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                       int64_t t_cap, const int32_t* pos, const int32_t* group_idx, void* o, float* lse,
-                      void* group_sum, void* chunk_sum, void* stream) {
+                      void* group_sum, void* chunk_sum, void* workspace, size_t workspace_bytes, void* stream) {
   hga::Dims d;
   int st = resolve(shape, t_cap, 0, 0, d);
   if (st != HGA_OK) return st;
   if (!q || !k_cache || !v_cache || !pos || !o || !lse || (d.kg > 0 && !group_idx)) return HGA_ERR_NULL;
   if ((group_sum == nullptr) != (chunk_sum == nullptr)) return HGA_ERR_NULL;
+  if ((st = decode_ws_check(d, workspace, workspace_bytes)) != HGA_OK) return st;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
       (group_idx && !aligned16(group_idx)) || (group_sum && !aligned16(group_sum)) ||
       (chunk_sum && !aligned16(chunk_sum)))
     return HGA_ERR_ALIGN;
   return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, false, true, q, k_cache, v_cache, nullptr,
                                        nullptr, pos, nullptr, const_cast<int32_t*>(group_idx), nullptr, nullptr,
-                                       o, lse, group_sum, chunk_sum, (hipStream_t)stream));
+                                       o, lse, group_sum, chunk_sum, workspace, (hipStream_t)stream));
 }
 
 int hga_decode_step(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                     void* chunk_sum, void* group_sum, int64_t t_cap, const int32_t* pos, int32_t* chunk_idx,
-                    int32_t* group_idx, void* o, float* lse, void* stream) {
+                    int32_t* group_idx, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   hga::Dims d;
   int st = resolve(shape, t_cap, 0, 0, d);
   if (st != HGA_OK) return st;
   if (t_cap / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
-  if (!q || !k_cache || !v_cache || !chunk_sum || !group_sum || !pos || !o || !lse) return HGA_ERR_NULL;
+  if (!q || !k_cache || !v_cache || !chunk_sum || !group_sum || !pos || !o || !lse || (d.kg > 0 && !group_idx))
+    return HGA_ERR_NULL;
+  if ((st = decode_ws_check(d, workspace, workspace_bytes)) != HGA_OK) return st;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(chunk_sum) || !aligned16(group_sum) || (chunk_idx && !aligned16(chunk_idx)) ||
       (group_idx && !aligned16(group_idx)))
     return HGA_ERR_ALIGN;
   return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, true, true, q, k_cache, v_cache, chunk_sum,
                                        group_sum, pos, chunk_idx, group_idx, nullptr, nullptr, o, lse, group_sum,
-                                       chunk_sum, (hipStream_t)stream));
+                                       chunk_sum, workspace, (hipStream_t)stream));
 }
 
 int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,

@@ -35,10 +35,12 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
                              void* workspace, hipStream_t s, const hipEvent_t* events = nullptr);
 
 // Generation path (one token per sequence; pos [B] on the device): routing,
-// attention, or both in one launch (then group_idx is written if non-null).
+// attention, or both (two launches); ws: decode_workspace_bytes(d) bytes.
+size_t decode_workspace_bytes(const Dims& d);
 hipError_t launch_decode(const Dims& d, bool bf16, bool route, bool attend, const void* q, const void* k,
                          const void* v, const void* chunk_sum, const void* group_sum, const int32_t* pos,
                          int32_t* chunk_idx, int32_t* group_idx, float* chunk_score, float* group_score,
-                         void* o, float* lse, void* group_sum_out, void* chunk_sum_out, hipStream_t s);
+                         void* o, float* lse, void* group_sum_out, void* chunk_sum_out, void* ws,
+                         hipStream_t s);
 
 }  // namespace hga

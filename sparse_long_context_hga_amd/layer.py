@@ -230,6 +230,7 @@ class HGADecoder:
         self.gidx = torch.empty(B, Hkv, top_groups, dtype=torch.int32, device=dev)
         self.o = torch.empty(B, n_q_heads, d, dtype=cache.dtype, device=dev)
         self.lse = torch.empty(B, n_q_heads, dtype=torch.float32, device=dev)
+        self.ws = torch.zeros(L.hga_decode_workspace_size(self.shape, cache.t_cap), dtype=torch.uint8, device=dev)
         self._b = torch.arange(B, device=dev)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor):
@@ -239,5 +240,5 @@ class HGADecoder:
         c.k[bi, :, p] = k_new[live].to(c.dtype)
         c.v[bi, :, p] = v_new[live].to(c.dtype)
         L.hga_decode_step(self.shape, q.contiguous(), c.k, c.v, c.csum, c.gsum, c.t_cap, pos, self.cidx,
-                          self.gidx, self.o, self.lse)
+                          self.gidx, self.o, self.lse, self.ws)
         return self.o, self.lse, self.gidx

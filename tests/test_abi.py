@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert set(names) == {"hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd",
                           "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_attend_bwd_timed",
-                          "hga_decode_step", "hga_decode_route", "hga_decode_attend",
+                          "hga_decode_step", "hga_decode_route", "hga_decode_attend", "hga_decode_workspace_size",
                           "hga_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -138,32 +138,42 @@ def test_attend_validation(L):
 
 def test_decode_validation(L):
     s = _shape(batch=8)
+    need = hga.hga_decode_workspace_size(s, 32768)
+    assert need >= 8 * 8 * 512 * 4 and need % 256 == 0
+    assert hga.hga_decode_workspace_size(_shape(head_dim=80), 32768) == 0
+    assert hga.hga_decode_workspace_size(s, 100) == 0
     r = L.hga_decode_route
 
-    def route(shape=s, t_cap=32768, q=A, pos=A, cidx=A):
+    def route(shape=s, t_cap=32768, q=A, pos=A, cidx=A, ws=A, nbytes=need):
         return r(ctypes.byref(shape) if shape is not None else None, q, A, A, t_cap, pos, cidx, A, None, None,
-                 None)
+                 ws, nbytes, None)
     assert route(shape=None) == -1
     assert route(pos=None) == -1
     assert route(cidx=None) == -1
     assert route(q=M) == -5
+    assert route(ws=None) == -6
+    assert route(nbytes=need - 1) == -6
+    assert route(ws=M) == -5
     assert route(t_cap=100) == -2
-    assert route(t_cap=64 * 8193) == -3
+    assert route(t_cap=64 * 8193, nbytes=1 << 40) == -3
     assert route(shape=_shape(n_q_heads=24)) == -3
     at = L.hga_decode_attend
 
-    def attend(gsum=None, csum=None, k=A, lse=A, gidx=A):
-        return at(ctypes.byref(s), A, k, A, 32768, A, gidx, A, lse, gsum, csum, None)
+    def attend(gsum=None, csum=None, k=A, lse=A, gidx=A, nbytes=need):
+        return at(ctypes.byref(s), A, k, A, 32768, A, gidx, A, lse, gsum, csum, A, nbytes, None)
     assert attend(k=None) == -1
     assert attend(lse=None) == -1
     assert attend(gidx=None) == -1
     assert attend(gsum=A) == -1                       # summaries: both or neither
     assert attend(gsum=A, csum=M) == -5
+    assert attend(nbytes=0) == -6
     st = L.hga_decode_step
 
-    def step(csum=A, o=A, cidx=None, t_cap=32768):
-        return st(ctypes.byref(s), A, A, A, csum, A, t_cap, A, cidx, None, o, A, None)
+    def step(csum=A, o=A, cidx=None, gidx=A, t_cap=32768, nbytes=need):
+        return st(ctypes.byref(s), A, A, A, csum, A, t_cap, A, cidx, gidx, o, A, A, nbytes, None)
     assert step(csum=None) == -1
     assert step(o=None) == -1
+    assert step(gidx=None) == -1
     assert step(cidx=M) == -5
-    assert step(t_cap=64 * 8193) == -3
+    assert step(nbytes=need - 1) == -6
+    assert step(t_cap=64 * 8193, nbytes=1 << 40) == -3

@@ -81,22 +81,23 @@ class Dev:
         self.cscore = torch.zeros((B, Hkv, w.top_chunks), dtype=torch.float32, device="cuda")
         self.o = torch.full((B, w.n_q_heads, w.head_dim), 5.0, dtype=self.q.dtype, device="cuda")
         self.lse = torch.zeros((B, w.n_q_heads), dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(hga.hga_decode_workspace_size(self.shape, w.t_cap), dtype=torch.uint8, device="cuda")
         self.w = w
 
     def route(self):
         import sparse_long_context_hga_amd as hga
         hga.hga_decode_route(self.shape, self.q, self.cs, self.gs, self.w.t_cap, self.pos, self.cidx, self.gidx,
-                             chunk_score=self.cscore)
+                             self.ws, chunk_score=self.cscore)
 
     def attend(self, gidx=None, gs=None, cs=None):
         import sparse_long_context_hga_amd as hga
         hga.hga_decode_attend(self.shape, self.q, self.k, self.v, self.w.t_cap, self.pos,
-                              self.gidx if gidx is None else gidx, self.o, self.lse, gs, cs)
+                              self.gidx if gidx is None else gidx, self.o, self.lse, self.ws, gs, cs)
 
     def step(self):
         import sparse_long_context_hga_amd as hga
         hga.hga_decode_step(self.shape, self.q, self.k, self.v, self.cs, self.gs, self.w.t_cap, self.pos,
-                            self.cidx, self.gidx, self.o, self.lse)
+                            self.cidx, self.gidx, self.o, self.lse, self.ws)
 
 
 def _check_route(chk, w, gs, cs, cidx, gidx, cscore=None):
@@ -190,6 +191,29 @@ def test_decode_step_equals_route_then_attend(chk, name):
         assert torch.equal(x, y)
     _check_route(chk, w, *_summaries(w), d2.cidx.cpu().numpy(), d2.gidx.cpu().numpy())
     _check_attend(chk, w, chk.to_np(d2.o), d2.lse.cpu().numpy(), d2.gidx.cpu().numpy())
+
+
+def test_decode_workspace_reuse(chk):
+    """Two layers of different shapes share one workspace, alternating: every repeat
+    is bit-identical and the arrival counters are back at zero after each call."""
+    wa = hi.decode_batch(name="a", **CASES["bf16_g4_d128"])
+    wb = hi.decode_batch(name="b", **CASES["bf16_g8_d128"])
+    ga, ca = _summaries(wa)
+    gb, cb = _summaries(wb)
+    da, db = Dev(chk, wa, ga, ca), Dev(chk, wb, gb, cb)
+    shared = torch.zeros(max(da.ws.numel(), db.ws.numel()), dtype=torch.uint8, device="cuda")
+    da.ws = db.ws = shared
+    runs = []
+    for layer in (da, db, da, db, da):
+        layer.step()
+        torch.cuda.synchronize()
+        runs.append((layer.gidx.clone(), layer.o.clone(), layer.lse.clone()))
+        assert not shared[:512].any()      # both counter arrays (8 and 4 units) back at zero
+    for i, j in ((0, 2), (0, 4), (1, 3)):
+        for x, y in zip(runs[i], runs[j]):
+            assert torch.equal(x, y)
+    _check_route(chk, wa, ga, ca, da.cidx.cpu().numpy(), runs[0][0].cpu().numpy())
+    _check_attend(chk, wa, chk.to_np(runs[4][1]), runs[4][2].cpu().numpy(), runs[4][0].cpu().numpy())
 
 
 def test_decode_b8_ctx32k(chk):
