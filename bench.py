@@ -138,7 +138,7 @@ def traffic_summary(fetch_csv, write_csv, calib_mib, workload):
     import csv
     import collections
     n = calib_mib * (1 << 20)
-    out = {"workload": workload, "source_sha256": kernel_source_digest(), "calibration_bytes": n,
+    out = {"workload": workload, "source_sha256": kernel_source_digest(workload), "calibration_bytes": n,
            "kernels": {}}
     per = {}
     for label, path in (("fetch", fetch_csv), ("write", write_csv)):
@@ -167,13 +167,20 @@ def traffic_summary(fetch_csv, write_csv, calib_mib, workload):
     return out
 
 
-def kernel_source_digest():
-    """sha256 over the kernel sources: counter figures are only valid for this exact code."""
+# Kernel sources each measured workload runs (device headers included).
+WORKLOAD_SOURCES = {
+    "qwen3_8b_layer_ctx16k": ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "hga_device.h",
+                              "hga_select.h"],
+    "decode_b8_ctx32k": ["decode.hip", "summaries.hip", "hga_device.h", "hga_select.h"],
+}
+
+
+def kernel_source_digest(workload):
+    """sha256 over the kernel sources the workload runs: counter figures are only
+    valid for this exact code."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if not name.endswith((".hip", ".h")):
-            continue
+    for name in sorted(WORKLOAD_SOURCES[workload]):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -188,7 +195,7 @@ def measured_traffic(kernel, workload):
             summ = json.load(f)
     except (KeyError, OSError, ValueError):
         return None
-    if summ.get("workload") != workload or summ.get("source_sha256") != kernel_source_digest():
+    if summ.get("workload") != workload or summ.get("source_sha256") != kernel_source_digest(workload):
         return None
     k = summ.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
