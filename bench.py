@@ -105,8 +105,8 @@ def algorithmic_work(w, gidx):
         "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops},
         "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops},
         "attend_bwd_dkdv": {"bytes": dkdv_bytes, "flops": dkdv_flops},
-        # the selection inverse reads group_idx; the partial sums are not part of the method
-        "attend_bwd_plan": {"bytes": float(gidx.size * 4), "flops": 0.0},
+        # the work list and the partial sums are not part of the method
+        "attend_bwd_order": {"bytes": 0.0, "flops": 0.0},
         "attend_bwd_finalize": {"bytes": 0.0, "flops": 0.0},
     }
 
@@ -116,7 +116,7 @@ PMC_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_st
 CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 # kernel-name prefix -> step kernel (first match wins)
 KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_", "route"), ("attend_fwd_", "attend_fwd"),
-               ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_plan_", "attend_bwd_plan"),
+               ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_order_", "attend_bwd_order"),
                ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv"),
                ("decode_route_kernel", "decode_route"), ("decode_attend_kernel", "decode_attend")]
 
@@ -481,7 +481,7 @@ def main():
         "attend_fwd": avg((ev[i][2], ev[i][3]) for i in marked),
     }
     if L.do is not None:
-        for k, name in enumerate(("attend_bwd_dq", "attend_bwd_plan", "attend_bwd_dkdv", "attend_bwd_finalize")):
+        for k, name in enumerate(("attend_bwd_dq", "attend_bwd_order", "attend_bwd_dkdv", "attend_bwd_finalize")):
             kern_ms[name] = avg((bev[i][2 * k], bev[i][2 * k + 1]) for i in marked)
 
     gidx = L.gidx.cpu().numpy()

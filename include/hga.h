@@ -195,11 +195,11 @@ int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache,
 
 /*
  * hga_attend_bwd_timed -- hga_attend_bwd, plus per-kernel timing marks: for
- * kernel i of the backward (HGA_BWD_KERNELS of them, in launch order: 0 dQ and
- * rowsum(dO*O), 1 selection inverse / work list, 2 dK/dV, 3 dK/dV partial sums)
- * events[2i] is recorded on `stream` just before its launch and events[2i+1] just
- * after; a kernel that a dtype's path does not launch (the fp32 path has no
- * work list and no partial sums) gets its two marks back to back.  events:
+ * kernel i of the backward (HGA_BWD_KERNELS of them, in launch order: 0 dQ,
+ * rowsum(dO*O) and the selection inverse, 1 the dK/dV work list, 2 dK/dV, 3 dK/dV
+ * partial sums) events[2i] is recorded on `stream` just before its launch and
+ * events[2i+1] just after; a kernel that a dtype's path does not launch (the fp32
+ * path has no work list and no partial sums) gets its two marks back to back.  events:
  * 2*HGA_BWD_KERNELS hipEvent_t handles created by the caller (NULL entries are
  * skipped).  Everything else as hga_attend_bwd.
  */

@@ -57,8 +57,7 @@ struct BwdArgs {
   int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
   int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
   int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
-  int* bcount;      // [64] work items per bucket (bucket = rounds, capped at 63) (workspace)
-  int* bitems;      // [64, B*Hkv*S/64*kMaxParts] work items (chunk * kMaxParts + part) (workspace)
+  int* order;       // [1 + B*Hkv*S/64*kMaxParts] number of work items, then the items heaviest first
   float* parts;     // [B, Hkv, S/64, kMaxParts, 2, 64, d] fp32 partials (workspace)
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kg, nb, n_units;
@@ -75,6 +74,56 @@ __device__ __forceinline__ float dot8_bf16(bf16x8 x, bf16x8 y) {
     s += __uint_as_float(av[i] & 0xFFFF0000u) * __uint_as_float(bv[i] & 0xFFFF0000u);
   }
   return s;
+}
+
+// Inverse of the selection for the active segment, for active chunk cc of
+// (sequence, KV head) bh: the ascending list of query blocks that attend it (its own
+// block, causally, and every later block whose group list holds one of its 8
+// groups), with the mask of the selected groups, and into how many work items its
+// dK/dV is cut.  Runs inside the dQ kernel (one of the work-groups of unit (bh, cc))
+// before its tile pipeline; gv holds this thread's first group ids of the later
+// blocks, loaded early so that their latency overlaps the dQ kernel's own loads.
+constexpr int kPlanLoads = 8;
+template <int NT, int G>
+__device__ __forceinline__ void plan_chunk(const BwdArgs& a, int bh, int cc, const int32_t (&gv)[kPlanLoads],
+                                           uint32_t* mask) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int64_t g_lo = (a.t_hist / kChunk + cc) * 8;
+  const int32_t* g0 = a.gidx + ((int64_t)bh * a.nb + cc + 1) * a.kg;
+  const int total = (a.nb - 1 - cc) * a.kg;
+  auto mark = [&](int e, int64_t gid) __attribute__((always_inline)) {
+    if (gid >= g_lo && gid < g_lo + 8) atomicOr(&mask[cc + 1 + e / a.kg], 1u << (int)(gid - g_lo));
+  };
+#pragma unroll
+  for (int u = 0; u < kPlanLoads; ++u) mark(NT * u + tid, gv[u]);
+  for (int e0 = NT * kPlanLoads; e0 < total; e0 += NT * kPlanLoads) {   // long segments only
+    int32_t gx[kPlanLoads];
+#pragma unroll
+    for (int u = 0; u < kPlanLoads; ++u) {
+      const int e = e0 + NT * u + tid;
+      gx[u] = e < total ? g0[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPlanLoads; ++u) mark(e0 + NT * u + tid, gx[u]);
+  }
+  __syncthreads();
+  if (w != 0) return;
+  const int unit = bh * a.nb + cc;
+  int n = 0;
+  int* out = a.vis + (int64_t)unit * a.nb;
+  for (int j0 = cc; j0 < a.nb; j0 += 64) {
+    const int jj = j0 + l;
+    const uint32_t m = jj < a.nb ? mask[jj] : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    if (m != 0u) out[n + __popcll(bal & ((1ull << l) - 1ull))] = jj | (int)(m << 16);
+    n += __popcll(bal);
+  }
+  if (l == 0) {
+    // G rounds (query heads) per attending block, cut into items of about kTargetRounds
+    const int rounds = G * n;
+    a.nvis[unit] = n;
+    a.flags[unit] = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
+  }
 }
 
 // ---------------------------------------------------------------- dQ (bf16)
@@ -112,6 +161,23 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bh * a.t_cap * D;
   const uint16_t* vb = (const uint16_t*)a.v + (int64_t)bh * a.t_cap * D;
 
+  // The selection inverse of active chunk j: its group ids are loaded first (their
+  // latency overlaps the loads below), used after the group list is in LDS.
+  __shared__ uint32_t pmask[kMaxBlocks];
+  const bool do_plan = item % (G / HPW) == 0;
+  int32_t pgv[kPlanLoads];
+  {
+    const int32_t* g0 = a.gidx + ((int64_t)bh * a.nb + j + 1) * a.kg;
+    const int total = (a.nb - 1 - j) * a.kg;
+#pragma unroll
+    for (int u = 0; u < kPlanLoads; ++u) {
+      const int e = NT * u + tid;
+      pgv[u] = do_plan && e < total ? g0[e] : -1;
+    }
+    if (do_plan)
+      for (int i = tid; i < a.nb; i += NT) pmask[i] = i == j ? 0xFFu : 0u;   // ordered by the barrier below
+  }
+
   bf16x8 qf[KS], dof[KS];
   float dpart = 0.f;
   {
@@ -127,11 +193,11 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   }
   const float Dr = half_sum(dpart);
   if (h == 0) a.dvec[qrow] = Dr;
-  if (item == 0 && tid < kBuckets) a.bcount[tid] = 0;   // work-list counters for the plan kernel
   const float lse2 = a.lse[qrow] * kLog2e;
 
   const int n_valid = __builtin_amdgcn_readfirstlane(
       count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
+  if (do_plan) plan_chunk<NT, G>(a, bh, j, pgv, pmask);
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
   // Tile t: 8 selected groups, or the own chunk as the last tile; slots past the
@@ -248,79 +314,46 @@ struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) ve
   static size_t flags_off(size_t rows) { return up(rows * 4); }
   static size_t nvis_off(size_t rows, size_t units) { return up(flags_off(rows) + units * 4); }
   static size_t vis_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
-  static size_t bcount_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
-  static size_t bitems_off(size_t rows, size_t units, size_t nb) { return up(bcount_off(rows, units, nb) + kBuckets * 4); }
+  static size_t order_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
   static size_t part_off(size_t rows, size_t units, size_t nb) {
-    return up(bitems_off(rows, units, nb) + (size_t)kBuckets * units * kMaxParts * 4);
+    return up(order_off(rows, units, nb) + (1 + units * kMaxParts) * 4);
   }
 };
 
-// Inverse of the selection for the active segment: for every active chunk, the
-// ascending list of query blocks that attend it (its own block, causally, and
-// every later block whose group list holds one of its 8 groups), with the mask of
-// the selected groups, and whether its dK/dV work is split over several items.
-// One work-group of 256 threads per (sequence, KV head, active chunk); reads only
-// group_idx.  A chunk's items differ in size by at most one round, so it files them
-// into the size buckets with at most two atomics.
-constexpr int kPlanThreads = 256;
+// The dK/dV work list: every chunk's items (item k of a chunk with R rounds cut
+// into np items has (k+1)R/np - kR/np rounds), heaviest first, so that the long
+// items start early.  One work-group; the order within one size is immaterial
+// (every item writes its own output or partial).
+constexpr int kOrderThreads = 1024;
 template <int G>
-__global__ __launch_bounds__(kPlanThreads) void attend_bwd_plan_kernel(BwdArgs a) {
-  __shared__ uint32_t mask[kMaxBlocks];
-  const int unit = blockIdx.x;
-  if (unit >= a.n_units) return;
-  const int cc = unit % a.nb;
-  const int bh = unit / a.nb;
+__global__ __launch_bounds__(kOrderThreads) void attend_bwd_order_kernel(BwdArgs a) {
+  __shared__ int cnt[kBuckets];
   const int tid = threadIdx.x, l = tid & 63;
-  const int64_t g_lo = (a.t_hist / kChunk + cc) * 8;
-  for (int i = tid; i < a.nb; i += kPlanThreads) mask[i] = i == cc ? 0xFFu : 0u;
+  if (tid < kBuckets) cnt[tid] = 0;
   __syncthreads();
-  const int later = a.nb - 1 - cc;
-  const int32_t* g0 = a.gidx + ((int64_t)bh * a.nb + cc + 1) * a.kg;
-  const int total = later * a.kg;
-  // 8 independent loads in flight per thread, then the tests.
-  for (int e0 = 0; e0 < total; e0 += kPlanThreads * 8) {
-    int32_t gv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + kPlanThreads * u + tid;
-      gv[u] = e < total ? g0[e] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t gid = gv[u];
-      if (gid >= g_lo && gid < g_lo + 8)
-        atomicOr(&mask[cc + 1 + (e0 + kPlanThreads * u + tid) / a.kg], 1u << (int)(gid - g_lo));
-    }
+  auto size_of = [&](int np_u, int r_u, int k) __attribute__((always_inline)) {
+    return min(kBuckets - 1, (k + 1) * r_u / np_u - k * r_u / np_u);
+  };
+  for (int u = tid; u < a.n_units; u += kOrderThreads) {
+    const int np_u = a.flags[u], r_u = G * a.nvis[u];
+    for (int k = 0; k < np_u; ++k) atomicAdd(&cnt[size_of(np_u, r_u, k)], 1);
   }
   __syncthreads();
-  if (tid >= 64) return;
-  int n = 0;
-  int* out = a.vis + (int64_t)unit * a.nb;
-  for (int j0 = cc; j0 < a.nb; j0 += 64) {
-    const int jj = j0 + l;
-    const uint32_t m = jj < a.nb ? mask[jj] : 0u;
-    const uint64_t bal = __ballot(m != 0u);
-    if (m != 0u) out[n + __popcll(bal & ((1ull << l) - 1ull))] = jj | (int)(m << 16);
-    n += __popcll(bal);
-  }
-  if (l == 0) {
-    // G rounds (query heads) per attending block; cut into np items of q or q+1 rounds.
-    const int rounds = G * n;
-    const int np = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
-    const size_t cap = (size_t)a.n_units * kMaxParts;
-    const int q = rounds / np, n_big = rounds - q * np;     // n_big items of q+1 rounds
-    // item k has (k+1)*rounds/np - k*rounds/np rounds; file each size class with one atomic
-    int pos_small = 0, pos_big = 0;
-    const int b_small = min(q, kBuckets - 1), b_big = min(q + 1, kBuckets - 1);
-    if (np - n_big > 0) pos_small = atomicAdd(&a.bcount[b_small], np - n_big);
-    if (n_big > 0) pos_big = atomicAdd(&a.bcount[b_big], n_big);
-    for (int k = 0; k < np; ++k) {
-      const int rk = (k + 1) * rounds / np - k * rounds / np;
-      if (rk == q + 1 && n_big > 0) a.bitems[b_big * cap + pos_big++] = unit * kMaxParts + k;
-      else a.bitems[b_small * cap + pos_small++] = unit * kMaxParts + k;
+  if (tid < 64) {   // first position of each size, largest size first
+    const int c = cnt[kBuckets - 1 - l];
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (l >= off) incl += y;
     }
-    a.nvis[unit] = n;
-    a.flags[unit] = np;
+    cnt[kBuckets - 1 - l] = incl - c;
+    if (l == 63) a.order[0] = incl;
+  }
+  __syncthreads();
+  for (int u = tid; u < a.n_units; u += kOrderThreads) {
+    const int np_u = a.flags[u], r_u = G * a.nvis[u];
+    for (int k = 0; k < np_u; ++k) a.order[1 + atomicAdd(&cnt[size_of(np_u, r_u, k)], 1)] = u * kMaxParts + k;
   }
 }
 
@@ -347,27 +380,15 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   };
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
-  // Work item number blockIdx.x in heaviest-bucket-first order (the plan kernel filled the buckets).
-  if (w == 0) {
-    const int c = a.bcount[kBuckets - 1 - l];            // lane l: bucket 63 - l
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (l >= off) incl += y;
-    }
-    const int rank = (int)blockIdx.x;
-    const uint64_t hit = __ballot(rank < incl);
-    const int lb = hit ? __ffsll((long long)hit) - 1 : 0;   // first lane whose prefix covers rank
-    const int before = __shfl(incl, lb, 64) - __shfl(c, lb, 64);
-    if (l == 0)
-      s_item = hit ? a.bitems[(size_t)(kBuckets - 1 - lb) * ((size_t)a.n_units * kMaxParts) + (rank - before)] : -1;
-  }
+  // Work item number blockIdx.x of the list the order kernel wrote (heaviest first).
+  if ((int)blockIdx.x >= a.order[0]) return;
+  if (tid == 0) s_item = a.order[1 + blockIdx.x];
   __syncthreads();
   const int item = s_item;
   if (item < 0) return;
   const int part = item % kMaxParts;
   const int unit = item / kMaxParts;
+  if (unit >= a.n_units || part >= a.flags[unit]) return;   // not an item of this selection
   const int cc = unit % a.nb;                      // active chunk == its own query block
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
@@ -682,7 +703,7 @@ template <int D, int G>
 void launch_bf16(const BwdArgs& a, const Launcher& run) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per dQ work-group
   run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))), dim3(128 * HPW), a);
-  run(1, attend_bwd_plan_kernel<G>, dim3(a.n_units), dim3(kPlanThreads), a);
+  run(1, attend_bwd_order_kernel<G>, dim3(1), dim3(kOrderThreads), a);
   run(2, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
   run(3, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
 }
@@ -721,8 +742,7 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
     a.flags = (int*)((char*)workspace + DkdvLayout::flags_off(rows));
     a.nvis = (int*)((char*)workspace + DkdvLayout::nvis_off(rows, units));
     a.vis = (int*)((char*)workspace + DkdvLayout::vis_off(rows, units));
-    a.bcount = (int*)((char*)workspace + DkdvLayout::bcount_off(rows, units, (size_t)d.nb));
-    a.bitems = (int*)((char*)workspace + DkdvLayout::bitems_off(rows, units, (size_t)d.nb));
+    a.order = (int*)((char*)workspace + DkdvLayout::order_off(rows, units, (size_t)d.nb));
     a.parts = (float*)((char*)workspace + DkdvLayout::part_off(rows, units, (size_t)d.nb));
   }
   a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
