@@ -185,69 +185,6 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Candidates for the selection: score key << 32 | (2^32 - 1 - index), so that a
-// larger value is a higher score or, at equal score, a lower index; 0 = none.
-__device__ __forceinline__ uint64_t cand(uint32_t key, int idx) {
-  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-__device__ __forceinline__ int cand_index(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
-  return ((uint64_t)dpp<CTRL>((uint32_t)(x >> 32)) << 32) | dpp<CTRL>((uint32_t)x);
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-  x = umax64(x, dpp64<0xB1>(x));
-  x = umax64(x, dpp64<0x4E>(x));
-  x = umax64(x, dpp64<0x141>(x));
-  x = umax64(x, dpp64<0x140>(x));
-  x = umax64(x, ((uint64_t)swz_xor16((uint32_t)(x >> 32)) << 32) | swz_xor16((uint32_t)x));
-  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
-  const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  return umax64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
-}
-
-// The k-th largest of the wave's candidates v[P] (P per lane), or 0 when the wave
-// holds at most k: a most-significant-bit-first search on the 64-bit values,
-// counting with ballots (the counts are wave-uniform scalars).  Candidates are
-// distinct, so exactly min(k, #candidates) of them are >= the result and nonzero.
-template <int P>
-__device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[P], int k) {
-  uint64_t res = 0;
-  for (int bit = 63; bit >= 0; --bit) {
-    const uint64_t t = res | (1ull << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < P; ++i) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[i] >= t));
-    if (cnt >= k) {
-      res = t;
-      if (cnt == k) break;   // exactly k at or above: any larger threshold keeps the same set
-    }
-  }
-  return res;
-}
-
-// Number of set bits of m in the lanes below this one.
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Selects the k largest of the wave's candidates (k >= 1) and stores them to out
-// in an order fixed by (lane, i); returns their number (wave-uniform).
-template <int P>
-__device__ __forceinline__ int wave_select(const uint64_t (&v)[P], int k, uint64_t* out) {
-  const uint64_t th = wave_kth<P>(v, k);
-  int base = 0;
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const bool sel = v[i] != 0 && v[i] >= th;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
-    if (sel) out[base + lanes_below(m)] = v[i];
-    base += __builtin_popcountll(m);
-  }
-  return base;
-}
-
 template <typename T, int D, int G>
 __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int kvh, float (&qv)[G][8], float mul) {
   constexpr int LPR = D / 8;
@@ -370,33 +307,10 @@ __device__ __forceinline__ int select_chunks(RouteShared& sm, int N, int kc, con
   return select_two_stage<32, P2>(sm, N, kc, cand_at);
 }
 
-// Top-k_g of the group keys[0 .. n) (n <= 512) by wave 0, stored in ascending slot
-// order (= ascending group id) to out.  Returns their number (all threads).
+// Top-k_g of the group keys[0 .. n) (n <= 512), ascending slots (= ascending group ids).
 template <int P>
 __device__ __forceinline__ int select_groups(RouteShared& sm, int n, int kg, int* out) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (w == 0) {
-    uint64_t v[P];   // lane l holds slots P l .. P l + P - 1
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int s = P * lane + i;
-      v[i] = s < n ? cand(sm.gkeys[s], s) : 0;
-    }
-    const uint64_t th = wave_kth<P>(v, kg);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < P; ++i) cnt += v[i] != 0 && v[i] >= th;
-    int before = 0;   // selected slots of the lanes below: bit-sliced ballots of cnt (< 16)
-#pragma unroll
-    for (int bit = 0; bit < 4; ++bit) before += lanes_below(__builtin_amdgcn_ballot_w64((cnt >> bit) & 1)) << bit;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      if (v[i] != 0 && v[i] >= th) out[before++] = P * lane + i;
-    }
-    if (lane == 63) sm.nsel = before;
-  }
-  __syncthreads();
-  return sm.nsel;
+  return wave_topk_sorted<P>(sm.gkeys, n, kg, out, &sm.nsel);
 }
 
 // ---------------------------------------------------------------- routing

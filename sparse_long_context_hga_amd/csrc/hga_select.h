@@ -142,5 +142,86 @@ __device__ int block_topk_rank(const uint32_t* keys, int n, int k, int* out, Sel
   return tot;
 }
 
+
+// ---------------------------------------------------------------- one-wave selection
+// Candidates for the selection: score key << 32 | (2^32 - 1 - index), so that a
+// larger value is a higher score or, at equal score, a lower index; 0 = none.
+__device__ __forceinline__ uint64_t cand(uint32_t key, int idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ int cand_index(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
+// The k-th largest of the wave's candidates v[P] (P per lane), or 0 when the wave
+// holds at most k: a most-significant-bit-first search on the 64-bit values,
+// counting with ballots (the counts are wave-uniform scalars).  Candidates are
+// distinct, so exactly min(k, #candidates) of them are >= the result and nonzero.
+template <int P>
+__device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[P], int k) {
+  uint64_t res = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t t = res | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[i] >= t));
+    if (cnt >= k) {
+      res = t;
+      if (cnt == k) break;   // exactly k at or above: any larger threshold keeps the same set
+    }
+  }
+  return res;
+}
+
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Selects the k largest of the wave's candidates (k >= 1) and stores them to out
+// in an order fixed by (lane, i); returns their number (wave-uniform).
+template <int P>
+__device__ __forceinline__ int wave_select(const uint64_t (&v)[P], int k, uint64_t* out) {
+  const uint64_t th = wave_kth<P>(v, k);
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const bool sel = v[i] != 0 && v[i] >= th;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
+    if (sel) out[base + lanes_below(m)] = v[i];
+    base += __builtin_popcountll(m);
+  }
+  return base;
+}
+
+// Wave 0 of the calling work-group selects the top k (k >= 1) of keys[0 .. n)
+// (n <= 64 P; keys nonzero) by (key desc, index asc) and stores their indices in
+// ascending order to out.  Lane l holds the candidates P l .. P l + P - 1, so the
+// selected ones of the lanes below come first: their count is a prefix sum, taken
+// from bit-sliced ballots.  Returns the number selected (all threads; sm_n: LDS).
+template <int P>
+__device__ __forceinline__ int wave_topk_sorted(const uint32_t* keys, int n, int k, int* out, int* sm_n) {
+  static_assert(P <= 8, "counts of at most 15 per lane");
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint64_t v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int s = P * lane + i;
+      v[i] = s < n ? cand(keys[s], s) : 0;
+    }
+    const uint64_t th = wave_kth<P>(v, k);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) cnt += v[i] != 0 && v[i] >= th;
+    int before = 0;
+#pragma unroll
+    for (int bit = 0; bit < 4; ++bit) before += lanes_below(__builtin_amdgcn_ballot_w64((cnt >> bit) & 1)) << bit;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if (v[i] != 0 && v[i] >= th) out[before++] = P * lane + i;
+    if (lane == 63) *sm_n = before;
+  }
+  __syncthreads();
+  return *sm_n;
+}
+
 }  // namespace
 }  // namespace hga

@@ -22,9 +22,11 @@
 // registers for the whole kernel), operand B = 32 summary rows, so each lane
 // ends with one candidate column and 16 of the rows and the row-maximum is a
 // register reduction plus one cross-half exchange.  Block maxima of the waves
-// meet in LDS through an atomic max on order-preserving integer keys; the top-k
-// is an exact 4-pass radix select over those keys followed by an index-ordered
-// compaction (deterministic; ties resolved by index).
+// meet in LDS through an atomic max on order-preserving integer keys.  The top-k
+// (up to 512 candidates) is one wave's most-significant-bit-first search for the
+// k-th largest (key, index) pair, counting with ballots, then an index-ordered
+// compaction; larger candidate sets use a block-wide rank or radix select.  All
+// are exact and deterministic, ties resolved by index.
 #include "hga_device.h"
 #include "hga_internal.h"
 #include "hga_select.h"
@@ -79,6 +81,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   __shared__ int gsel[kMaxGroupCand];
   __shared__ SelectShared<kRouteThreads> sh;
   __shared__ __align__(16) uint64_t pk[kRankMax + 16];
+  __shared__ int nsel;
   auto SB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (B() == 0) return sb0; else return sb1;
   };
@@ -168,8 +171,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   __syncthreads();
   if (J > 0) score_rows(J, chunk_row, ckeys, qf);
   __syncthreads();
-  const int nc = J <= kRankMax ? block_topk_rank(ckeys, J, a.kc, csel, sh, pk)
-                               : block_topk(ckeys, J, a.kc, csel, sh);   // ascending chunk ids
+  // ascending chunk ids: one wave's bit search up to 512 candidates, block-wide above
+  const int nc = (J == 0 || a.kc == 0) ? 0
+                 : J <= 64              ? wave_topk_sorted<1>(ckeys, J, a.kc, csel, &nsel)
+                 : J <= 128             ? wave_topk_sorted<2>(ckeys, J, a.kc, csel, &nsel)
+                 : J <= 256             ? wave_topk_sorted<4>(ckeys, J, a.kc, csel, &nsel)
+                 : J <= 512             ? wave_topk_sorted<8>(ckeys, J, a.kc, csel, &nsel)
+                 : J <= kRankMax        ? block_topk_rank(ckeys, J, a.kc, csel, sh, pk)
+                                        : block_topk(ckeys, J, a.kc, csel, sh);
 
   // ---- group scores over the 8 groups of each selected chunk, then top-k_g
   const int ng_cand = 8 * nc;
@@ -181,7 +190,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
     score_rows(ng_cand, group_row, gkeys, qf);
   }
   __syncthreads();
-  const int ng = block_topk_rank(gkeys, ng_cand, a.kg, gsel, sh, pk);   // ascending slots == ascending ids
+  const int ng = (ng_cand == 0 || a.kg == 0) ? 0        // ascending slots == ascending ids
+                 : ng_cand <= 64  ? wave_topk_sorted<1>(gkeys, ng_cand, a.kg, gsel, &nsel)
+                 : ng_cand <= 128 ? wave_topk_sorted<2>(gkeys, ng_cand, a.kg, gsel, &nsel)
+                 : ng_cand <= 256 ? wave_topk_sorted<4>(gkeys, ng_cand, a.kg, gsel, &nsel)
+                                  : wave_topk_sorted<8>(gkeys, ng_cand, a.kg, gsel, &nsel);
 
   // ---- outputs
   int32_t* co = a.cidx + (int64_t)unit * a.kc;
