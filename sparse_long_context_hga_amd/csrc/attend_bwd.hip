@@ -12,12 +12,13 @@
 // bf16 path: four kernels, deterministic (no floating-point atomics):
 //  * dq (query-major, one work-group per (sequence, KV head, query block) and
 //    query-head slice): the forward's gathered tiles again; recomputes P from
-//    LSE; writes dQ and D = rowsum(dO * O) (workspace) for the dK/dV kernel;
-//  * plan (one wave per (sequence, KV head, active chunk)): inverts the
-//    selection -- the ascending list of query blocks that attend the chunk --
-//    and cuts the chunk's work into 1..8 items of about 12 "rounds" (one round =
-//    the 64 rows of one query head of one attending block), filed into buckets
-//    by size so that the dK/dV grid starts with the heaviest items;
+//    LSE; writes dQ and D = rowsum(dO * O) (workspace) for the dK/dV kernel.  It
+//    also inverts the selection for the active chunk of its own block -- the
+//    ascending list of query blocks that attend the chunk -- and cuts the
+//    chunk's work into 1..8 items of about 12 "rounds" (one round = the 64 rows
+//    of one query head of one attending block);
+//  * order (one work-group): lists all items by size, largest first, so that
+//    the dK/dV grid starts with the heaviest items;
 //  * dkdv (one work-group per item): the chunk's 64 keys and values stay in
 //    registers; the item's rounds stream Q / dO rows through swizzled LDS; dK,
 //    dV accumulate in fp32 registers (dV^T += dO^T P, dK^T += Q^T dS, the
@@ -40,7 +41,7 @@ constexpr int kStages = 2;   // K/V tile buffer sets of the dQ kernel
 constexpr int kMaxBlocks = 1024;   // query blocks per segment supported by the dkdv kernel
 constexpr int kTargetRounds = 12;  // dK/dV work is cut into items of about this many rounds
 constexpr int kMaxParts = 8;       // at most this many items per active chunk
-constexpr int kBuckets = 64;       // work-list buckets (rounds per work item, capped)
+constexpr int kBuckets = 64;       // work-list size classes (rounds per work item, capped)
 
 struct BwdArgs {
   const void* q;
@@ -301,7 +302,7 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 // Work item (sequence, KV head, active chunk, part).  A chunk is attended by its
 // own block (causally) and by every later block whose selection holds one of its
 // groups; each such block contributes G "rounds" (64 rows of one query head).
-// The plan kernel cuts a chunk's rounds into np = min(kMaxParts, ceil(rounds /
+// The dQ kernel cuts a chunk's rounds into np = min(kMaxParts, ceil(rounds /
 // kTargetRounds)) contiguous slices.  With np = 1 the item writes bf16 dK/dV
 // itself; otherwise every item writes an fp32 partial, summed in part order by
 // the finalize kernel (deterministic; no atomics).
