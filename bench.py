@@ -43,8 +43,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
                    choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k",
-                            "decode_b8_ctx32k"],
-                   help="decode_b8_ctx32k times the generation path (hga_decode_route + hga_decode_attend)")
+                            "decode_b8_ctx32k", "rollout_131k"],
+                   help="decode_b8_ctx32k times the generation path (hga_decode_route + hga_decode_attend); "
+                        "rollout_131k the 64-segment forward rollout")
     p.add_argument("--routing", default="block", choices=["block", "causal"],
                    help="block: each block routes itself (hga_route); causal: the block before it routes it")
     p.add_argument("--mark-every", type=int, default=8,
@@ -385,6 +386,112 @@ def main_decode(args):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------ rollout
+ROLLOUT_METRIC = "HGA rollout tokens/s (summaries + route + forward, 64 segments) at 131K ctx; % of HBM roofline"
+
+
+def main_rollout(args):
+    """The 131,072-token evaluation rollout: 64 segments of 2,048 tokens, each
+    building its summaries, routing against all earlier segments and attending
+    (forward only), with every segment's Q, K and V resident in HBM.  One step is
+    the whole rollout; tokens/s = 131,072 / step time."""
+    import numpy as np
+    import torch
+    import hga_inputs as hi
+    import sparse_long_context_hga_amd as hga
+
+    S, T, Hq, Hkv, d = hi.ROLLOUT_SEG, hi.ROLLOUT_TOKENS, 32, 8, 128
+    n_seg = T // S
+    print(f"[bench] workload rollout_131k: {n_seg} segments of {S} tokens, {Hq}/{Hkv}/{d}, top-16/top-64",
+          file=sys.stderr, flush=True)
+    shape = hga.make_shape(1, Hq, Hkv, d, 16, 64, "bf16", 1.0 / np.sqrt(d))
+    dt = torch.bfloat16
+    kc = torch.zeros(1, Hkv, T, d, dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    qs = []
+    for s_ in range(n_seg):
+        q, k, v = hi.rollout_segment(s_)
+        kc[:, :, s_ * S:(s_ + 1) * S] = torch.from_numpy(k).to(dt).cuda()
+        vc[:, :, s_ * S:(s_ + 1) * S] = torch.from_numpy(v).to(dt).cuda()
+        qs.append(torch.from_numpy(q).to(dt).cuda().contiguous())
+    gsum = torch.zeros(1, Hkv, T // 8, d, dtype=dt, device="cuda")
+    csum = torch.zeros(1, Hkv, T // 64, d, dtype=dt, device="cuda")
+    nb = S // 64
+    cidx = torch.empty(1, Hkv, nb, 16, dtype=torch.int32, device="cuda")
+    gidx = torch.empty(1, Hkv, nb, 64, dtype=torch.int32, device="cuda")
+    o = torch.empty(1, Hq, S, d, dtype=dt, device="cuda")
+    lse = torch.empty(1, Hq, S, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    ev = [[mk() for _ in range(4)] for _ in range(n_seg)]
+    for e in [x for row in ev for x in row]:
+        e.record(stream)
+    torch.cuda.synchronize()
+
+    def rollout(marks):
+        for s_ in range(n_seg):
+            se = ev[s_] if marks else None
+            if se: se[0].record(stream)
+            hga.hga_build_summaries(shape, kc, T, s_ * S, (s_ + 1) * S, gsum, csum)
+            if se: se[1].record(stream)
+            hga.hga_route(shape, qs[s_], csum, gsum, T, s_ * S, S, cidx, gidx)
+            if se: se[2].record(stream)
+            hga.hga_attend_fwd(shape, qs[s_], kc, vc, T, s_ * S, S, gidx, o, lse)
+            if se: se[3].record(stream)
+
+    for _ in range(args.warmup):
+        rollout(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rollout(False)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    rollout(True)                                   # one more, with timing marks
+    torch.cuda.synchronize()
+    kern_ms = {"summaries": 0.0, "route": 0.0, "attend_fwd": 0.0}
+    for s_ in range(n_seg):
+        kern_ms["summaries"] += ev[s_][0].elapsed_time(ev[s_][1])
+        kern_ms["route"] += ev[s_][1].elapsed_time(ev[s_][2])
+        kern_ms["attend_fwd"] += ev[s_][2].elapsed_time(ev[s_][3])
+    # algorithmic bytes of the whole rollout: every segment's summaries (its K read,
+    # summaries written), route (Q and the candidate chunk summaries of every block,
+    # the group summaries of its selected chunks) and forward (Q, gathered and own
+    # K/V, O, LSE); every block selects min(16, J) chunks and then 64 groups once
+    # J >= 8.
+    el = 2
+    work = {"summaries": 0.0, "route": 0.0, "attend_fwd": 0.0}
+    for s_ in range(n_seg):
+        work["summaries"] += Hkv * S * d * el + Hkv * (S // 8 + S // 64) * d * el
+        J = np.arange(nb) + s_ * S // 64
+        nc = np.minimum(16, J)
+        ng = np.minimum(64, 8 * nc)
+        q_bytes = Hq * S * d * el
+        work["route"] += q_bytes + Hkv * float(np.sum(J + 8 * nc)) * d * el
+        work["attend_fwd"] += (2 * q_bytes + Hkv * float(np.sum(8 * ng)) * d * el * 2
+                               + Hkv * nb * 64 * d * el * 2 + Hq * S * 4)
+    kernels = {}
+    for k_, ms in kern_ms.items():
+        gbs = work[k_] / (ms * 1e-3) / 1e9
+        kernels[k_] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(kern_ms, key=lambda k_: kern_ms[k_])
+    ach = work[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    out = {
+        "metric": ROLLOUT_METRIC, "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rollout_131k", "batch": 1, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
+                   "segments": n_seg, "seg_len": S, "context": T, "top_chunks": 16, "top_groups": 64,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom},
+        "kernels": kernels,
+        "kernel_timing": "HIP events around every call of one extra, marked rollout (summed over the 64 segments)",
+    }
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -411,6 +518,8 @@ def main():
     hga.lib()
     if args.workload.startswith("decode"):
         return main_decode(args)
+    if args.workload == "rollout_131k":
+        return main_rollout(args)
     w = make_workload(args.workload)
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
           f"t_hist={w.t_hist} S={w.seg_len} k_c={w.top_chunks} k_g={w.top_groups}", file=sys.stderr, flush=True)
