@@ -237,75 +237,10 @@ struct RouteShared {
   uint32_t gkeys[kMaxGroupCand + 4];
   int csel[64];
   int gsel[kMaxGroupCand];
-  uint64_t win[kDecWaves * 64];  // each wave's best chunk candidates (k_c per wave)
-  uint64_t fin[64];              // the selected chunks, best first
   uint32_t cscr[64];             // score keys of csel
+  TopkShared<kDecThreads> top;
   int nsel, flag;
 };
-
-// Wave 0: the selected chunks fin[0 .. n) (any order) to csel / cscr in ascending
-// chunk order (rank = number of selected chunks with a lower index).
-__device__ __forceinline__ void sort_selected(RouteShared& sm, int n) {
-  const int lane = threadIdx.x & 63;
-  if (lane < n) {
-    const uint64_t x = sm.fin[lane];
-    const int idx = cand_index(x);
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) rank += j < n && cand_index(sm.fin[j]) < idx;
-    sm.csel[rank] = idx;
-    sm.cscr[rank] = (uint32_t)(x >> 32);
-  }
-  if (lane == 0) sm.nsel = n;
-}
-
-// Top-k_c (1 <= k_c <= 64) of N candidates (cand_at(i), i < N): wave 0 alone
-// (P = N/64 per lane, N <= 512), or each wave over P per lane (i = tid + 256 p)
-// and then wave 0 over the waves' best (P2 per lane).  The result goes to csel in
-// ascending chunk order; returns its size (all threads).
-template <int P, typename F>
-__device__ __forceinline__ int select_one_wave(RouteShared& sm, int N, int kc, const F& cand_at) {
-  if ((threadIdx.x >> 6) == 0) {
-    const int lane = threadIdx.x & 63;
-    uint64_t v[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) v[i] = lane + 64 * i < N ? cand_at(lane + 64 * i) : 0;
-    sort_selected(sm, wave_select<P>(v, kc, sm.fin));
-  }
-  __syncthreads();
-  return sm.nsel;
-}
-template <int P, int P2, typename F>
-__device__ __forceinline__ int select_two_stage(RouteShared& sm, int N, int kc, const F& cand_at) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint64_t v[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) v[i] = tid + kDecThreads * i < N ? cand_at(tid + kDecThreads * i) : 0;
-  uint64_t* mine = sm.win + w * kc;
-  const int m = wave_select<P>(v, kc, mine);
-  for (int i = m + lane; i < kc; i += 64) mine[i] = 0;
-  __syncthreads();
-  if (w == 0) {
-    uint64_t u[P2];
-#pragma unroll
-    for (int q = 0; q < P2; ++q) u[q] = lane + 64 * q < kDecWaves * kc ? sm.win[lane + 64 * q] : 0;
-    sort_selected(sm, wave_select<P2>(u, kc, sm.fin));
-  }
-  __syncthreads();
-  return sm.nsel;
-}
-template <typename F>
-__device__ __forceinline__ int select_chunks(RouteShared& sm, int N, int kc, const F& cand_at) {
-  if (N <= 64) return select_one_wave<1>(sm, N, kc, cand_at);
-  if (N <= 128) return select_one_wave<2>(sm, N, kc, cand_at);
-  if (N <= 256) return select_one_wave<4>(sm, N, kc, cand_at);
-  if (N <= 512) return select_one_wave<8>(sm, N, kc, cand_at);
-  constexpr int P2 = 4;   // 4 waves x k_c <= 256 candidates
-  if (N <= 1024) return select_two_stage<4, P2>(sm, N, kc, cand_at);
-  if (N <= 2048) return select_two_stage<8, P2>(sm, N, kc, cand_at);
-  if (N <= 4096) return select_two_stage<16, P2>(sm, N, kc, cand_at);
-  return select_two_stage<32, P2>(sm, N, kc, cand_at);
-}
 
 // Top-k_g of the group keys[0 .. n) (n <= 512), ascending slots (= ascending group ids).
 template <int P>
@@ -340,15 +275,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_route_kernel(DecodeArgs a)
     __syncthreads();
     if (tid < 64) {
       uint64_t v[1] = {tid < nrows ? cand(sm.ckeys[tid], c0 + tid) : 0};
-      const int m = wave_select<1>(v, a.kc, sm.fin);
-      if (tid < a.kc) put(cands + slice * a.kc + tid, tid < m ? sm.fin[tid] : 0ull);
+      const int m = wave_select<1>(v, a.kc, sm.top.fin);
+      if (tid < a.kc) put(cands + slice * a.kc + tid, tid < m ? sm.top.fin[tid] : 0ull);
     }
   }
   if (!arrive_last(a.rcount + unit, a.n_slices, &sm.flag)) return;
 
   // ---- the last work-group of the unit: top-k_c, group scores, top-k_g
   const int N = a.kc > 0 ? (J + kSliceChunks - 1) / kSliceChunks * a.kc : 0;
-  const int nc = N == 0 ? 0 : select_chunks(sm, N, a.kc, [&](int i) { return get(cands + i); });
+  const int nc = N == 0 ? 0 : topk64(sm.top, N, a.kc, sm.csel, sm.cscr, [&](int i) { return get(cands + i); });
   const int ng_cand = 8 * nc;
   if (ng_cand > 0 && a.kg > 0) {
     load_q<T, D, G>(a, b, kvh, qv, 1.0f);

@@ -88,61 +88,6 @@ __device__ int block_topk(const uint32_t* keys, int n, int k, int* out, SelectSh
   return k;
 }
 
-// The same selection for small candidate sets (n <= kRankMax): candidate i is taken
-// iff fewer than k candidates beat it.  With v = key << 32 | (2^32 - 1 - index),
-// "j beats i" (a larger key, or an equal key at a lower index) is v_j > v_i: one
-// 64-bit compare per pair.  Thread t owns the contiguous candidates [t*per, t*per +
-// per), so an exclusive scan of the per-thread counts places the selected ids in
-// ascending order.  pk: LDS scratch of at least n + 1 entries.
-constexpr int kRankMax = 1024;
-template <int NT>
-__device__ int block_topk_rank(const uint32_t* keys, int n, int k, int* out, SelectShared<NT>& sh, uint64_t* pk) {
-  static_assert(4 * NT >= kRankMax, "at most 4 candidates per thread");
-  const int tid = threadIdx.x;
-  if (k <= 0 || n <= 0) return 0;
-  const int n16 = (n + 15) & ~15;   // zero padding never beats a real candidate (key > 0)
-  for (int i = tid; i < n16; i += NT)
-    pk[i] = i < n ? ((uint64_t)keys[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
-  __syncthreads();
-  const int per = (n + NT - 1) / NT;   // 1 .. 4
-  const int lo = tid * per, hi = min(n, lo + per);
-  uint64_t mine[4];
-  int beat[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int u = 0; u < 4; ++u) mine[u] = lo + u < hi ? pk[lo + u] : ~0ull;
-  const uint4* pk4 = reinterpret_cast<const uint4*>(pk);
-  // 16 candidates per step: 8 broadcast reads in flight, then the compares (waves
-  // that own no candidate skip the loop).
-  for (int j = 0; lo < hi && j < n16 / 2; j += 8) {
-    uint4 kv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kv[e] = pk4[j + e];
-    if (per == 1) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        beat[0] += ((((uint64_t)kv[e].y << 32) | kv[e].x) > mine[0]) + ((((uint64_t)kv[e].w << 32) | kv[e].z) > mine[0]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint64_t a0 = ((uint64_t)kv[e].y << 32) | kv[e].x, a1 = ((uint64_t)kv[e].w << 32) | kv[e].z;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) beat[u] += (a0 > mine[u]) + (a1 > mine[u]);
-      }
-    }
-  }
-  int cnt = 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) cnt += (lo + u < hi) && beat[u] < k;
-  int tot;
-  int o = block_exclusive_scan<NT>(cnt, sh.scan, tot);
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if ((lo + u < hi) && beat[u] < k) out[o++] = lo + u;
-  __syncthreads();
-  return tot;
-}
-
-
 // ---------------------------------------------------------------- one-wave selection
 // Candidates for the selection: score key << 32 | (2^32 - 1 - index), so that a
 // larger value is a higher score or, at equal score, a lower index; 0 = none.
@@ -221,6 +166,92 @@ __device__ __forceinline__ int wave_topk_sorted(const uint32_t* keys, int n, int
   }
   __syncthreads();
   return *sm_n;
+}
+
+// ---------------------------------------------------------------- top-k of at most 64, any n
+// Scratch of topk64 for a work-group of NT threads.
+template <int NT>
+struct TopkShared {
+  uint64_t win[NT];   // each wave's best k (k <= 64)
+  uint64_t fin[64];   // the selected candidates, any order
+  int nsel;
+};
+
+// Lanes n' < n of the calling wave: the candidates fin[0 .. n) (distinct, any order)
+// to out / out_keys (nullable) in ascending index order; a candidate's slot is the
+// number of selected candidates with a lower index.
+__device__ __forceinline__ void sort_by_index(const uint64_t* fin, int n, int* out, uint32_t* out_keys) {
+  const int lane = threadIdx.x & 63;
+  if (lane < n) {
+    const uint64_t x = fin[lane];
+    const int idx = cand_index(x);
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) rank += j < n && cand_index(fin[j]) < idx;
+    out[rank] = idx;
+    if (out_keys) out_keys[rank] = (uint32_t)(x >> 32);
+  }
+}
+
+template <int NT, int P, typename F>
+__device__ __forceinline__ int topk64_one_wave(TopkShared<NT>& sh, int n, int k, int* out, uint32_t* out_keys,
+                                               const F& cand_at) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    uint64_t v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) v[i] = lane + 64 * i < n ? cand_at(lane + 64 * i) : 0;
+    const int m = wave_select<P>(v, k, sh.fin);
+    sort_by_index(sh.fin, m, out, out_keys);
+    if (lane == 0) sh.nsel = m;
+  }
+  __syncthreads();
+  return sh.nsel;
+}
+
+// Every wave keeps the best k of its candidates (i = tid + NT p), then wave 0 selects
+// among the waves' NW k (P2 per lane).
+template <int NT, int P, int P2, typename F>
+__device__ __forceinline__ int topk64_two_stage(TopkShared<NT>& sh, int n, int k, int* out, uint32_t* out_keys,
+                                                const F& cand_at) {
+  constexpr int NW = NT / 64;
+  static_assert(64 * P2 >= NT, "room for every wave's best 64");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint64_t v[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) v[i] = tid + NT * i < n ? cand_at(tid + NT * i) : 0;
+  uint64_t* mine = sh.win + w * k;
+  const int m = wave_select<P>(v, k, mine);
+  for (int i = m + lane; i < k; i += 64) mine[i] = 0;
+  __syncthreads();
+  if (w == 0) {
+    uint64_t u[P2];
+#pragma unroll
+    for (int q = 0; q < P2; ++q) u[q] = lane + 64 * q < NW * k ? sh.win[lane + 64 * q] : 0;
+    const int m2 = wave_select<P2>(u, k, sh.fin);
+    sort_by_index(sh.fin, m2, out, out_keys);
+    if (lane == 0) sh.nsel = m2;
+  }
+  __syncthreads();
+  return sh.nsel;
+}
+
+// Top-k (1 <= k <= 64) of the n candidates cand_at(i), i < n <= 8192 (nonzero,
+// distinct 64-bit candidate values, see cand), written to out (and their score keys
+// to out_keys, nullable) in ascending index order.  Returns min(k, n); all threads
+// of the work-group must call it.
+template <int NT, typename F>
+__device__ __forceinline__ int topk64(TopkShared<NT>& sh, int n, int k, int* out, uint32_t* out_keys,
+                                      const F& cand_at) {
+  static_assert(NT == 256, "candidate counts per lane below are sized for 4 waves");
+  if (n <= 64) return topk64_one_wave<NT, 1>(sh, n, k, out, out_keys, cand_at);
+  if (n <= 128) return topk64_one_wave<NT, 2>(sh, n, k, out, out_keys, cand_at);
+  if (n <= 256) return topk64_one_wave<NT, 4>(sh, n, k, out, out_keys, cand_at);
+  if (n <= 512) return topk64_one_wave<NT, 8>(sh, n, k, out, out_keys, cand_at);
+  if (n <= 1024) return topk64_two_stage<NT, 4, 4>(sh, n, k, out, out_keys, cand_at);
+  if (n <= 2048) return topk64_two_stage<NT, 8, 4>(sh, n, k, out, out_keys, cand_at);
+  if (n <= 4096) return topk64_two_stage<NT, 16, 4>(sh, n, k, out, out_keys, cand_at);
+  return topk64_two_stage<NT, 32, 4>(sh, n, k, out, out_keys, cand_at);
 }
 
 }  // namespace

@@ -79,8 +79,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   __shared__ __align__(16) uint32_t gkeys[kMaxGroupCand + 4];
   __shared__ int csel[64];
   __shared__ int gsel[kMaxGroupCand];
-  __shared__ SelectShared<kRouteThreads> sh;
-  __shared__ __align__(16) uint64_t pk[kRankMax + 16];
+  __shared__ TopkShared<kRouteThreads> top;
   __shared__ int nsel;
   auto SB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (B() == 0) return sb0; else return sb1;
@@ -182,14 +181,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   __syncthreads();
   if (J > 0) score_rows(J, chunk_row, ckeys, qf);
   __syncthreads();
-  // ascending chunk ids: one wave's bit search up to 512 candidates, block-wide above
+  // ascending chunk ids: one wave's bit search up to 512 candidates; above, every
+  // wave keeps the best k_c of its share and one wave selects among those
   const int nc = (J == 0 || a.kc == 0) ? 0
                  : J <= 64              ? wave_topk_sorted<1>(ckeys, J, a.kc, csel, &nsel)
                  : J <= 128             ? wave_topk_sorted<2>(ckeys, J, a.kc, csel, &nsel)
                  : J <= 256             ? wave_topk_sorted<4>(ckeys, J, a.kc, csel, &nsel)
                  : J <= 512             ? wave_topk_sorted<8>(ckeys, J, a.kc, csel, &nsel)
-                 : J <= kRankMax        ? block_topk_rank(ckeys, J, a.kc, csel, sh, pk)
-                                        : block_topk(ckeys, J, a.kc, csel, sh);
+                                        : topk64(top, J, a.kc, csel, (uint32_t*)nullptr,
+                                                 [&](int i) { return cand(ckeys[i], i); });
 
   // ---- group scores over the 8 groups of each selected chunk, then top-k_g
   const int ng_cand = 8 * nc;

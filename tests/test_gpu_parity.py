@@ -110,6 +110,41 @@ def test_route_accepted(chk, cases, name):
     print(f"near-tie exemptions: {exempt}")
 
 
+LONG_HISTORY = {
+    # the blocks' candidate counts J span each regime of the chunk selection: the
+    # two-stage selection at 4, 8, 16 and 32 candidates per lane, the last at the
+    # library's maximum of 8,192 chunks
+    "j600_kc64": dict(t_hist=600 * 64, top_chunks=64, top_groups=100),
+    "j1500_kc16": dict(t_hist=1500 * 64, top_chunks=16, top_groups=64),
+    "j3000_kc33": dict(t_hist=3000 * 64, top_chunks=33, top_groups=200),
+    "j8188_kc64": dict(t_hist=8188 * 64, top_chunks=64, top_groups=511),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_HISTORY))
+def test_route_long_history(chk, name):
+    """Routing over histories of 600 to 8,191 candidate chunks: every unit accepted
+    against the oracle's scores, and the reported chunk scores match them."""
+    w = hi.random_layer(seed=70, batch=1, n_q_heads=2, n_kv_heads=1, head_dim=64, seg_len=256,
+                        chunk_mean_var=0.5, backward=False, name=name, **LONG_HISTORY[name])
+    print(f"case {name}", flush=True)
+    gs, cs = chk.oracle_summaries(w)
+    L = chk.DeviceLayer(w)
+    L.summaries(0, w.t_hist + w.seg_len)
+    L.route()
+    torch.cuda.synchronize()
+    cidx, gidx, cscore = L.cidx.cpu().numpy(), L.gidx.cpu().numpy(), L.cscore.cpu().numpy()
+    exempt = 0
+    for j in range(w.seg_len // 64):
+        exempt += chk.check_route_unit(w, gs, cs, 0, 0, j, cidx[0, 0, j], gidx[0, 0, j])
+        J = w.t_hist // 64 + j
+        sig = ora.block_scores(ora.block_rows(w.q, 0, 0, j, w.group_size), cs[0, 0, :J])
+        assert np.all(cidx[0, 0, j] >= 0)
+        for i, c in enumerate(cidx[0, 0, j]):
+            assert abs(cscore[0, 0, j, i] - sig[c]) <= 1e-5 * max(1.0, abs(sig[c]))
+    print(f"near-tie exemptions: {exempt}")
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_forward_on_oracle_selection(chk, cases, name):
     w, _, _, _, gidx = cases[name]
