@@ -120,37 +120,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
           if (bt + 1 < n_batches) issue(bt + 1, ic<1 - B()>{});
           ro.refresh();
           const uint16_t* tb = SB(B);
-          static_for<0, 2>([&](auto ST2) {       // pairs of 32-row subtiles of the batch
-            bf16x8 bfr[2][KS];
-            static_for<0, 2>([&](auto U) {
-              constexpr int ST = 2 * ST2() + U();
+          // The batch's four 32-row subtiles are read at once and scored as four
+          // independent MFMA chains per row tile, so the matrix unit stays busy while
+          // the maxima of the previous row tile are taken.
+          bf16x8 bfr[4][KS];
+          static_for<0, 4>([&](auto ST) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              bfr[ST()][ks] = ro.template read<(ST() & 1) * 32 * D * 2>(tb + (ST() >> 1) * 64 * D, ks);
+          });
+          float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+          for (int i = 0; i < RPW; ++i) {
+            if (NRT % 4 == 0 || w + 4 * i < NRT) {
+              f32x16 acc[4] = {};
 #pragma unroll
               for (int ks = 0; ks < KS; ++ks)
-                bfr[U()][ks] = ro.template read<(ST & 1) * 32 * D * 2>(tb + (ST >> 1) * 64 * D, ks);
-            });
-            float best[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-              if (w + 4 * i < NRT) {
-                f32x16 acc0 = {}, acc1 = {};
+                for (int st = 0; st < 4; ++st) acc[st] = mfma32(qf[i][ks], bfr[st][ks], acc[st]);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                  acc0 = mfma32(qf[i][ks], bfr[0][ks], acc0);
-                  acc1 = mfma32(qf[i][ks], bfr[1][ks], acc1);
-                }
+              for (int st = 0; st < 4; ++st)
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                  best[0] = fmaxf(best[0], acc0[rr]);
-                  best[1] = fmaxf(best[1], acc1[rr]);
-                }
-              }
+                for (int rr = 0; rr < 16; ++rr) best[st] = fmaxf(best[st], acc[st][rr]);
             }
-            static_for<0, 2>([&](auto U) {
-              const int r = bt * kBatch + 32 * (2 * ST2() + U()) + n;
-              const float bb = half_max(best[U()]);
-              if (h == 0 && r < n_rows && w < NRT) atomicMax(&keys[r], score_key(bb));
-            });
-          });
+          }
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int r = bt * kBatch + 32 * st + n;
+            const float bb = half_max(best[st]);
+            if (h == 0 && r < n_rows && w < NRT) atomicMax(&keys[r], score_key(bb));
+          }
         }
       });
     }
