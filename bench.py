@@ -40,7 +40,9 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=300,
+                   help="untimed steps first (default 300): the GPU clock ramps up over the first tens of "
+                        "milliseconds of sustained work, so the timed steps see its steady state")
     p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
                    choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k",
                             "decode_b8_ctx32k", "rollout_131k"],
