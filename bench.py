@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run a fill and a scale-copy kernel of this size (reference for HBM counters)")
+    p.add_argument("--mfma-summary", metavar="COUNTER_CSV",
+                   help="no GPU work: reduce a rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 counter_collection.csv "
+                        "into the MFMA summary under profiles/")
     p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                         "WRITE_SIZE) of a --copy-calibration-mib run into the traffic summary under profiles/")
@@ -116,6 +119,7 @@ def algorithmic_work(w, gidx):
 
 PMC_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_hbm_traffic.json"),
                  "decode_b8_ctx32k": os.path.join(ROOT, "profiles", "hga_decode_ctx32k_hbm_traffic.json")}
+MFMA_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_mfma.json")}
 CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 # kernel-name prefix -> step kernel (first match wins)
 KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_", "route"), ("attend_fwd_", "attend_fwd"),
@@ -168,6 +172,56 @@ def traffic_summary(fetch_csv, write_csv, calib_mib, workload):
     for k in out["kernels"].values():
         k["hbm_bytes_per_launch"] = k.get("fetch_bytes_per_launch", 0) + k.get("write_bytes_per_launch", 0)
     return out
+
+
+def mfma_summary(counter_csv, workload):
+    """Matrix-core use of each step kernel from one counter pass (rocprofv3 derived
+    counters, per dispatch): MfmaUtil = busy cycles of the MFMA units over (GPU
+    active cycles x SIMDs), in percent; MfmaFlopsBF16 = bf16 MFMA operations x 512
+    flops, as the hardware counts them (masked and padded work included).  Averaged
+    over the step's dispatches of each kernel (most frequent grid)."""
+    import csv
+    import collections
+    out = {"workload": workload, "source_sha256": kernel_source_digest(workload), "kernels": {}}
+    groups = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(counter_csv)):
+        short = _short_name(r["Kernel_Name"])
+        key = next((k for pre, k in KERNEL_KEYS if short.startswith(pre)), None)
+        if key is None:
+            continue
+        groups[(key, r["Grid_Size"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    best = {}
+    for (key, _grid), cnt in groups.items():
+        n = len(cnt.get("MfmaUtil", []))
+        if key not in best or n > best[key][0]:
+            best[key] = (n, cnt)
+    for key, (n, cnt) in sorted(best.items()):
+        out["kernels"][key] = {
+            "launches": n,
+            "mfma_util_pct": round(statistics.mean(cnt["MfmaUtil"]), 2) if cnt.get("MfmaUtil") else None,
+            "mfma_bf16_flops_per_launch": round(statistics.mean(cnt["MfmaFlopsBF16"]))
+            if cnt.get("MfmaFlopsBF16") else None,
+        }
+    return out
+
+
+def measured_mfma(kernel, workload, ms):
+    """Counter figures of `kernel` from the committed MFMA summary, with the hardware
+    bf16 MFMA rate over the HIP-event duration `ms`; None when no summary exists for
+    this workload or the kernels changed since it was taken."""
+    try:
+        with open(MFMA_SUMMARIES[workload]) as f:
+            summ = json.load(f)
+    except (KeyError, OSError, ValueError):
+        return None
+    if summ.get("workload") != workload or summ.get("source_sha256") != kernel_source_digest(workload):
+        return None
+    k = summ.get("kernels", {}).get(kernel)
+    if k is None or k.get("mfma_bf16_flops_per_launch") is None:
+        return None
+    tfl = k["mfma_bf16_flops_per_launch"] / (ms * 1e-3) / 1e12
+    return {"util_pct": k.get("mfma_util_pct"), "hw_bf16_tflops": round(tfl, 2),
+            "frac_of_peak": round(tfl / BF16_PEAK_TFLOPS, 4)}
 
 
 # Kernel sources each measured workload runs (device headers included).
@@ -497,6 +551,12 @@ def main_rollout(args):
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.mfma_summary:
+        summ = mfma_summary(args.mfma_summary, args.workload)
+        with open(MFMA_SUMMARIES[args.workload], "w") as f:
+            json.dump(summ, f, indent=1)
+        print(json.dumps(summ, indent=1))
+        return
     if args.traffic_summary:
         if not args.copy_calibration_mib:
             raise SystemExit("--traffic-summary needs the --copy-calibration-mib of the profiled run")
@@ -604,6 +664,10 @@ def main():
         tfl = wk["flops"] / (ms * 1e-3) / 1e12
         kernels[k] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "TFLOP/s": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
+        if args.routing == "block":
+            mc = measured_mfma(k, w.name, ms)
+            if mc is not None:
+                kernels[k]["mfma_counters"] = mc
     dom = max(kern_ms, key=lambda k: kern_ms[k])
     wk = work.get(dom, {"bytes": 0.0, "flops": 0.0})
     intensity = wk["flops"] / max(wk["bytes"], 1.0)
