@@ -232,14 +232,23 @@ WORKLOAD_SOURCES = {
 }
 
 
+def _code_only(text):
+    """C++ source without comments and with every whitespace run folded to one
+    space (string and character literals kept as they are)."""
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    text = tok.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(workload):
-    """sha256 over the kernel sources the workload runs: counter figures are only
-    valid for this exact code."""
+    """sha256 over the code of the kernel sources the workload runs (comments and
+    layout left out): counter figures are only valid for this exact code."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(WORKLOAD_SOURCES[workload]):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

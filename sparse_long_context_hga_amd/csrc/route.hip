@@ -25,8 +25,10 @@
 // meet in LDS through an atomic max on order-preserving integer keys.  The top-k
 // (up to 512 candidates) is one wave's most-significant-bit-first search for the
 // k-th largest (key, index) pair, counting with ballots, then an index-ordered
-// compaction; larger candidate sets use a block-wide rank or radix select.  All
-// are exact and deterministic, ties resolved by index.
+// compaction; above 512 candidate chunks every wave keeps the best k_c of its
+// share the same way and one wave selects among those.  All are exact and
+// deterministic, ties resolved by index.  The fp32 path uses a block-wide radix
+// select.
 #include "hga_device.h"
 #include "hga_internal.h"
 #include "hga_select.h"
@@ -63,8 +65,9 @@ __device__ __forceinline__ const T* routing_row(const RouteArgs& a, int b, int h
 // ---------------------------------------------------------------- bf16 / MFMA
 // Rows of the block: row = hh * 64 + pos (hh = query head within the KV group).
 // Row tile rt (32 rows) belongs to wave rt % 4.  Candidate summaries are copied
-// into swizzled LDS tiles in batches of 128 rows (double-buffered) and scored
-// from there: each batch is read from memory once per work-group.
+// into swizzled LDS tiles in batches of 128 rows (two buffers: the next batch
+// is copied while one is scored) and scored from there: each batch is read from
+// memory once per work-group.
 constexpr int kBatch = 128;   // summary rows per batch (two 64-row tiles)
 
 template <int D, int G>

@@ -97,3 +97,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_source_digest_ignores_comments_only(tmp_path, monkeypatch):
+    import shutil
+    for name in bench.WORKLOAD_SOURCES["decode_b8_ctx32k"]:
+        shutil.copy(os.path.join(bench.CSRC, name), tmp_path / name)
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    d0 = bench.kernel_source_digest("decode_b8_ctx32k")
+    p = tmp_path / "decode.hip"
+    src = p.read_text()
+    p.write_text("// a new comment line\n" + src.replace("\n", "\n\n", 3) + "\n/* trailing */\n")
+    assert bench.kernel_source_digest("decode_b8_ctx32k") == d0
+    p.write_text(src + "\nstatic int unused_for_test = 1;\n")
+    assert bench.kernel_source_digest("decode_b8_ctx32k") != d0
+    assert bench._code_only('x = "a // b"; // tail\ny /* z */ = 1;') == 'x = "a // b"; y = 1;'

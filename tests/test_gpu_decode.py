@@ -5,8 +5,8 @@ arrives.
 
 Cases span ragged positions (first chunk, mid-chunk, chunk-completing, idle
 slots), every GQA width, both head sizes, both dtypes, a zero budget, budgets
-above the candidate count, and a context long enough for the radix select
-(more than 1,024 candidate chunks).  Routing is checked with the near-tie
+above the candidate count, and contexts of 2,047 and 4,095 candidate chunks
+(the merge of the per-slice candidates by one wave, and by every wave then one).  Routing is checked with the near-tie
 acceptance rule; attention on the oracle's own selection; summaries bit-exactly.
 Expected values come only from the oracle.
 """
@@ -34,8 +34,10 @@ CASES = {
                        pos=[767, 900], top_chunks=4, top_groups=19, dtype="f32"),
     "f32_g1_d128": dict(seed=77, batch=2, n_q_heads=2, n_kv_heads=2, head_dim=128, t_cap=512,
                         pos=[5, 319], top_chunks=2, top_groups=11, dtype="f32"),
-    "bf16_long_ctx_radix": dict(seed=78, batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, t_cap=131072,
-                                pos=[131066], top_chunks=16, top_groups=64, chunk_mean_var=0.5),
+    "bf16_ctx128k": dict(seed=78, batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, t_cap=131072,
+                         pos=[131066], top_chunks=16, top_groups=64, chunk_mean_var=0.5),
+    "bf16_ctx256k_two_stage": dict(seed=79, batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64, t_cap=262144,
+                                   pos=[262130], top_chunks=33, top_groups=100, chunk_mean_var=0.5),
 }
 
 
