@@ -58,7 +58,8 @@ struct BwdArgs {
   int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
   int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
   int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
-  int* order;       // [1 + B*Hkv*S/64*kMaxParts] number of work items, then the items heaviest first
+  int* order;       // [4 + 4*B*Hkv*S/64*kMaxParts] number of work items (padded to 16 bytes), then the
+                    // items heaviest first, each {unit * kMaxParts + part, parts of the unit, visits of the unit, 0}
   float* parts;     // [B, Hkv, S/64, kMaxParts, 2, 64, d] fp32 partials (workspace)
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kg, nb, n_units;
@@ -317,7 +318,7 @@ struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) ve
   static size_t vis_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
   static size_t order_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
   static size_t part_off(size_t rows, size_t units, size_t nb) {
-    return up(order_off(rows, units, nb) + (1 + units * kMaxParts) * 4);
+    return up(order_off(rows, units, nb) + (4 + 4 * units * kMaxParts) * 4);
   }
 };
 
@@ -354,7 +355,10 @@ __global__ __launch_bounds__(kOrderThreads) void attend_bwd_order_kernel(BwdArgs
   __syncthreads();
   for (int u = tid; u < a.n_units; u += kOrderThreads) {
     const int np_u = a.flags[u], r_u = G * a.nvis[u];
-    for (int k = 0; k < np_u; ++k) a.order[1 + atomicAdd(&cnt[size_of(np_u, r_u, k)], 1)] = u * kMaxParts + k;
+    const int nv_u = a.nvis[u];
+    for (int k = 0; k < np_u; ++k)
+      reinterpret_cast<int4*>(a.order + 4)[atomicAdd(&cnt[size_of(np_u, r_u, k)], 1)] =
+          make_int4(u * kMaxParts + k, np_u, nv_u, 0);
   }
 }
 
@@ -366,7 +370,6 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   __shared__ __align__(16) float ls0[64], dr0[64], ls1[64], dr1[64], ls2[64], dr2[64];
   __shared__ uint32_t vmask[kMaxBlocks];   // group mask of the i-th attending block
   __shared__ int vlist[kMaxBlocks];        // i-th attending block
-  __shared__ int s_item;
   auto QB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (B() == 0) return q0; else if constexpr (B() == 1) return q1; else return q2;
   };
@@ -381,15 +384,20 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   };
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
-  // Work item number blockIdx.x of the list the order kernel wrote (heaviest first).
-  if ((int)blockIdx.x >= a.order[0]) return;
-  if (tid == 0) s_item = a.order[1 + blockIdx.x];
-  __syncthreads();
-  const int item = s_item;
+  // Work item number blockIdx.x of the list the order kernel wrote (heaviest first),
+  // with its unit's part and visit counts: the count and the entry are loaded
+  // together (the entry lies inside the list's capacity) and the entry is used
+  // only below the count.
+  const int n_items = a.order[0];
+  const int4 entry = reinterpret_cast<const int4*>(a.order + 4)[blockIdx.x];
+  if ((int)blockIdx.x >= n_items) return;
+  const int item = __builtin_amdgcn_readfirstlane(entry.x);
+  const int np = __builtin_amdgcn_readfirstlane(entry.y);
+  const int n_visits = __builtin_amdgcn_readfirstlane(entry.z);
   if (item < 0) return;
   const int part = item % kMaxParts;
   const int unit = item / kMaxParts;
-  if (unit >= a.n_units || part >= a.flags[unit]) return;   // not an item of this selection
+  if (unit >= a.n_units || part >= np || n_visits > a.nb) return;   // not an item of this selection
   const int cc = unit % a.nb;                      // active chunk == its own query block
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
@@ -399,18 +407,6 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   const int kh = w & 1, rh = w >> 1;
   const int key = 32 * kh + n;                     // this lane's key (operand-B column)
   const int64_t tok = cglob * kChunk + key;
-
-  const int np = a.flags[unit];
-  const int n_visits = a.nvis[unit];
-  for (int i = tid; i < n_visits; i += 256) {
-    const int v = a.vis[(int64_t)unit * a.nb + i];
-    vlist[i] = v & 0xFFFF;
-    vmask[i] = (uint32_t)v >> 16;
-  }
-  __syncthreads();
-  // This item's slice of the chunk's rounds (round r = attending block r / G, query head r % G).
-  const int rounds = G * n_visits;
-  const int r_lo = part * rounds / np, r_hi = (part + 1) * rounds / np;
 
   bf16x8 kf[KS], vf[KS];
   {
@@ -422,6 +418,16 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
       vf[ks] = *reinterpret_cast<const bf16x8*>(vp + 16 * ks + 8 * h);
     }
   }
+  for (int i = tid; i < n_visits; i += 256) {
+    const int v = a.vis[(int64_t)unit * a.nb + i];
+    vlist[i] = v & 0xFFFF;
+    vmask[i] = (uint32_t)v >> 16;
+  }
+  __syncthreads();
+  // This item's slice of the chunk's rounds (round r = attending block r / G, query head r % G).
+  const int rounds = G * n_visits;
+  const int r_lo = part * rounds / np, r_hi = (part + 1) * rounds / np;
+
 
   const uint16_t* qg = (const uint16_t*)a.q;
   const uint16_t* dg = (const uint16_t*)a.d_o;

@@ -8,7 +8,8 @@
 namespace hga {
 namespace {
 
-constexpr int kRouteThreads = 256;   // threads of the segment path's routing work-groups
+constexpr int kRouteThreads = 512;      // threads of the segment path's bf16 routing work-groups
+constexpr int kRouteThreadsF32 = 256;   // and of its fp32 ones
 constexpr int kMaxChunks = 8192;     // = HGA_MAX_CHUNKS
 constexpr int kMaxGroupCand = 512;   // 8 * max top_chunks
 
@@ -236,22 +237,24 @@ __device__ __forceinline__ int topk64_two_stage(TopkShared<NT>& sh, int n, int k
   return sh.nsel;
 }
 
-// Top-k (1 <= k <= 64) of the n candidates cand_at(i), i < n <= 8192 (nonzero,
+// Top-k (1 <= k <= 64) of the n candidates cand_at(i), i < n <= 32 NT (nonzero,
 // distinct 64-bit candidate values, see cand), written to out (and their score keys
 // to out_keys, nullable) in ascending index order.  Returns min(k, n); all threads
 // of the work-group must call it.
 template <int NT, typename F>
 __device__ __forceinline__ int topk64(TopkShared<NT>& sh, int n, int k, int* out, uint32_t* out_keys,
                                       const F& cand_at) {
-  static_assert(NT == 256, "candidate counts per lane below are sized for 4 waves");
+  static_assert(NT == 256 || NT == 512, "4 or 8 waves");
+  constexpr int P2 = NT / 64;   // the waves' best k (<= 64 each), per lane of the final wave
   if (n <= 64) return topk64_one_wave<NT, 1>(sh, n, k, out, out_keys, cand_at);
   if (n <= 128) return topk64_one_wave<NT, 2>(sh, n, k, out, out_keys, cand_at);
   if (n <= 256) return topk64_one_wave<NT, 4>(sh, n, k, out, out_keys, cand_at);
   if (n <= 512) return topk64_one_wave<NT, 8>(sh, n, k, out, out_keys, cand_at);
-  if (n <= 1024) return topk64_two_stage<NT, 4, 4>(sh, n, k, out, out_keys, cand_at);
-  if (n <= 2048) return topk64_two_stage<NT, 8, 4>(sh, n, k, out, out_keys, cand_at);
-  if (n <= 4096) return topk64_two_stage<NT, 16, 4>(sh, n, k, out, out_keys, cand_at);
-  return topk64_two_stage<NT, 32, 4>(sh, n, k, out, out_keys, cand_at);
+  if (n <= NT * 2) return topk64_two_stage<NT, 2, P2>(sh, n, k, out, out_keys, cand_at);
+  if (n <= NT * 4) return topk64_two_stage<NT, 4, P2>(sh, n, k, out, out_keys, cand_at);
+  if (n <= NT * 8) return topk64_two_stage<NT, 8, P2>(sh, n, k, out, out_keys, cand_at);
+  if (n <= NT * 16) return topk64_two_stage<NT, 16, P2>(sh, n, k, out, out_keys, cand_at);
+  return topk64_two_stage<NT, 32, P2>(sh, n, k, out, out_keys, cand_at);
 }
 
 }  // namespace

@@ -17,7 +17,7 @@
 // of the decision lies at or after the block's first position.  Only the source
 // of the query rows differs (RouteArgs::lag).
 //
-// One work-group (256 threads) per (sequence, KV head, query block).  The bf16
+// One work-group per (sequence, KV head, query block).  The bf16
 // path scores with v_mfma_f32_32x32x16_bf16: operand A = 32 query rows (held in
 // registers for the whole kernel), operand B = 32 summary rows, so each lane
 // ends with one candidate column and 16 of the rows and the row-maximum is a
@@ -64,25 +64,32 @@ __device__ __forceinline__ const T* routing_row(const RouteArgs& a, int b, int h
 
 // ---------------------------------------------------------------- bf16 / MFMA
 // Rows of the block: row = hh * 64 + pos (hh = query head within the KV group).
-// Row tile rt (32 rows) belongs to wave rt % 4.  Candidate summaries are copied
+// Row tile rt (32 rows) belongs to waves rt % 4 (and rt % 4 + 4).  Candidate summaries are copied
 // into swizzled LDS tiles in batches of 128 rows (two buffers: the next batch
 // is copied while one is scored) and scored from there: each batch is read from
 // memory once per work-group.
 constexpr int kBatch = 128;   // summary rows per batch (two 64-row tiles)
 
+// Threads of the bf16 router: 8 waves, two per SIMD, up to 4 query heads per KV head;
+// with 8 heads the row tiles take the registers of a wave per SIMD.
+template <int G>
+constexpr int route_threads() { return G >= 8 ? 256 : kRouteThreads; }
+
 template <int D, int G>
-__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) {
+__global__ __launch_bounds__(route_threads<G>()) void route_bf16_kernel(RouteArgs a) {
+  constexpr int NT = route_threads<G>();
   constexpr int KS = D / 16;
   constexpr int NRT = 2 * G;                      // 32-row tiles in the block
   constexpr int RPW = (NRT + 3) / 4;              // row tiles per wave
-  constexpr int NW = kRouteThreads / 64;
+  constexpr int NW = NT / 64;
+  constexpr int SPW = 8 / NW;                     // pairs of a batch's 32-row subtiles per wave
   constexpr int L = 2 * dma_per_wave<D, NW>();    // copies per wave per batch
   __shared__ __align__(16) uint16_t sb0[kBatch * D], sb1[kBatch * D];
   __shared__ __align__(16) uint32_t ckeys[kMaxChunks + 4];
   __shared__ __align__(16) uint32_t gkeys[kMaxGroupCand + 4];
   __shared__ int csel[64];
   __shared__ int gsel[kMaxGroupCand];
-  __shared__ TopkShared<kRouteThreads> top;
+  __shared__ TopkShared<NT> top;
   __shared__ int nsel;
   auto SB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (B() == 0) return sb0; else return sb1;
@@ -95,6 +102,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int J = (int)(a.t_hist / kChunk) + j;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
+  const int wr = w & 3, sp0 = (w >> 2) * SPW;   // row-tile set; first subtile pair of a batch
 
   const uint16_t* cs = (const uint16_t*)a.csum + (int64_t)bh * (a.t_cap / kChunk) * D;
   const uint16_t* gs = (const uint16_t*)a.gsum + (int64_t)bh * (a.t_cap / kGroup) * D;
@@ -123,35 +131,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
           if (bt + 1 < n_batches) issue(bt + 1, ic<1 - B()>{});
           ro.refresh();
           const uint16_t* tb = SB(B);
-          // The batch's four 32-row subtiles are read at once and scored as four
-          // independent MFMA chains per row tile, so the matrix unit stays busy while
-          // the maxima of the previous row tile are taken.
-          bf16x8 bfr[4][KS];
-          static_for<0, 4>([&](auto ST) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-              bfr[ST()][ks] = ro.template read<(ST() & 1) * 32 * D * 2>(tb + (ST() >> 1) * 64 * D, ks);
-          });
-          float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-          for (int i = 0; i < RPW; ++i) {
-            if (NRT % 4 == 0 || w + 4 * i < NRT) {
-              f32x16 acc[4] = {};
+          // With 8 waves, waves w and w + 4 hold the same row tiles and score one pair of
+          // the batch's four 32-row subtiles each (two waves per SIMD); with 4 waves a
+          // wave scores both pairs in turn.  Two independent MFMA chains per row tile.
+          for (int sp = sp0; sp < sp0 + SPW; ++sp) {
+            bf16x8 bfr[2][KS];
+            static_for<0, 2>([&](auto U) {
 #pragma unroll
               for (int ks = 0; ks < KS; ++ks)
+                bfr[U()][ks] = ro.template read<U() * 32 * D * 2>(tb + sp * 64 * D, ks);
+            });
+            float best[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc[st] = mfma32(qf[i][ks], bfr[st][ks], acc[st]);
+            for (int i = 0; i < RPW; ++i) {
+              if (NRT % 4 == 0 || wr + 4 * i < NRT) {
+                f32x16 acc[2] = {};
 #pragma unroll
-              for (int st = 0; st < 4; ++st)
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) best[st] = fmaxf(best[st], acc[st][rr]);
+                  for (int u = 0; u < 2; ++u) acc[u] = mfma32(qf[i][ks], bfr[u][ks], acc[u]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                  for (int rr = 0; rr < 16; ++rr) best[u] = fmaxf(best[u], acc[u][rr]);
+              }
             }
-          }
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const int r = bt * kBatch + 32 * st + n;
-            const float bb = half_max(best[st]);
-            if (h == 0 && r < n_rows && w < NRT) atomicMax(&keys[r], score_key(bb));
+            for (int u = 0; u < 2; ++u) {
+              const int r = bt * kBatch + 64 * sp + 32 * u + n;
+              const float bb = half_max(best[u]);
+              if (h == 0 && r < n_rows && wr < NRT) atomicMax(&keys[r], score_key(bb));
+            }
           }
         }
       });
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   bf16x8 qf[RPW][KS];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
-    const int rt = w + 4 * i;
+    const int rt = wr + 4 * i;
     if (rt < NRT && J > 0) {
       const int hh = rt >> 1, pos = 32 * (rt & 1) + n;
       const uint16_t* qp = routing_row<uint16_t>(a, b, kvh * G + hh, j, pos, D);
@@ -179,7 +189,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   }
 
   // ---- chunk scores and top-k_c over the candidate chunks [0, J)
-  for (int i = tid; i < ((J + 3) & ~3); i += kRouteThreads) ckeys[i] = 0u;
+  for (int i = tid; i < ((J + 3) & ~3); i += NT) ckeys[i] = 0u;
   __syncthreads();
   if (J > 0) score_rows(J, chunk_row, ckeys, qf);
   __syncthreads();
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
 
   // ---- group scores over the 8 groups of each selected chunk, then top-k_g
   const int ng_cand = 8 * nc;
-  for (int i = tid; i < ((ng_cand + 3) & ~3); i += kRouteThreads) gkeys[i] = 0u;
+  for (int i = tid; i < ((ng_cand + 3) & ~3); i += NT) gkeys[i] = 0u;
   __syncthreads();
   if (ng_cand > 0) {
     auto group_row = [&](int r) __attribute__((always_inline)) { return gs + (int64_t)(8 * csel[r >> 3] + (r & 7)) * D; };
@@ -212,11 +222,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
   // ---- outputs
   int32_t* co = a.cidx + (int64_t)unit * a.kc;
   int32_t* go = a.gidx + (int64_t)unit * a.kg;
-  for (int i = tid; i < a.kc; i += kRouteThreads) {
+  for (int i = tid; i < a.kc; i += NT) {
     co[i] = i < nc ? csel[i] : -1;
     if (a.cscore) a.cscore[(int64_t)unit * a.kc + i] = i < nc ? key_score(ckeys[csel[i]]) : -INFINITY;
   }
-  for (int i = tid; i < a.kg; i += kRouteThreads) {
+  for (int i = tid; i < a.kg; i += NT) {
     const int slot = i < ng ? gsel[i] : 0;
     go[i] = i < ng ? 8 * csel[slot >> 3] + (slot & 7) : -1;
     if (a.gscore) a.gscore[(int64_t)unit * a.kg + i] = i < ng ? key_score(gkeys[slot]) : -INFINITY;
@@ -226,12 +236,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(RouteArgs a) 
 // ---------------------------------------------------------------- fp32 (SIMT)
 // Same routing with fp32 dot products on the vector ALUs (exact-precision mode).
 template <int D>
-__global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a, int G) {
+__global__ __launch_bounds__(kRouteThreadsF32) void route_f32_kernel(RouteArgs a, int G) {
   __shared__ uint32_t ckeys[kMaxChunks];
   __shared__ uint32_t gkeys[kMaxGroupCand];
   __shared__ int csel[64];
   __shared__ int gsel[kMaxGroupCand];
-  __shared__ SelectShared<kRouteThreads> sh;
+  __shared__ SelectShared<kRouteThreadsF32> sh;
 
   const int unit = xcd_unit(blockIdx.x, gridDim.x);
   if (unit >= a.n_units) return;
@@ -256,22 +266,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a, i
     return best;
   };
 
-  for (int c = tid; c < J; c += kRouteThreads) ckeys[c] = score_key(block_max(cs + (int64_t)c * D));
+  for (int c = tid; c < J; c += kRouteThreadsF32) ckeys[c] = score_key(block_max(cs + (int64_t)c * D));
   __syncthreads();
   const int nc = block_topk(ckeys, J, a.kc, csel, sh);
   const int ng_cand = 8 * nc;
-  for (int s = tid; s < ng_cand; s += kRouteThreads)
+  for (int s = tid; s < ng_cand; s += kRouteThreadsF32)
     gkeys[s] = score_key(block_max(gs + (int64_t)(8 * csel[s >> 3] + (s & 7)) * D));
   __syncthreads();
   const int ng = block_topk(gkeys, ng_cand, a.kg, gsel, sh);
 
   int32_t* co = a.cidx + (int64_t)unit * a.kc;
   int32_t* go = a.gidx + (int64_t)unit * a.kg;
-  for (int i = tid; i < a.kc; i += kRouteThreads) {
+  for (int i = tid; i < a.kc; i += kRouteThreadsF32) {
     co[i] = i < nc ? csel[i] : -1;
     if (a.cscore) a.cscore[(int64_t)unit * a.kc + i] = i < nc ? key_score(ckeys[csel[i]]) : -INFINITY;
   }
-  for (int i = tid; i < a.kg; i += kRouteThreads) {
+  for (int i = tid; i < a.kg; i += kRouteThreadsF32) {
     const int slot = i < ng ? gsel[i] : 0;
     go[i] = i < ng ? 8 * csel[slot >> 3] + (slot & 7) : -1;
     if (a.gscore) a.gscore[(int64_t)unit * a.kg + i] = i < ng ? key_score(gkeys[slot]) : -INFINITY;
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(RouteArgs a, i
 
 template <int D, int G>
 void launch_bf16(const RouteArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((route_bf16_kernel<D, G>), dim3(grid), dim3(kRouteThreads), 0, s, a);
+  hipLaunchKernelGGL((route_bf16_kernel<D, G>), dim3(grid), dim3(route_threads<G>()), 0, s, a);
 }
 
 template <int D>
@@ -310,8 +320,8 @@ hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* q_p
     if (d.D == 128) launch_bf16_g<128>(a, d.G, grid, s);
     else launch_bf16_g<64>(a, d.G, grid, s);
   } else {
-    if (d.D == 128) hipLaunchKernelGGL((route_f32_kernel<128>), dim3(grid), dim3(kRouteThreads), 0, s, a, d.G);
-    else hipLaunchKernelGGL((route_f32_kernel<64>), dim3(grid), dim3(kRouteThreads), 0, s, a, d.G);
+    if (d.D == 128) hipLaunchKernelGGL((route_f32_kernel<128>), dim3(grid), dim3(kRouteThreadsF32), 0, s, a, d.G);
+    else hipLaunchKernelGGL((route_f32_kernel<64>), dim3(grid), dim3(kRouteThreadsF32), 0, s, a, d.G);
   }
   return hipGetLastError();
 }
