@@ -53,6 +53,11 @@ def parse():
     p.add_argument("--mark-every", type=int, default=8,
                    help="put per-kernel timing marks on every N-th timed step (default 8)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--cold", action="store_true",
+                   help="write 512 MiB between timed steps (outside the timing) so that no step finds its "
+                        "inputs in the 256 MB MALL; the step time is then the sum of per-step HIP events")
+    p.add_argument("--no-calibration", action="store_true",
+                   help="skip the measurement of the box's achievable copy bandwidth and bf16 GEMM rate")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run a fill and a scale-copy kernel of this size (reference for HBM counters)")
     p.add_argument("--mfma-summary", metavar="COUNTER_CSV",
@@ -108,8 +113,8 @@ def algorithmic_work(w, gidx):
     return {
         "summaries": {"bytes": sum_bytes, "flops": 0.0},
         "route": {"bytes": route_bytes, "flops": route_flops},
-        "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops},
-        "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops},
+        "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops, "gather_bytes": kv_sel},
+        "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops, "gather_bytes": kv_sel},
         "attend_bwd_dkdv": {"bytes": dkdv_bytes, "flops": dkdv_flops},
         # the work list and the partial sums are not part of the method
         "attend_bwd_order": {"bytes": 0.0, "flops": 0.0},
@@ -273,6 +278,51 @@ def make_workload(name):
             "planted_b8_ctx32k": hi.planted_batch}[name]()
 
 
+def achievable_rates():
+    """What this machine reaches on plain library work, for context next to the spec
+    peaks: a device copy of 512 MiB (torch copy_: reads and writes 512 MiB) and a
+    dense 8192^3 bf16 GEMM (torch.matmul, hipBLASLt); best of 10 after warm-up."""
+    import torch
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def best(fn, n=10):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(n):
+            e0, e1 = mk(), mk()
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+    n = 512 << 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    copy_gbs = 2 * n / best(lambda: y.copy_(x)) / 1e9
+    del x, y
+    m = 8192
+    a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16).contiguous()
+    b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16).contiguous()
+    gemm_tfs = 2 * m ** 3 / best(lambda: torch.matmul(a, b)) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tfs, 1),
+            "how": "best of 10: torch copy_ of 512 MiB (bytes read + written); torch.matmul 8192^3 bf16"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 # ------------------------------------------------------------------ CPU oracle leg
 def cpu_baseline(w, q_prev=None, min_seconds=10.0, max_reps=5):
     """The CPU oracle, as it stands, on the same step (all of it), repeated until
@@ -304,6 +354,7 @@ def cpu_baseline(w, q_prev=None, min_seconds=10.0, max_reps=5):
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": w.batch * w.seg_len / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"the full step of this workload (active summaries, route, forward, backward), "
                       f"{len(times)} repetitions, median {t:.2f} s"}
 
@@ -416,12 +467,25 @@ def main_decode(args):
     for i in range(args.warmup):
         step(-1 - i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    if args.cold:
+        # every step's inputs leave the MALL first: 512 MiB written between steps,
+        # outside the step's own events
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        sev = [(mk(), mk()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 255)
+            sev[i][0].record(stream)
+            step(i)
+            sev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = statistics.mean(a.elapsed_time(b) for a, b in sev)
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
     kern_ms = {"decode_route": avg((ev[i][0], ev[i][1]) for i in marked),
                "decode_attend": avg((ev[i][1], ev[i][2]) for i in marked)}
@@ -648,12 +712,25 @@ def main():
     for i in range(args.warmup):
         step(-1 - i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    if args.cold:
+        # every step's inputs leave the MALL first: 512 MiB written between steps,
+        # outside the step's own events
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        sev = [(mk(), mk()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 255)
+            sev[i][0].record(stream)
+            step(i)
+            sev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = statistics.mean(a.elapsed_time(b) for a, b in sev)
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
     kern_ms = {
         "summaries": avg((ev[i][0], ev[i][1]) for i in marked),
@@ -673,7 +750,9 @@ def main():
         tfl = wk["flops"] / (ms * 1e-3) / 1e12
         kernels[k] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "TFLOP/s": round(tfl, 2), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
-        if args.routing == "block":
+        if "gather_bytes" in wk:
+            kernels[k]["gather_GB/s"] = round(wk["gather_bytes"] / (ms * 1e-3) / 1e9, 1)
+        if args.routing == "block" and not args.cold:
             mc = measured_mfma(k, w.name, ms)
             if mc is not None:
                 kernels[k]["mfma_counters"] = mc
@@ -689,8 +768,12 @@ def main():
         ach = wk["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roofline["traffic"] = measured_traffic(dom, w.name) if args.routing == "block" else None
+    roofline["traffic"] = measured_traffic(dom, w.name) if args.routing == "block" and not args.cold else None
     roofline["kernel"] = dom
+    achievable = None if args.no_calibration else achievable_rates()
+    if achievable is not None:
+        roofline["frac_of_achievable"] = round(
+            ach / (achievable["hbm_copy_GBps"] if roofline["bound"] == "hbm" else achievable["bf16_gemm_TFLOPs"]), 4)
 
     tokens = w.batch * w.seg_len
     out = {
@@ -701,8 +784,11 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "t_hist": w.t_hist,
                    "seg_len": w.seg_len, "context": w.t_hist + w.seg_len, "top_chunks": w.top_chunks,
-                   "top_groups": w.top_groups, "routing": args.routing, "parallelism": "none (1 GPU)"},
+                   "top_groups": w.top_groups, "routing": args.routing,
+                   "mall": "flushed before every step (512 MiB written)" if args.cold else "warm",
+                   "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "achievable": achievable,
         "kernels": kernels,
         "kernel_timing": f"HIP events on {len(marked)} of the {args.steps} timed steps; backward kernels "
                          f"timed from their dispatches, the other calls between events on the stream",
