@@ -618,7 +618,48 @@ def main_rollout(args):
         "kernels": kernels,
         "kernel_timing": "HIP events around every call of one extra, marked rollout (summed over the 64 segments)",
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_rollout()
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_rollout(max_reps=3, min_seconds=10.0):
+    """The CPU oracle, as it stands, on a bounded sample of the rollout: the last
+    segment (2,048 tokens routed over 2,016 to 2,047 candidate chunks per block,
+    then attended), with every earlier segment's summaries built untimed."""
+    import numpy as np
+    import hga_inputs as hi
+    from oracle import hga_oracle as ora
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    S, T, Hkv, d = hi.ROLLOUT_SEG, hi.ROLLOUT_TOKENS, 8, 128
+    n_seg = T // S
+    k_all = np.zeros((1, Hkv, T, d), np.float32)
+    v_all = np.zeros((1, Hkv, T, d), np.float32)
+    for s_ in range(n_seg):
+        _, k, v = hi.rollout_segment(s_)
+        k_all[:, :, s_ * S:(s_ + 1) * S] = k
+        v_all[:, :, s_ * S:(s_ + 1) * S] = v
+    q, _, _ = hi.rollout_segment(n_seg - 1)
+    t_hist = (n_seg - 1) * S
+    gs = np.zeros((1, Hkv, T // 8, d), np.float32)
+    cs = np.zeros((1, Hkv, T // 64, d), np.float32)
+    ora.build_summaries(k_all, 0, t_hist, "bf16", gs, cs)            # earlier segments: untimed
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_all) < min_seconds:
+        t0 = time.perf_counter()
+        ora.build_summaries(k_all, t_hist, T, "bf16", gs, cs)
+        _, gidx, _ = ora.route(q, cs, gs, t_hist, S, 16, 64, 4)
+        ora.attend_fwd(q, k_all, v_all, t_hist, gidx, 1.0 / np.sqrt(d), 4)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"the last segment of the rollout (summaries, route over 2,016-2,047 candidate chunks per "
+                      f"block, forward), {len(times)} repetitions, median {t:.2f} s"}
 
 
 # ------------------------------------------------------------------ main
