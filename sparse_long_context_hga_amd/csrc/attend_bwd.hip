@@ -58,8 +58,10 @@ struct BwdArgs {
   int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
   int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
   int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
+  int* first;       // [B, Hkv, S/64, kMaxParts] per item: block of its first round | block of its second << 16
   int* order;       // [4 + 4*B*Hkv*S/64*kMaxParts] number of work items (padded to 16 bytes), then the
-                    // items heaviest first, each {unit * kMaxParts + part, parts of the unit, visits of the unit, 0}
+                    // items heaviest first, each {unit * kMaxParts + part, parts of the unit, visits of the unit,
+                    // the item's entry of `first`}
   float* parts;     // [B, Hkv, S/64, kMaxParts, 2, 64, d] fp32 partials (workspace)
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kg, nb, n_units;
@@ -117,14 +119,28 @@ __device__ __forceinline__ void plan_chunk(const BwdArgs& a, int bh, int cc, con
     const int jj = j0 + l;
     const uint32_t m = jj < a.nb ? mask[jj] : 0u;
     const uint64_t bal = __ballot(m != 0u);
-    if (m != 0u) out[n + __popcll(bal & ((1ull << l) - 1ull))] = jj | (int)(m << 16);
+    const int at = n + __popcll(bal & ((1ull << l) - 1ull));
+    if (m != 0u) {
+      out[at] = jj | (int)(m << 16);
+      // The list again in LDS, from mask[cc] on: at <= jj - cc, so this overwrites only
+      // entries this wave has already read.
+      mask[cc + at] = (uint32_t)jj;
+    }
     n += __popcll(bal);
   }
+  // G rounds (query heads) per attending block (n >= 1: the own block), cut into np
+  // items of about kTargetRounds; item k starts at round k * rounds / np.  The blocks
+  // of every item's first two rounds go into the work list, so that the dK/dV kernel
+  // can start their copies before it has read the visit list.
+  const int rounds = G * n;
+  const int np = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
+  if (l < np) {
+    const int r0 = l * rounds / np, r1 = min(r0 + 1, rounds - 1);
+    a.first[(int64_t)unit * kMaxParts + l] = (int)(mask[cc + r0 / G] | (mask[cc + r1 / G] << 16));
+  }
   if (l == 0) {
-    // G rounds (query heads) per attending block, cut into items of about kTargetRounds
-    const int rounds = G * n;
     a.nvis[unit] = n;
-    a.flags[unit] = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
+    a.flags[unit] = np;
   }
 }
 
@@ -308,14 +324,15 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 // itself; otherwise every item writes an fp32 partial, summed in part order by
 // the finalize kernel (deterministic; no atomics).
 // Inside a work-group: 4 waves; wave w owns keys 32*(w&1) .. +31 of the chunk
-// and rows 32*(w>>1) .. +31 of every round; the next round's Q/dO rows are
-// prefetched into registers while the current round is computed.
+// and rows 32*(w>>1) .. +31 of every round; each round's Q/dO rows are copied
+// into LDS two rounds ahead of their use (three buffer sets).
 
 struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) vector
   static size_t up(size_t x) { return (x + 255) & ~(size_t)255; }
   static size_t flags_off(size_t rows) { return up(rows * 4); }
   static size_t nvis_off(size_t rows, size_t units) { return up(flags_off(rows) + units * 4); }
-  static size_t vis_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
+  static size_t first_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
+  static size_t vis_off(size_t rows, size_t units) { return up(first_off(rows, units) + units * kMaxParts * 4); }
   static size_t order_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
   static size_t part_off(size_t rows, size_t units, size_t nb) {
     return up(order_off(rows, units, nb) + (4 + 4 * units * kMaxParts) * 4);
@@ -356,9 +373,15 @@ __global__ __launch_bounds__(kOrderThreads) void attend_bwd_order_kernel(BwdArgs
   for (int u = tid; u < a.n_units; u += kOrderThreads) {
     const int np_u = a.flags[u], r_u = G * a.nvis[u];
     const int nv_u = a.nvis[u];
-    for (int k = 0; k < np_u; ++k)
-      reinterpret_cast<int4*>(a.order + 4)[atomicAdd(&cnt[size_of(np_u, r_u, k)], 1)] =
-          make_int4(u * kMaxParts + k, np_u, nv_u, 0);
+    int fst[kMaxParts];   // loaded whole, with the counts (entries k >= np_u unused)
+    *reinterpret_cast<int4*>(fst) = reinterpret_cast<const int4*>(a.first)[2 * u];
+    *reinterpret_cast<int4*>(fst + 4) = reinterpret_cast<const int4*>(a.first)[2 * u + 1];
+    static_assert(kMaxParts == 8, "two int4 per unit");
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k)
+      if (k < np_u)
+        reinterpret_cast<int4*>(a.order + 4)[atomicAdd(&cnt[size_of(np_u, r_u, k)], 1)] =
+            make_int4(u * kMaxParts + k, np_u, nv_u, fst[k]);
   }
 }
 
@@ -394,10 +417,12 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   const int item = __builtin_amdgcn_readfirstlane(entry.x);
   const int np = __builtin_amdgcn_readfirstlane(entry.y);
   const int n_visits = __builtin_amdgcn_readfirstlane(entry.z);
+  const uint32_t first = (uint32_t)__builtin_amdgcn_readfirstlane(entry.w);
   if (item < 0) return;
   const int part = item % kMaxParts;
   const int unit = item / kMaxParts;
   if (unit >= a.n_units || part >= np || n_visits > a.nb) return;   // not an item of this selection
+  if ((int)(first & 0xFFFFu) >= a.nb || (int)(first >> 16) >= a.nb) return;
   const int cc = unit % a.nb;                      // active chunk == its own query block
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
@@ -406,46 +431,72 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   // two row halves are summed at the end.
   const int kh = w & 1, rh = w >> 1;
   const int key = 32 * kh + n;                     // this lane's key (operand-B column)
-  const int64_t tok = cglob * kChunk + key;
 
-  bf16x8 kf[KS], vf[KS];
-  {
-    const uint16_t* kp = (const uint16_t*)a.k + ((int64_t)bh * a.t_cap + tok) * D;
-    const uint16_t* vp = (const uint16_t*)a.v + ((int64_t)bh * a.t_cap + tok) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks + 8 * h);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(vp + 16 * ks + 8 * h);
-    }
-  }
-  for (int i = tid; i < n_visits; i += 256) {
-    const int v = a.vis[(int64_t)unit * a.nb + i];
-    vlist[i] = v & 0xFFFF;
-    vmask[i] = (uint32_t)v >> 16;
-  }
-  __syncthreads();
   // This item's slice of the chunk's rounds (round r = attending block r / G, query head r % G).
   const int rounds = G * n_visits;
   const int r_lo = part * rounds / np, r_hi = (part + 1) * rounds / np;
 
-
   const uint16_t* qg = (const uint16_t*)a.q;
   const uint16_t* dg = (const uint16_t*)a.d_o;
-  auto round_row0 = [&](int r) __attribute__((always_inline)) -> int64_t {
-    const int jj = vlist[r / G];
-    const int hh = r % G;
-    return (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)jj * kQBlock;
+  auto round_row0 = [&](int r, int jj) __attribute__((always_inline)) -> int64_t {
+    return (((int64_t)b * a.Hq + kvh * G + r % G) * a.seg_len) + (int64_t)jj * kQBlock;
   };
   // Round: the 64 rows of one query head of one attending block -> Q, dO tiles, LSE, D.
   // Every wave copies the 64 LSE and D values itself (identical data), so that all
   // waves issue the same number of copies per round.
-  auto issue = [&](int i, auto B) __attribute__((always_inline)) {
-    const int64_t row0 = round_row0(r_lo + i);
+  auto issue_rows = [&](int64_t row0, auto B) __attribute__((always_inline)) {
     dma_tile<D, 4>(QB(B), [&](int rr) { return qg + (row0 + rr) * D; });
     dma_tile<D, 4>(OB(B), [&](int rr) { return dg + (row0 + rr) * D; });
     __builtin_amdgcn_global_load_lds((const void*)(a.lse + row0 + l), (lds_void_t*)LB(B), 4, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(a.dvec + row0 + l), (lds_void_t*)RB(B), 4, 0, 0);
   };
+  auto issue = [&](int i, auto B) __attribute__((always_inline)) {
+    issue_rows(round_row0(r_lo + i, vlist[(r_lo + i) / G]), B);
+  };
+  // Everything the first round needs travels at once: the visit list (into
+  // registers), the first round's rows, the chunk's K and V rows (coalesced copies
+  // into buffer set 2, which the third round uses later), then the second round's
+  // rows, whose blocks also come with the work-list entry.
+  int vv[kMaxBlocks / 256];
+#pragma unroll
+  for (int k = 0; k < kMaxBlocks / 256; ++k) {
+    const int i = tid + 256 * k;
+    vv[k] = i < n_visits ? a.vis[(int64_t)unit * a.nb + i] : 0;
+  }
+  issue_rows(round_row0(r_lo, (int)(first & 0xFFFFu)), ic<0>{});
+  {
+    const uint16_t* kp = (const uint16_t*)a.k + ((int64_t)bh * a.t_cap + cglob * kChunk) * D;
+    const uint16_t* vp = (const uint16_t*)a.v + ((int64_t)bh * a.t_cap + cglob * kChunk) * D;
+    dma_tile<D, 4>(q2, [&](int rr) { return kp + (int64_t)rr * D; });
+    dma_tile<D, 4>(do2, [&](int rr) { return vp + (int64_t)rr * D; });
+  }
+  constexpr int L = 2 * dma_per_wave<D, 4>() + 2;   // copies per wave per round
+  const bool two = r_hi - r_lo > 1;
+  if (two) issue_rows(round_row0(r_lo + 1, (int)(first >> 16)), ic<1>{});
+#pragma unroll
+  for (int k = 0; k < kMaxBlocks / 256; ++k) {
+    const int i = tid + 256 * k;
+    if (i < n_visits) {
+      vlist[i] = vv[k] & 0xFFFF;
+      vmask[i] = (uint32_t)vv[k] >> 16;
+    }
+  }
+  // This wave's share of the K/V copies has landed (only the second round's may still
+  // be in flight); after the barrier every wave's share and the visit list are in LDS.
+  if (two) wait_vmcnt<L>(); else wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  tile_barrier();
+  bf16x8 kf[KS], vf[KS];
+  {
+    RowOffsets<D> kvo;   // key row 32 kh + n
+    kvo.init(key, h);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = kvo.read(q2, ks);
+      vf[ks] = kvo.read(do2, ks);
+    }
+  }
+  wait_lgkmcnt0();   // read before the pipeline's first barrier lets set 2 be refilled
 
   const float c2 = a.scale * kLog2e;
   f32x16 dvacc[DT], dkacc[DT];
@@ -517,45 +568,99 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
     }
   };
 
-  pipeline<3, 2 * dma_per_wave<D, 4>() + 2>(r_hi - r_lo, issue, compute);
-  __syncthreads();
+  pipeline<3, L, /*PREISSUED=*/true>(r_hi - r_lo, issue, compute);
 
-  // Sum the two row halves (waves 2,3 -> waves 0,1) through LDS, then write bf16 dK/dV
-  // (chunk done by one item) or this item's fp32 partial.
-  const int64_t orow = (int64_t)bh * a.seg_len + (int64_t)cc * kChunk + key;
-  float* partial = a.parts + ((size_t)unit * kMaxParts + part) * (size_t)(2 * 64 * D);
-  float* red = reinterpret_cast<float*>(kh == 0 ? q0 : q1);   // per key half: DT*16*64 floats
+  // Sum the two row halves (waves 2,3 -> waves 0,1) through LDS; waves 0,1 then put
+  // the sums, row-major by key, in their own halves' buffers, and all four waves
+  // store them with whole-row (coalesced) writes: bf16 dK/dV when one item does the
+  // chunk, this item's fp32 partial otherwise.  The halves sit in the stage buffers
+  // (dV in q0/q1, dK in do0/do1, by key half); no copies are in flight after the last
+  // round and every wave's reads of them have been consumed, so LDS-only barriers
+  // suffice, and the global stores are never waited for.
+  float* red_v = reinterpret_cast<float*>(kh == 0 ? q0 : q1);    // per key half: DT*16*64 floats
+  float* red_k = reinterpret_cast<float*>(kh == 0 ? do0 : do1);
   static_assert(sizeof(q0) >= DT * 16 * 64 * sizeof(float), "reduction buffer");
+  constexpr int C32 = D / 4, C16 = D / 8;   // 16-byte chunks per fp32 / bf16 row
+  const bool split = np > 1;
+  tile_barrier();
+  // The halves travel as 16-byte pieces, lane-major: piece (dt, q) of lane l holds
+  // accumulator elements 4q .. 4q+3 of tile dt.
+  auto piece = [&](float* red, int dt, int q) __attribute__((always_inline)) -> float4* {
+    return reinterpret_cast<float4*>(red) + (dt * 4 + q) * 64 + l;
+  };
+  if (rh == 1) {
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    if (rh == 1) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int q = 0; q < 4; ++q) {
+        *piece(red_v, dt, q) = make_float4(dvacc[dt][4 * q], dvacc[dt][4 * q + 1], dvacc[dt][4 * q + 2], dvacc[dt][4 * q + 3]);
+        *piece(red_k, dt, q) = make_float4(dkacc[dt][4 * q], dkacc[dt][4 * q + 1], dkacc[dt][4 * q + 2], dkacc[dt][4 * q + 3]);
+      }
+  }
+  wait_lgkmcnt0();
+  tile_barrier();
+  if (rh == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red[(dt * 16 + e) * 64 + l] = which ? dkacc[dt][e] : dvacc[dt][e];
-    }
-    __syncthreads();
-    if (rh == 0) {
-      const float sc = which ? a.scale : 1.f;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 xv = *piece(red_v, dt, q), xk = *piece(red_k, dt, q);
+        dvacc[dt][4 * q] += xv.x; dvacc[dt][4 * q + 1] += xv.y; dvacc[dt][4 * q + 2] += xv.z; dvacc[dt][4 * q + 3] += xv.w;
+        dkacc[dt][4 * q] += xk.x; dkacc[dt][4 * q + 1] += xk.y; dkacc[dt][4 * q + 2] += xk.z; dkacc[dt][4 * q + 3] += xk.w;
+      }
+    // Row n (key 32 kh + n) of this half; the lane holds columns 32 dt + 8 g + 4 h .. +3.
+    // Chunks are XOR-swizzled by row so that the 32 rows' writes spread over the banks.
+    if (split) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float x[4];
+          const int c = (8 * dt + 2 * g + h) ^ (n & (C32 - 1));
+          *reinterpret_cast<float4*>(red_v + n * D + 4 * c) =
+              make_float4(dvacc[dt][4 * g], dvacc[dt][4 * g + 1], dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]);
+          *reinterpret_cast<float4*>(red_k + n * D + 4 * c) =
+              make_float4(dkacc[dt][4 * g], dkacc[dt][4 * g + 1], dkacc[dt][4 * g + 2], dkacc[dt][4 * g + 3]);
+        }
+    } else {
+      uint16_t* ov = reinterpret_cast<uint16_t*>(red_v);
+      uint16_t* ok = reinterpret_cast<uint16_t*>(red_k);
+      const float sc = a.scale;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            x[i] = (which ? dkacc[dt][4 * g + i] : dvacc[dt][4 * g + i]) + red[(dt * 16 + 4 * g + i) * 64 + l];
-          const int col = 32 * dt + 8 * g + 4 * h;
-          if (np > 1) {
-            *reinterpret_cast<float4*>(partial + (size_t)which * 64 * D + (size_t)key * D + col) =
-                make_float4(x[0], x[1], x[2], x[3]);
-          } else {
-            uint16_t* out = (uint16_t*)(which ? a.dk : a.dv) + orow * D;
-            *reinterpret_cast<uint2*>(out + col) = f32x4_to_bf16x4_bits(x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc);
-          }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int at = n * D + 8 * ((4 * dt + g) ^ (n & (C16 - 1))) + 4 * h;
+          *reinterpret_cast<uint2*>(ov + at) =
+              f32x4_to_bf16x4_bits(dvacc[dt][4 * g], dvacc[dt][4 * g + 1], dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]);
+          *reinterpret_cast<uint2*>(ok + at) = f32x4_to_bf16x4_bits(
+              dkacc[dt][4 * g] * sc, dkacc[dt][4 * g + 1] * sc, dkacc[dt][4 * g + 2] * sc, dkacc[dt][4 * g + 3] * sc);
         }
     }
-    __syncthreads();
+  }
+  wait_lgkmcnt0();
+  tile_barrier();
+  // Wave w stores the tile of (which = w >> 1: 0 dV, 1 dK; key half w & 1).
+  const int which = w >> 1, half = w & 1;
+  const char* src = reinterpret_cast<const char*>(which ? (half ? do1 : do0) : (half ? q1 : q0));
+  if (split) {
+    float* dst = a.parts + ((size_t)unit * kMaxParts + part) * (size_t)(2 * 64 * D) + (size_t)which * 64 * D +
+                 (size_t)(32 * half) * D;
+    constexpr int RPI = 64 / C32;   // rows per instruction
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int row = RPI * it + l / C32, c = l % C32;
+      const float4 x = *reinterpret_cast<const float4*>(src + 16 * (row * C32 + (c ^ (row & (C32 - 1)))));
+      *reinterpret_cast<float4*>(dst + (size_t)row * D + 4 * c) = x;
+    }
+  } else {
+    uint16_t* dst = (uint16_t*)(which ? a.dk : a.dv) + ((int64_t)bh * a.seg_len + (int64_t)cc * kChunk + 32 * half) * D;
+    constexpr int RPI = 64 / C16;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int row = RPI * it + l / C16, c = l % C16;
+      const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * (row * C16 + (c ^ (row & (C16 - 1)))));
+      *reinterpret_cast<uint4*>(dst + (int64_t)row * D + 8 * c) = x;
+    }
   }
 }
 
@@ -748,6 +853,7 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
     const size_t units = (size_t)d.B * d.Hkv * (size_t)d.nb;
     a.flags = (int*)((char*)workspace + DkdvLayout::flags_off(rows));
     a.nvis = (int*)((char*)workspace + DkdvLayout::nvis_off(rows, units));
+    a.first = (int*)((char*)workspace + DkdvLayout::first_off(rows, units));
     a.vis = (int*)((char*)workspace + DkdvLayout::vis_off(rows, units));
     a.order = (int*)((char*)workspace + DkdvLayout::order_off(rows, units, (size_t)d.nb));
     a.parts = (float*)((char*)workspace + DkdvLayout::part_off(rows, units, (size_t)d.nb));

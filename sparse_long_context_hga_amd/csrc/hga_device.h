@@ -341,6 +341,9 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const RowSrc& row_src) 
 // Wait until every global->LDS copy issued by this wave has landed.
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS accesses have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // s_waitcnt vmcnt(N) for a compile-time N (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -375,19 +378,23 @@ __device__ __forceinline__ void tile_barrier() {
 
 // Software pipeline over n tiles with NBUF buffer sets and NBUF-1 tiles in flight.
 // issue(t, ic<B>) starts the asynchronous copies of tile t into buffer set B;
+// with PREISSUED the caller has already issued tiles 0 .. NBUF-2 (those below n)
+// into sets 0 .. NBUF-2, each wave with the same L copies per tile;
 // compute(t, ic<B>) consumes buffer set B.  Every wave issues exactly L copies
 // per tile (or none at all), so "tile t has landed" is vmcnt(L * tiles issued
 // after t).  Buffer sets must be distinct LDS arrays chosen at compile time: the
 // compiler then knows that reading one set never aliases copies into another
 // and adds no wait of its own.  One barrier per tile: before tile t+NBUF-1 is
 // issued into the set of tile t-1, every wave has finished computing tile t-1.
-template <int NBUF, int L, typename Issue, typename Compute>
+template <int NBUF, int L, bool PREISSUED = false, typename Issue, typename Compute>
 __device__ __forceinline__ void pipeline(int n, Issue&& issue, Compute&& compute) {
   static_assert(NBUF >= 2 && NBUF <= 4, "2 to 4 buffer sets");
   constexpr int P = NBUF - 1;
-  static_for<0, P>([&](auto B) {
-    if (B() < n) issue(B(), B);
-  });
+  if constexpr (!PREISSUED) {
+    static_for<0, P>([&](auto B) {
+      if (B() < n) issue(B(), B);
+    });
+  }
   for (int t0 = 0; t0 < n; t0 += NBUF) {
     static_for<0, NBUF>([&](auto B) {
       const int t = t0 + B();
