@@ -175,9 +175,17 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n = l & 31;
   const int hh = (item % (G / HPW)) * HPW + (w >> 1);
   const int pos = 32 * (w & 1) + n;
-  const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
+  // First row of this wave's 32 (wave-uniform) and this lane's row.
+  const int64_t qrow0 = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + 32 * (w & 1);
+  const int64_t qrow = qrow0 + n;
   const uint16_t* kb = (const uint16_t*)a.k + (int64_t)bh * a.t_cap * D;
   const uint16_t* vb = (const uint16_t*)a.v + (int64_t)bh * a.t_cap * D;
+  // 32-row LDS region of wave wv in the two tile buffer sets (for dQ after the last
+  // tile).
+  auto row_region = [&](int wv) __attribute__((always_inline)) -> uint16_t* {
+    uint16_t* base = (wv >> 1) == 0 ? k0 : (wv >> 1) == 1 ? v0 : (wv >> 1) == 2 ? k1 : v1;
+    return base + (wv & 1) * 32 * D;
+  };
 
   // The selection inverse of active chunk j: its group ids are loaded first (their
   // latency overlaps the loads below), used after the group list is in LDS.
@@ -303,16 +311,13 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 
   pipeline<kStages, 2 * BPW>(n_tiles, issue, compute);
 
-  uint16_t* qo = (uint16_t*)a.dq + qrow * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int col = 32 * dt + 8 * g + 4 * h;
-      *reinterpret_cast<uint2*>(qo + col) = f32x4_to_bf16x4_bits(
-          dqacc[dt][4 * g] * a.scale, dqacc[dt][4 * g + 1] * a.scale, dqacc[dt][4 * g + 2] * a.scale,
-          dqacc[dt][4 * g + 3] * a.scale);
-    }
+  // dQ leaves through this wave's 32-row LDS region as whole rows; the barrier keeps
+  // every region free until all waves have finished their last tile.
+  tile_barrier();
+  store_rows32<D>(row_region(w), (uint16_t*)a.dq + qrow0 * D, [&](int dt, int g) __attribute__((always_inline)) {
+    return f32x4_to_bf16x4_bits(dqacc[dt][4 * g] * a.scale, dqacc[dt][4 * g + 1] * a.scale,
+                                dqacc[dt][4 * g + 2] * a.scale, dqacc[dt][4 * g + 3] * a.scale);
+  });
 }
 
 // ---------------------------------------------------------------- dK/dV (bf16)

@@ -73,10 +73,18 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
   const int hh = (item % (G / HPW)) * HPW + (w >> 1);   // query head within the KV group
   const int pos = 32 * (w & 1) + n;       // this lane's query position in the block
-  const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + pos;
+  // First row of this wave's 32 (wave-uniform) and this lane's row.
+  const int64_t qrow0 = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + 32 * (w & 1);
+  const int64_t qrow = qrow0 + n;
 
   const char* kb = (const char*)a.k + (int64_t)bh * a.t_cap * D * 2;
   const char* vb = (const char*)a.v + (int64_t)bh * a.t_cap * D * 2;
+  // 32-row LDS region of wave wv in the first two tile buffer sets (for O after the
+  // last tile).
+  auto row_region = [&](int wv) __attribute__((always_inline)) -> uint16_t* {
+    uint16_t* base = (wv >> 1) == 0 ? k0 : (wv >> 1) == 1 ? v0 : (wv >> 1) == 2 ? k1 : v1;
+    return base + (wv & 1) * 32 * D;
+  };
 
   bf16x8 qf[KS];
   {
@@ -217,17 +225,15 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
   pipeline<kStagesHere, 2 * BPW>(n_tiles, issue, compute);
 
   // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
+  // O leaves through this wave's 32-row LDS region as whole rows; the barrier keeps
+  // every region free until all waves have finished their last tile.
   const float ltot = half_sum(lsum);
   const float inv = 1.f / ltot;
-  uint16_t* op = (uint16_t*)a.o + qrow * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int col = 32 * dt + 8 * g + 4 * h;
-      *reinterpret_cast<uint2*>(op + col) = f32x4_to_bf16x4_bits(
-          oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-    }
+  tile_barrier();
+  store_rows32<D>(row_region(w), (uint16_t*)a.o + qrow0 * D, [&](int dt, int g) __attribute__((always_inline)) {
+    return f32x4_to_bf16x4_bits(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                                oacc[dt][4 * g + 3] * inv);
+  });
   if (h == 0) a.lse[qrow] = (m2 + log2f(ltot)) * kLn2;
 }
 

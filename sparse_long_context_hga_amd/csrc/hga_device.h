@@ -338,6 +338,35 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const RowSrc& row_src) 
   }
 }
 
+// ------------------------------------------------------ a wave's 32 query rows
+// A wave's 32 query rows (lane n = l & 31 holds row n in the MFMA output layout, the
+// lane halves h the column halves) are contiguous in the row-major [.., rows, D]
+// tensors.  Stored straight from that layout, every store instruction touches 32
+// rows; through a private 32-row LDS region (16-byte chunks XOR-swizzled by row)
+// every instruction writes whole rows instead.
+
+// Store of a wave's 32 output rows dst .. dst + 31 (D bf16 each) through a 32-row
+// region: val(dt, g) gives the lane's four bf16 values of its row at columns
+// 32 dt + 8 g + 4 h .. +3 (the MFMA output layout) as a uint2.  The region must not
+// be in use by another wave.
+template <int D, typename Val>
+__device__ __forceinline__ void store_rows32(uint16_t* region, uint16_t* dst, Val&& val) {
+  constexpr int CH = D / 8, RPI = 64 / CH;   // chunks per row, rows per store
+  const int l = threadIdx.x & 63, n = l & 31, h = l >> 5;
+  const int f = swz_f<D>(n);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint2*>(region + n * D + 8 * ((4 * dt + g) ^ f) + 4 * h) = val(dt, g);
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = RPI * it + l / CH, c = l % CH;
+    const uint4 x = *reinterpret_cast<const uint4*>(region + r * D + 8 * (c ^ swz_f<D>(r)));
+    *reinterpret_cast<uint4*>(dst + (int64_t)r * D + 8 * c) = x;
+  }
+}
+
 // Wait until every global->LDS copy issued by this wave has landed.
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
