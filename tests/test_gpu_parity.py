@@ -38,6 +38,11 @@ CASES = {
                                            t_hist=128, seg_len=256, top_chunks=64, top_groups=512),
     "bf16_single_block": dict(seed=9, batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, t_hist=1024,
                               seg_len=64, top_chunks=7, top_groups=50, t_cap=2048),
+    # every block selects every earlier chunk and group: the segment's first chunks are
+    # attended by up to 16 blocks x 8 heads = 128 rounds, cut into the maximum of 8
+    # dK/dV items each (items of 16 rounds, partial sums of 8 parts)
+    "bf16_g8_full_coverage": dict(seed=13, batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128, t_hist=0,
+                                  seg_len=1024, top_chunks=16, top_groups=128),
     "f32_g1_d64": dict(seed=10, batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, t_hist=320,
                        seg_len=256, top_chunks=3, top_groups=19, dtype="f32"),
     "f32_g4_d128": dict(seed=11, batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, t_hist=256,
