@@ -15,7 +15,7 @@
 //    LSE; writes dQ and D = rowsum(dO * O) (workspace) for the dK/dV kernel.  It
 //    also inverts the selection for the active chunk of its own block -- the
 //    ascending list of query blocks that attend the chunk -- and cuts the
-//    chunk's work into 1..8 items of about 12 "rounds" (one round = the 64 rows
+//    chunk's work into 1..8 items of about 12 or 16 "rounds" (one round = the 64 rows
 //    of one query head of one attending block);
 //  * order (one work-group): lists all items by size, largest first, so that
 //    the dK/dV grid starts with the heaviest items;
@@ -39,7 +39,14 @@ namespace {
 constexpr int kStages = 2;   // K/V tile buffer sets of the dQ kernel
 
 constexpr int kMaxBlocks = 1024;   // query blocks per segment supported by the dkdv kernel
-constexpr int kTargetRounds = 12;  // dK/dV work is cut into items of about this many rounds
+// dK/dV work is cut into items of about this many rounds.  Longer items mean fewer
+// items (each pays a start-up and an epilogue of a few microseconds) but a longer
+// slowest item.  The segment's own blocks attend its chunks more often when the
+// history is short, so the chunks carry more rounds and longer items pay: measured
+// on the 32-query / 8-KV-head layer, 12 is fastest with 14,336 history tokens per
+// 2,048-token segment and 16 with 2,048 (8 to 32 tried).
+constexpr int kTargetRoundsLongHistory = 12;
+constexpr int kTargetRoundsShortHistory = 16;
 constexpr int kMaxParts = 8;       // at most this many items per active chunk
 constexpr int kBuckets = 64;       // work-list size classes (rounds per work item, capped)
 
@@ -65,6 +72,7 @@ struct BwdArgs {
   float* parts;     // [B, Hkv, S/64, kMaxParts, 2, 64, d] fp32 partials (workspace)
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kg, nb, n_units;
+  int target_rounds;   // dK/dV rounds per work item (see kTargetRounds*)
   float scale;
 };
 
@@ -129,11 +137,11 @@ __device__ __forceinline__ void plan_chunk(const BwdArgs& a, int bh, int cc, con
     n += __popcll(bal);
   }
   // G rounds (query heads) per attending block (n >= 1: the own block), cut into np
-  // items of about kTargetRounds; item k starts at round k * rounds / np.  The blocks
+  // items of about a.target_rounds; item k starts at round k * rounds / np.  The blocks
   // of every item's first two rounds go into the work list, so that the dK/dV kernel
   // can start their copies before it has read the visit list.
   const int rounds = G * n;
-  const int np = min(kMaxParts, (rounds + kTargetRounds - 1) / kTargetRounds);
+  const int np = min(kMaxParts, (rounds + a.target_rounds - 1) / a.target_rounds);
   if (l < np) {
     const int r0 = l * rounds / np, r1 = min(r0 + 1, rounds - 1);
     a.first[(int64_t)unit * kMaxParts + l] = (int)(mask[cc + r0 / G] | (mask[cc + r1 / G] << 16));
@@ -325,7 +333,7 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 // own block (causally) and by every later block whose selection holds one of its
 // groups; each such block contributes G "rounds" (64 rows of one query head).
 // The dQ kernel cuts a chunk's rounds into np = min(kMaxParts, ceil(rounds /
-// kTargetRounds)) contiguous slices.  With np = 1 the item writes bf16 dK/dV
+// target_rounds)) contiguous slices.  With np = 1 the item writes bf16 dK/dV
 // itself; otherwise every item writes an fp32 partial, summed in part order by
 // the finalize kernel (deterministic; no atomics).
 // Inside a work-group: 4 waves; wave w owns keys 32*(w&1) .. +31 of the chunk
@@ -866,6 +874,7 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kg = d.kg; a.nb = d.nb; a.n_units = d.B * d.Hkv * d.nb;
   a.scale = d.scale;
+  a.target_rounds = d.t_hist >= 3 * d.seg_len ? kTargetRoundsLongHistory : kTargetRoundsShortHistory;
   const int grid = xcd_grid(a.n_units);
   if (bf16) {
     if (d.D == 128) launch_bf16_g<128>(a, d.G, run);
