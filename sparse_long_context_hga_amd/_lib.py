@@ -41,10 +41,50 @@ class HgaShape(ctypes.Structure):
     ]
 
 
+_DTYPE_CODES = {"bf16": HGA_BF16, "f32": HGA_F32}
+
+
 def make_shape(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, top_chunks: int,
                top_groups: int, dtype: str = "bf16", softmax_scale: float = 0.0) -> HgaShape:
+    """The hga_shape of a call; dtype is "bf16" or "f32" (anything else raises)."""
+    if dtype not in _DTYPE_CODES:
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
     return HgaShape(batch, n_q_heads, n_kv_heads, head_dim, 64, 8, 64, top_chunks, top_groups,
-                    HGA_BF16 if dtype == "bf16" else HGA_F32, softmax_scale)
+                    _DTYPE_CODES[dtype], softmax_scale)
+
+
+def _float_dtype(shape: HgaShape) -> torch.dtype:
+    return torch.bfloat16 if shape.dtype == HGA_BF16 else torch.float32
+
+
+def _need(fn: str, name: str, t: Optional[torch.Tensor], dtype: torch.dtype, numel: int, device,
+          optional: bool = False) -> None:
+    """Host-side check of one tensor argument before its pointer crosses the C ABI:
+    the library trusts pointers, so a tensor of the wrong dtype, layout, device or
+    size would become an out-of-bounds device access instead of an error."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{fn}: {name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{fn}: {name} is on {t.device}, expected {device}")
+    if t.numel() != numel:
+        raise ValueError(f"{fn}: {name} has {t.numel()} elements, expected {numel}")
+
+
+def _dev_of(*ts) -> torch.device:
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            if t.device.type != "cuda":
+                raise ValueError(f"tensors must be on a ROCm device, got {t.device}")
+            return t.device
+    raise ValueError("no tensor arguments")
 
 
 _lib = None
@@ -104,18 +144,59 @@ def _check(fn: str, st: int):
 
 
 # ---------------------------------------------------------------- thin wrappers
+# Each wrapper checks its tensors on the host (dtype, contiguity, device, element
+# count implied by the shape and sizes) and then passes their device pointers.
+_I32, _F32, _U8 = torch.int32, torch.float32, torch.uint8
+
+
+def _dims(shape: HgaShape):
+    return shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+
+
+def _cache_checks(fn, shape, dev, t_cap, k_cache, v_cache, group_sum, chunk_sum, optional_sums=False):
+    """K/V cache [B,Hkv,t_cap,d] and summary tables [B,Hkv,t_cap/8,d], [B,Hkv,t_cap/64,d]
+    (k_cache / v_cache skipped when passed as False)."""
+    B, _, Hkv, d = _dims(shape)
+    ft = _float_dtype(shape)
+    if k_cache is not False:
+        _need(fn, "k_cache", k_cache, ft, B * Hkv * t_cap * d, dev)
+    if v_cache is not False:
+        _need(fn, "v_cache", v_cache, ft, B * Hkv * t_cap * d, dev)
+    _need(fn, "group_sum", group_sum, ft, B * Hkv * (t_cap // 8) * d, dev, optional=optional_sums)
+    _need(fn, "chunk_sum", chunk_sum, ft, B * Hkv * (t_cap // 64) * d, dev, optional=optional_sums)
+
+
 def hga_build_summaries(shape: HgaShape, k_cache: torch.Tensor, t_cap: int, t_begin: int, t_end: int,
                         group_sum: torch.Tensor, chunk_sum: torch.Tensor, stream=None) -> None:
-    _check("hga_build_summaries", lib().hga_build_summaries(
+    fn = "hga_build_summaries"
+    dev = _dev_of(k_cache, group_sum, chunk_sum)
+    _cache_checks(fn, shape, dev, t_cap, k_cache, False, group_sum, chunk_sum)
+    _check(fn, lib().hga_build_summaries(
         ctypes.byref(shape), _ptr(k_cache), t_cap, t_begin, t_end, _ptr(group_sum), _ptr(chunk_sum),
         _stream(stream)))
+
+
+def _route_checks(fn, shape, dev, q, chunk_sum, group_sum, t_cap, seg_len, chunk_idx, group_idx, chunk_score,
+                  group_score):
+    B, Hq, Hkv, d = _dims(shape)
+    nb = seg_len // 64
+    _need(fn, "q", q, _float_dtype(shape), B * Hq * seg_len * d, dev)
+    _cache_checks(fn, shape, dev, t_cap, False, False, group_sum, chunk_sum)
+    _need(fn, "chunk_idx", chunk_idx, _I32, B * Hkv * nb * shape.top_chunks, dev, optional=shape.top_chunks == 0)
+    _need(fn, "group_idx", group_idx, _I32, B * Hkv * nb * shape.top_groups, dev, optional=shape.top_groups == 0)
+    _need(fn, "chunk_score", chunk_score, _F32, B * Hkv * nb * shape.top_chunks, dev, optional=True)
+    _need(fn, "group_score", group_score, _F32, B * Hkv * nb * shape.top_groups, dev, optional=True)
 
 
 def hga_route(shape: HgaShape, q: torch.Tensor, chunk_sum: torch.Tensor, group_sum: torch.Tensor,
               t_cap: int, t_hist: int, seg_len: int, chunk_idx: torch.Tensor, group_idx: torch.Tensor,
               chunk_score: Optional[torch.Tensor] = None, group_score: Optional[torch.Tensor] = None,
               stream=None) -> None:
-    _check("hga_route", lib().hga_route(
+    fn = "hga_route"
+    dev = _dev_of(q, chunk_sum, group_sum)
+    _route_checks(fn, shape, dev, q, chunk_sum, group_sum, t_cap, seg_len, chunk_idx, group_idx, chunk_score,
+                  group_score)
+    _check(fn, lib().hga_route(
         ctypes.byref(shape), _ptr(q), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist, seg_len,
         _ptr(chunk_idx), _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _stream(stream)))
 
@@ -124,15 +205,36 @@ def hga_route_causal(shape: HgaShape, q: torch.Tensor, q_prev: Optional[torch.Te
                      group_sum: torch.Tensor, t_cap: int, t_hist: int, seg_len: int, chunk_idx: torch.Tensor,
                      group_idx: torch.Tensor, chunk_score: Optional[torch.Tensor] = None,
                      group_score: Optional[torch.Tensor] = None, stream=None) -> None:
-    _check("hga_route_causal", lib().hga_route_causal(
+    fn = "hga_route_causal"
+    dev = _dev_of(q, chunk_sum, group_sum)
+    _route_checks(fn, shape, dev, q, chunk_sum, group_sum, t_cap, seg_len, chunk_idx, group_idx, chunk_score,
+                  group_score)
+    B, Hq, _, d = _dims(shape)
+    _need(fn, "q_prev", q_prev, _float_dtype(shape), B * Hq * 64 * d, dev, optional=t_hist == 0)
+    _check(fn, lib().hga_route_causal(
         ctypes.byref(shape), _ptr(q), _ptr(q_prev), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist, seg_len,
         _ptr(chunk_idx), _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _stream(stream)))
+
+
+def _attend_checks(fn, shape, dev, q, k_cache, v_cache, t_cap, seg_len, group_idx, o, lse):
+    B, Hq, Hkv, d = _dims(shape)
+    ft = _float_dtype(shape)
+    _need(fn, "q", q, ft, B * Hq * seg_len * d, dev)
+    _need(fn, "k_cache", k_cache, ft, B * Hkv * t_cap * d, dev)
+    _need(fn, "v_cache", v_cache, ft, B * Hkv * t_cap * d, dev)
+    _need(fn, "group_idx", group_idx, _I32, B * Hkv * (seg_len // 64) * shape.top_groups, dev,
+          optional=shape.top_groups == 0)
+    _need(fn, "o", o, ft, B * Hq * seg_len * d, dev)
+    _need(fn, "lse", lse, _F32, B * Hq * seg_len, dev)
 
 
 def hga_attend_fwd(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    t_cap: int, t_hist: int, seg_len: int, group_idx: torch.Tensor, o: torch.Tensor,
                    lse: torch.Tensor, stream=None) -> None:
-    _check("hga_attend_fwd", lib().hga_attend_fwd(
+    fn = "hga_attend_fwd"
+    dev = _dev_of(q, k_cache, v_cache)
+    _attend_checks(fn, shape, dev, q, k_cache, v_cache, t_cap, seg_len, group_idx, o, lse)
+    _check(fn, lib().hga_attend_fwd(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, t_hist, seg_len,
         _ptr(group_idx), _ptr(o), _ptr(lse), _stream(stream)))
 
@@ -141,13 +243,30 @@ def hga_attend_bwd_workspace_size(shape: HgaShape, t_hist: int, seg_len: int) ->
     return int(lib().hga_attend_bwd_workspace_size(ctypes.byref(shape), t_hist, seg_len))
 
 
+def _bwd_checks(fn, shape, dev, q, k_cache, v_cache, o, lse, d_o, t_cap, seg_len, group_idx, dq, dk_active,
+                dv_active, workspace):
+    B, Hq, Hkv, d = _dims(shape)
+    ft = _float_dtype(shape)
+    _attend_checks(fn, shape, dev, q, k_cache, v_cache, t_cap, seg_len, group_idx, o, lse)
+    _need(fn, "d_o", d_o, ft, B * Hq * seg_len * d, dev)
+    _need(fn, "dq", dq, ft, B * Hq * seg_len * d, dev)
+    _need(fn, "dk_active", dk_active, ft, B * Hkv * seg_len * d, dev)
+    _need(fn, "dv_active", dv_active, ft, B * Hkv * seg_len * d, dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"{fn}: workspace must be a contiguous tensor on {dev}")
+
+
 def hga_attend_bwd(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_cap: int, t_hist: int,
                    seg_len: int, group_idx, dq, dk_active, dv_active, workspace: torch.Tensor,
                    stream=None) -> None:
-    _check("hga_attend_bwd", lib().hga_attend_bwd(
+    fn = "hga_attend_bwd"
+    dev = _dev_of(q, k_cache, v_cache)
+    _bwd_checks(fn, shape, dev, q, k_cache, v_cache, o, lse, d_o, t_cap, seg_len, group_idx, dq, dk_active,
+                dv_active, workspace)
+    _check(fn, lib().hga_attend_bwd(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(d_o),
         t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(dq), _ptr(dk_active), _ptr(dv_active),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 HGA_BWD_KERNELS = 4
@@ -158,17 +277,21 @@ def hga_attend_bwd_timed(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_ca
                          events, stream=None) -> None:
     """hga_attend_bwd with torch.cuda.Event pairs recorded around each of its kernels
     (events[2i], events[2i+1] for kernel i; None entries are skipped)."""
+    fn = "hga_attend_bwd_timed"
     if len(events) != 2 * HGA_BWD_KERNELS:
         raise ValueError(f"need {2 * HGA_BWD_KERNELS} events, got {len(events)}")
+    dev = _dev_of(q, k_cache, v_cache)
+    _bwd_checks(fn, shape, dev, q, k_cache, v_cache, o, lse, d_o, t_cap, seg_len, group_idx, dq, dk_active,
+                dv_active, workspace)
     for e in events:
         if e is not None and not e.cuda_event:
             e.record(stream if stream is not None else torch.cuda.current_stream())  # creates it
     handles = (ctypes.c_void_p * (2 * HGA_BWD_KERNELS))(
         *[None if e is None else ctypes.c_void_p(e.cuda_event) for e in events])
-    _check("hga_attend_bwd_timed", lib().hga_attend_bwd_timed(
+    _check(fn, lib().hga_attend_bwd_timed(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(d_o),
         t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(dq), _ptr(dk_active), _ptr(dv_active),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), handles, _stream(stream)))
+        _ptr(workspace), _nbytes(workspace), handles, _stream(stream)))
 
 
 def hga_decode_workspace_size(shape: HgaShape, t_cap: int) -> int:
@@ -179,11 +302,29 @@ def _nbytes(t: torch.Tensor) -> int:
     return t.numel() * t.element_size()
 
 
+def _decode_checks(fn, shape, dev, q, t_cap, pos, chunk_idx, group_idx, workspace, chunk_optional=False):
+    B, Hq, Hkv, d = _dims(shape)
+    _need(fn, "q", q, _float_dtype(shape), B * Hq * d, dev)
+    _need(fn, "pos", pos, _I32, B, dev)
+    _need(fn, "chunk_idx", chunk_idx, _I32, B * Hkv * shape.top_chunks, dev,
+          optional=chunk_optional or shape.top_chunks == 0)
+    _need(fn, "group_idx", group_idx, _I32, B * Hkv * shape.top_groups, dev, optional=shape.top_groups == 0)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"{fn}: workspace must be a contiguous tensor on {dev}")
+
+
 def hga_decode_step(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     chunk_sum: torch.Tensor, group_sum: torch.Tensor, t_cap: int, pos: torch.Tensor,
                     chunk_idx: Optional[torch.Tensor], group_idx: torch.Tensor, o: torch.Tensor,
                     lse: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
-    _check("hga_decode_step", lib().hga_decode_step(
+    fn = "hga_decode_step"
+    dev = _dev_of(q, k_cache, v_cache)
+    B, Hq, _, d = _dims(shape)
+    _decode_checks(fn, shape, dev, q, t_cap, pos, chunk_idx, group_idx, workspace, chunk_optional=True)
+    _cache_checks(fn, shape, dev, t_cap, k_cache, v_cache, group_sum, chunk_sum)
+    _need(fn, "o", o, _float_dtype(shape), B * Hq * d, dev)
+    _need(fn, "lse", lse, _F32, B * Hq, dev)
+    _check(fn, lib().hga_decode_step(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap,
         _ptr(pos), _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
@@ -193,7 +334,14 @@ def hga_decode_route(shape: HgaShape, q: torch.Tensor, chunk_sum: torch.Tensor, 
                      t_cap: int, pos: torch.Tensor, chunk_idx: torch.Tensor, group_idx: torch.Tensor,
                      workspace: torch.Tensor, chunk_score: Optional[torch.Tensor] = None,
                      group_score: Optional[torch.Tensor] = None, stream=None) -> None:
-    _check("hga_decode_route", lib().hga_decode_route(
+    fn = "hga_decode_route"
+    dev = _dev_of(q, chunk_sum, group_sum)
+    B, _, Hkv, d = _dims(shape)
+    _decode_checks(fn, shape, dev, q, t_cap, pos, chunk_idx, group_idx, workspace)
+    _cache_checks(fn, shape, dev, t_cap, False, False, group_sum, chunk_sum)
+    _need(fn, "chunk_score", chunk_score, _F32, B * Hkv * shape.top_chunks, dev, optional=True)
+    _need(fn, "group_score", group_score, _F32, B * Hkv * shape.top_groups, dev, optional=True)
+    _check(fn, lib().hga_decode_route(
         ctypes.byref(shape), _ptr(q), _ptr(chunk_sum), _ptr(group_sum), t_cap, _ptr(pos), _ptr(chunk_idx),
         _ptr(group_idx), _ptr(chunk_score), _ptr(group_score), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
@@ -203,7 +351,14 @@ def hga_decode_attend(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v
                       t_cap: int, pos: torch.Tensor, group_idx: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
                       workspace: torch.Tensor, group_sum: Optional[torch.Tensor] = None,
                       chunk_sum: Optional[torch.Tensor] = None, stream=None) -> None:
-    _check("hga_decode_attend", lib().hga_decode_attend(
+    fn = "hga_decode_attend"
+    dev = _dev_of(q, k_cache, v_cache)
+    B, Hq, _, d = _dims(shape)
+    _decode_checks(fn, shape, dev, q, t_cap, pos, None, group_idx, workspace, chunk_optional=True)
+    _cache_checks(fn, shape, dev, t_cap, k_cache, v_cache, group_sum, chunk_sum, optional_sums=True)
+    _need(fn, "o", o, _float_dtype(shape), B * Hq * d, dev)
+    _need(fn, "lse", lse, _F32, B * Hq, dev)
+    _check(fn, lib().hga_decode_attend(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(pos), _ptr(group_idx), _ptr(o),
         _ptr(lse), _ptr(group_sum), _ptr(chunk_sum), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 

@@ -490,8 +490,11 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   for (int k = 0; k < kMaxBlocks / 256; ++k) {
     const int i = tid + 256 * k;
     if (i < n_visits) {
-      vlist[i] = vv[k] & 0xFFFF;
-      vmask[i] = (uint32_t)vv[k] >> 16;
+      // entries come from the dQ kernel's selection inverse; a block id outside the
+      // segment (never written that way) is clamped and masked out rather than read
+      const int jj = vv[k] & 0xFFFF;
+      vlist[i] = min(jj, a.nb - 1);
+      vmask[i] = jj < a.nb ? (uint32_t)vv[k] >> 16 : 0u;
     }
   }
   // This wave's share of the K/V copies has landed (only the second round's may still
@@ -805,40 +808,46 @@ __global__ __launch_bounds__(256) void attend_bwd_dkdv_f32_kernel(BwdArgs a, int
   for (int e = 0; e < DQ; ++e) { dko[e] = dk[e] * a.scale; dvo[e] = dv[e]; }
 }
 
-// Launches kernel i of the backward; with timing events, its start and stop
-// timestamps are taken from the dispatch itself (no extra packets in the stream).
+// Launches kernel i of the backward and returns the launch's own status; with
+// timing events, its start and stop timestamps are taken from the dispatch itself
+// (no extra packets in the stream).
 struct Launcher {
   const hipEvent_t* ev;
   hipStream_t s;
   template <typename... KA, typename... A>
-  void operator()(int i, void (*kernel)(KA...), dim3 grid, dim3 block, A... args) const {
-    if (ev && (ev[2 * i] || ev[2 * i + 1]))
-      hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev[2 * i], ev[2 * i + 1], 0, args...);
-    else
-      hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  hipError_t operator()(int i, void (*kernel)(KA...), dim3 grid, dim3 block, A... args) const {
+    return launch_kernel_timed(kernel, grid, block, s, ev ? ev[2 * i] : nullptr, ev ? ev[2 * i + 1] : nullptr,
+                               args...);
   }
   // a kernel that this path does not need: both marks back to back
-  void skip(int i) const {
-    if (ev && ev[2 * i]) (void)hipEventRecord(ev[2 * i], s);
-    if (ev && ev[2 * i + 1]) (void)hipEventRecord(ev[2 * i + 1], s);
+  hipError_t skip(int i) const {
+    hipError_t e = hipSuccess;
+    if (ev && ev[2 * i]) e = hipEventRecord(ev[2 * i], s);
+    if (e == hipSuccess && ev && ev[2 * i + 1]) e = hipEventRecord(ev[2 * i + 1], s);
+    return e;
   }
 };
 
+// The four launches in order; the first one the runtime rejects ends the sequence,
+// so no later kernel reads a workspace that an earlier one did not fill.
 template <int D, int G>
-void launch_bf16(const BwdArgs& a, const Launcher& run) {
+hipError_t launch_bf16(const BwdArgs& a, const Launcher& run) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per dQ work-group
-  run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))), dim3(128 * HPW), a);
-  run(1, attend_bwd_order_kernel<G>, dim3(1), dim3(kOrderThreads), a);
-  run(2, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
-  run(3, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
+  hipError_t e = run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))),
+                     dim3(128 * HPW), a);
+  if (e == hipSuccess) e = run(1, attend_bwd_order_kernel<G>, dim3(1), dim3(kOrderThreads), a);
+  if (e == hipSuccess) e = run(2, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
+  if (e == hipSuccess)
+    e = run(3, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
+  return e;
 }
 template <int D>
-void launch_bf16_g(const BwdArgs& a, int G, const Launcher& run) {
+hipError_t launch_bf16_g(const BwdArgs& a, int G, const Launcher& run) {
   switch (G) {
-    case 1: launch_bf16<D, 1>(a, run); break;
-    case 2: launch_bf16<D, 2>(a, run); break;
-    case 4: launch_bf16<D, 4>(a, run); break;
-    default: launch_bf16<D, 8>(a, run); break;
+    case 1: return launch_bf16<D, 1>(a, run);
+    case 2: return launch_bf16<D, 2>(a, run);
+    case 4: return launch_bf16<D, 4>(a, run);
+    default: return launch_bf16<D, 8>(a, run);
   }
 }
 
@@ -876,19 +885,16 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   a.scale = d.scale;
   a.target_rounds = d.t_hist >= 3 * d.seg_len ? kTargetRoundsLongHistory : kTargetRoundsShortHistory;
   const int grid = xcd_grid(a.n_units);
-  if (bf16) {
-    if (d.D == 128) launch_bf16_g<128>(a, d.G, run);
-    else launch_bf16_g<64>(a, d.G, run);
-  } else {
-    // fp32: dQ and dK/dV each in one kernel, no work list and no partial sums
-    if (d.D == 128) run(0, attend_bwd_dq_f32_kernel<128>, dim3(grid), dim3(64 * d.G), a, d.G);
-    else run(0, attend_bwd_dq_f32_kernel<64>, dim3(grid), dim3(64 * d.G), a, d.G);
-    run.skip(1);
-    if (d.D == 128) run(2, attend_bwd_dkdv_f32_kernel<128>, dim3(grid), dim3(256), a, d.G);
-    else run(2, attend_bwd_dkdv_f32_kernel<64>, dim3(grid), dim3(256), a, d.G);
-    run.skip(3);
-  }
-  return hipGetLastError();
+  if (bf16) return d.D == 128 ? launch_bf16_g<128>(a, d.G, run) : launch_bf16_g<64>(a, d.G, run);
+  // fp32: dQ and dK/dV each in one kernel, no work list and no partial sums
+  hipError_t e = d.D == 128 ? run(0, attend_bwd_dq_f32_kernel<128>, dim3(grid), dim3(64 * d.G), a, d.G)
+                            : run(0, attend_bwd_dq_f32_kernel<64>, dim3(grid), dim3(64 * d.G), a, d.G);
+  if (e == hipSuccess) e = run.skip(1);
+  if (e == hipSuccess)
+    e = d.D == 128 ? run(2, attend_bwd_dkdv_f32_kernel<128>, dim3(grid), dim3(256), a, d.G)
+                   : run(2, attend_bwd_dkdv_f32_kernel<64>, dim3(grid), dim3(256), a, d.G);
+  if (e == hipSuccess) e = run.skip(3);
+  return e;
 }
 
 }  // namespace hga

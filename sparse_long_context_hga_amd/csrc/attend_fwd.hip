@@ -285,19 +285,18 @@ __global__ __launch_bounds__(512) void attend_fwd_f32_kernel(FwdArgs a, int G) {
 }
 
 template <int D, int G>
-void launch_bf16(const FwdArgs& a, int grid, hipStream_t s) {
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per work-group
-  (void)grid;
-  hipLaunchKernelGGL((attend_fwd_bf16_kernel<D, G, HPW>), dim3(xcd_grid(a.n_units * (G / HPW))),
-                     dim3(128 * HPW), 0, s, a);
+  return launch_kernel(attend_fwd_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))), dim3(128 * HPW),
+                       s, a);
 }
 template <int D>
-void launch_bf16_g(const FwdArgs& a, int G, int grid, hipStream_t s) {
+hipError_t launch_bf16_g(const FwdArgs& a, int G, hipStream_t s) {
   switch (G) {
-    case 1: launch_bf16<D, 1>(a, grid, s); break;
-    case 2: launch_bf16<D, 2>(a, grid, s); break;
-    case 4: launch_bf16<D, 4>(a, grid, s); break;
-    default: launch_bf16<D, 8>(a, grid, s); break;
+    case 1: return launch_bf16<D, 1>(a, s);
+    case 2: return launch_bf16<D, 2>(a, s);
+    case 4: return launch_bf16<D, 4>(a, s);
+    default: return launch_bf16<D, 8>(a, s);
   }
 }
 
@@ -311,14 +310,9 @@ hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kg = d.kg; a.nb = d.nb; a.n_units = d.B * d.Hkv * d.nb;
   a.scale = d.scale;
   const int grid = xcd_grid(a.n_units);
-  if (bf16) {
-    if (d.D == 128) launch_bf16_g<128>(a, d.G, grid, s);
-    else launch_bf16_g<64>(a, d.G, grid, s);
-  } else {
-    if (d.D == 128) hipLaunchKernelGGL((attend_fwd_f32_kernel<128>), dim3(grid), dim3(64 * d.G), 0, s, a, d.G);
-    else hipLaunchKernelGGL((attend_fwd_f32_kernel<64>), dim3(grid), dim3(64 * d.G), 0, s, a, d.G);
-  }
-  return hipGetLastError();
+  if (bf16) return d.D == 128 ? launch_bf16_g<128>(a, d.G, s) : launch_bf16_g<64>(a, d.G, s);
+  return d.D == 128 ? launch_kernel(attend_fwd_f32_kernel<128>, dim3(grid), dim3(64 * d.G), s, a, d.G)
+                    : launch_kernel(attend_fwd_f32_kernel<64>, dim3(grid), dim3(64 * d.G), s, a, d.G);
 }
 
 }  // namespace hga

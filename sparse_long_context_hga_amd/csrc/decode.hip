@@ -536,24 +536,22 @@ template <typename T, int D>
 hipError_t launch_route_t(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_units * a.n_slices)), block(kDecThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_route_kernel<T, D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_route_kernel<T, D, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_route_kernel<T, D, 4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_route_kernel<T, D, 8>), grid, block, 0, s, a); break;
+    case 1: return launch_kernel(decode_route_kernel<T, D, 1>, grid, block, s, a);
+    case 2: return launch_kernel(decode_route_kernel<T, D, 2>, grid, block, s, a);
+    case 4: return launch_kernel(decode_route_kernel<T, D, 4>, grid, block, s, a);
+    default: return launch_kernel(decode_route_kernel<T, D, 8>, grid, block, s, a);
   }
-  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_attend_t(const DecodeArgs& a, int G, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_units * a.n_split)), block(kDecThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_attend_kernel<T, D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_attend_kernel<T, D, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_attend_kernel<T, D, 4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_attend_kernel<T, D, 8>), grid, block, 0, s, a); break;
+    case 1: return launch_kernel(decode_attend_kernel<T, D, 1>, grid, block, s, a);
+    case 2: return launch_kernel(decode_attend_kernel<T, D, 2>, grid, block, s, a);
+    case 4: return launch_kernel(decode_attend_kernel<T, D, 4>, grid, block, s, a);
+    default: return launch_kernel(decode_attend_kernel<T, D, 8>, grid, block, s, a);
   }
-  return hipGetLastError();
 }
 
 // Workspace: rcount, acount, keys, part (256-byte aligned pieces).

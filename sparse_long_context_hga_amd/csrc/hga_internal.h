@@ -1,10 +1,30 @@
 // Host-side launch interface between the C ABI (hga_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace hga {
+
+template <typename T>
+struct no_deduce { using type = T; };
+
+// Launch of kernel `k` on stream `s` that returns this launch's own status: the
+// HIP launch call reports it directly, so an error left behind by an unrelated
+// earlier HIP call on the thread is neither returned nor cleared.  With start /
+// stop events (may be null) the dispatch itself records them.
+template <typename... P>
+hipError_t launch_kernel_timed(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                               hipEvent_t stop, typename no_deduce<P>::type... args) {
+  void* ptrs[] = {static_cast<void*>(&args)...};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, s, start, stop, 0);
+}
+template <typename... P>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s,
+                         typename no_deduce<P>::type... args) {
+  return launch_kernel_timed(k, grid, block, s, nullptr, nullptr, args...);
+}
 
 // Validated, resolved sizes of one call.
 struct Dims {

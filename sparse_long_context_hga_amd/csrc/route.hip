@@ -289,17 +289,17 @@ __global__ __launch_bounds__(kRouteThreadsF32) void route_f32_kernel(RouteArgs a
 }
 
 template <int D, int G>
-void launch_bf16(const RouteArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((route_bf16_kernel<D, G>), dim3(grid), dim3(route_threads<G>()), 0, s, a);
+hipError_t launch_bf16(const RouteArgs& a, int grid, hipStream_t s) {
+  return launch_kernel(route_bf16_kernel<D, G>, dim3(grid), dim3(route_threads<G>()), s, a);
 }
 
 template <int D>
-void launch_bf16_g(const RouteArgs& a, int G, int grid, hipStream_t s) {
+hipError_t launch_bf16_g(const RouteArgs& a, int G, int grid, hipStream_t s) {
   switch (G) {
-    case 1: launch_bf16<D, 1>(a, grid, s); break;
-    case 2: launch_bf16<D, 2>(a, grid, s); break;
-    case 4: launch_bf16<D, 4>(a, grid, s); break;
-    default: launch_bf16<D, 8>(a, grid, s); break;
+    case 1: return launch_bf16<D, 1>(a, grid, s);
+    case 2: return launch_bf16<D, 2>(a, grid, s);
+    case 4: return launch_bf16<D, 4>(a, grid, s);
+    default: return launch_bf16<D, 8>(a, grid, s);
   }
 }
 
@@ -316,14 +316,9 @@ hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* q_p
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kc = d.kc; a.kg = d.kg; a.nb = d.nb;
   a.n_units = d.B * d.Hkv * d.nb;
   const int grid = xcd_grid(a.n_units);
-  if (bf16) {
-    if (d.D == 128) launch_bf16_g<128>(a, d.G, grid, s);
-    else launch_bf16_g<64>(a, d.G, grid, s);
-  } else {
-    if (d.D == 128) hipLaunchKernelGGL((route_f32_kernel<128>), dim3(grid), dim3(kRouteThreadsF32), 0, s, a, d.G);
-    else hipLaunchKernelGGL((route_f32_kernel<64>), dim3(grid), dim3(kRouteThreadsF32), 0, s, a, d.G);
-  }
-  return hipGetLastError();
+  if (bf16) return d.D == 128 ? launch_bf16_g<128>(a, d.G, grid, s) : launch_bf16_g<64>(a, d.G, grid, s);
+  return d.D == 128 ? launch_kernel(route_f32_kernel<128>, dim3(grid), dim3(kRouteThreadsF32), s, a, d.G)
+                    : launch_kernel(route_f32_kernel<64>, dim3(grid), dim3(kRouteThreadsF32), s, a, d.G);
 }
 
 }  // namespace hga

@@ -88,9 +88,8 @@ hipError_t launch_t(const Dims& d, const void* k, int64_t t_begin, int64_t t_end
   const int64_t nch = (t_end - t_begin) / kChunk;
   if (nch == 0) return hipSuccess;
   dim3 grid((unsigned)nch, (unsigned)d.Hkv, (unsigned)d.B);
-  hipLaunchKernelGGL((summaries_kernel<T, D>), grid, dim3(2 * D), 0, s, (const T*)k, d.t_cap,
-                     t_begin / kChunk, (T*)gs, (T*)cs);
-  return hipGetLastError();
+  return launch_kernel(summaries_kernel<T, D>, grid, dim3(2 * D), s, (const T*)k, d.t_cap, t_begin / kChunk,
+                       (T*)gs, (T*)cs);
 }
 
 }  // namespace

@@ -11,6 +11,9 @@ stream; every step of the computation runs in libhga.so.
   hga_attention    -- autograd op for one active segment: forward routes and
                       attends; backward returns dQ, dK, dV of the active segment
                       only (the history is detached).
+  HGAStack         -- segment-wise truncated backpropagation through a stack of
+                      HGA layers, each with its own cache (forward, backward,
+                      detach, next segment).
   HGADecoder       -- generation over an HGAKVCache: one new token per sequence
                       per step (per-token routing, attention, and the summaries of
                       a chunk once its last token is in).
@@ -151,10 +154,38 @@ class HGAKVCache:
         self.q_last, self._q_pending = self._q_pending, None
 
 
+def _check_segment(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cache: "HGAKVCache"):
+    """Host-side agreement of a segment's tensors with the cache they are attended
+    against (dtype, head size, batch, KV heads, device): the library reads the
+    cache with the dtype and head size of the call, so a mismatch would otherwise
+    become out-of-bounds device accesses."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, Hq, S, d], got {tuple(q.shape)}")
+    B, Hq, S, d = q.shape
+    if q.dtype != cache.dtype:
+        raise ValueError(f"q has dtype {q.dtype} but the cache holds {cache.dtype}")
+    if d != cache.head_dim or B != cache.batch:
+        raise ValueError(f"q [B={B}, d={d}] does not match the cache [B={cache.batch}, d={cache.head_dim}]")
+    if Hq % cache.n_kv_heads != 0:
+        raise ValueError(f"{Hq} query heads are not a multiple of the cache's {cache.n_kv_heads} KV heads")
+    if S <= 0 or S % 64 != 0:
+        raise ValueError(f"segment length {S} must be a positive multiple of 64")
+    want = (B, cache.n_kv_heads, S, d)
+    for name, t in (("k_seg", k_seg), ("v_seg", v_seg)):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must be {list(want)}, got {list(t.shape)}")
+        if t.dtype != cache.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype} but the cache holds {cache.dtype}")
+    for name, t in (("q", q), ("k_seg", k_seg), ("v_seg", v_seg)):
+        if t.device != cache.k.device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {cache.k.device}")
+
+
 class _HGAAttentionFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k_seg, v_seg, cache: HGAKVCache, top_chunks: int, top_groups: int, scale: float,
                 causal_routing: bool):
+        _check_segment(q, k_seg, v_seg, cache)
         B, Hq, S, d = q.shape
         shape = L.make_shape(B, Hq, cache.n_kv_heads, d, top_chunks, top_groups, _dtype_name(q.dtype), scale)
         q = q.contiguous()
@@ -176,11 +207,11 @@ class _HGAAttentionFn(torch.autograd.Function):
         L.hga_attend_fwd(shape, q, cache.k, cache.v, cache.t_cap, t_hist, S, gidx, o, lse)
         ctx.save_for_backward(q, o, lse, gidx)
         ctx.cache, ctx.shape, ctx.t_hist = cache, shape, t_hist
-        ctx.mark_non_differentiable(gidx)
-        return o, gidx
+        ctx.mark_non_differentiable(lse, gidx)
+        return o, lse, gidx
 
     @staticmethod
-    def backward(ctx, d_o, _g):
+    def backward(ctx, d_o, _lse, _g):
         q, o, lse, gidx = ctx.saved_tensors
         cache, shape, t_hist = ctx.cache, ctx.shape, ctx.t_hist
         B, Hq, S, d = q.shape
@@ -200,7 +231,9 @@ def hga_attention(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cac
     """Routed attention of one active segment against the cache's history plus itself.
 
     q [B,Hq,S,d], k_seg/v_seg [B,Hkv,S,d] (the segment's keys/values, written into
-    the cache at its current length).  Returns (o [B,Hq,S,d], group_idx).  Call
+    the cache at its current length; same dtype, batch, KV heads and head size as
+    the cache).  Returns (o [B,Hq,S,d], lse [B,Hq,S] float32, group_idx); lse and
+    group_idx carry no gradient.  Call
     cache.commit(S) once the segment's backward is done to turn it into history.
     causal_routing: route each block with the block before it (hga_route_causal);
     then every segment written to the cache must be routed that way.
@@ -235,6 +268,15 @@ class HGADecoder:
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor):
         c = self.cache
+        B, Hq, Hkv, d = self.shape.batch, self.shape.n_q_heads, c.n_kv_heads, c.head_dim
+        if tuple(q.shape) != (B, Hq, d) or q.dtype != c.dtype or q.device != c.k.device:
+            raise ValueError(f"q must be [{B}, {Hq}, {d}] {c.dtype} on {c.k.device}, got "
+                             f"{list(q.shape)} {q.dtype} on {q.device}")
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if tuple(t.shape) != (B, Hkv, d):
+                raise ValueError(f"{name} must be [{B}, {Hkv}, {d}], got {list(t.shape)}")
+        if tuple(pos.shape) != (B,) or pos.dtype != torch.int32 or pos.device != c.k.device:
+            raise ValueError(f"pos must be a [{B}] int32 tensor on {c.k.device}")
         live = pos >= 0
         bi, p = self._b[live], pos[live].long()
         c.k[bi, :, p] = k_new[live].to(c.dtype)

@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -13,7 +14,16 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running oracle check")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests run in one process on the GPU machine; on a host without a GPU they are skipped
-    # unless selected explicitly with -m gpu (which then fails loudly if no GPU is present).
-    pass
+def pytest_sessionfinish(session, exitstatus):
+    """Write the near-tie exemptions that the GPU parity tests recorded (test name ->
+    exempt pairs, units that needed one, units checked) to $HGA_PARITY_RECORD, or to
+    gpurun_out/parity_exemptions.json when that folder exists."""
+    chk = sys.modules.get("tests.hga_check")
+    if chk is None or not getattr(chk, "EXEMPTIONS", None):
+        return
+    path = os.environ.get("HGA_PARITY_RECORD")
+    if not path and os.path.isdir(os.path.join(ROOT, "gpurun_out")):
+        path = os.path.join(ROOT, "gpurun_out", "parity_exemptions.json")
+    if path:
+        with open(path, "w") as f:
+            json.dump(chk.EXEMPTIONS, f, indent=1, sort_keys=True)

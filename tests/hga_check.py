@@ -77,6 +77,22 @@ def check_route_unit(w, gs, cs, b, kvh, j, cidx_row, gidx_row, causal=False, q_p
                            (b, kvh, j))
 
 
+def _top_by_rule(scores: np.ndarray, ids, k: int):
+    """The selection the oracle's rule makes -- first min(k, n) ids by (score
+    descending, id ascending) -- ascending (np.lexsort, for the fast path below)."""
+    ids = np.asarray(ids, np.int64)
+    order = np.lexsort((ids, -np.asarray(scores, np.float64)))
+    return sorted(int(x) for x in ids[order[:max(0, min(k, len(ids)))]])
+
+
+def _accept(sel, ids, scores, k):
+    """Acceptance of a GPU selection under the near-tie rule: equal to the rule's own
+    top-k needs no exemption; anything else goes through the oracle's pairwise check."""
+    if sel == _top_by_rule(scores, ids, k):
+        return True, 0
+    return ora.selection_accepted(sel, ids, scores, k, NEAR_TIE_REL)
+
+
 def check_selection(rows, J, gs, cs, b, kvh, cidx_row, gidx_row, top_chunks, top_groups, where) -> int:
     """Acceptance of a GPU selection made by the given query rows over candidate
     chunks [0, J), against the oracle's scores.  Returns the near-tie exemptions."""
@@ -84,16 +100,64 @@ def check_selection(rows, J, gs, cs, b, kvh, cidx_row, gidx_row, top_chunks, top
     csel = [int(x) for x in cidx_row if x >= 0]
     assert all(x == -1 for x in cidx_row[len(csel):]), "chunk list not -1 padded at the end"
     assert csel == sorted(csel), "chunk ids not ascending"
-    ok, ex1 = ora.selection_accepted(csel, list(range(J)), sig, top_chunks, NEAR_TIE_REL)
+    ok, ex1 = _accept(csel, list(range(J)), sig, top_chunks)
     assert ok, f"chunk selection rejected at unit {where}: {csel}"
     gids = [8 * c + u for c in csel for u in range(8)]
     tau = ora.block_scores(rows, gs[b, kvh, gids]) if gids else np.zeros(0, np.float32)
     gsel = [int(x) for x in gidx_row if x >= 0]
     assert all(x == -1 for x in gidx_row[len(gsel):]), "group list not -1 padded at the end"
     assert gsel == sorted(gsel), "group ids not ascending"
-    ok, ex2 = ora.selection_accepted(gsel, gids, tau, top_groups, NEAR_TIE_REL)
+    ok, ex2 = _accept(gsel, gids, tau, top_groups)
     assert ok, f"group selection rejected at unit {where}: {gsel}"
     return ex1 + ex2
+
+
+def accept_all_units(w, gs, cs, cidx, gidx, name: str, ocidx=None, tables=None) -> None:
+    """Acceptance of every unit's GPU selection (block routing), with the near-tie
+    exemptions recorded and bounded.  With the oracle's own route() output
+    (ocidx, tables) a unit whose chunk set equals the oracle's reuses the oracle's
+    score tables instead of scoring again."""
+    pairs = units_ex = n = 0
+    for b in range(w.batch):
+        for kvh in range(w.n_kv_heads):
+            for j in range(w.seg_len // 64):
+                crow, grow = cidx[b, kvh, j], gidx[b, kvh, j]
+                if tables is not None and np.array_equal(crow, ocidx[b, kvh, j]):
+                    sig, gids, tau = tables[(b, kvh, j)]
+                    J = w.t_hist // 64 + j
+                    csel = [int(x) for x in crow if x >= 0]
+                    gsel = [int(x) for x in grow if x >= 0]
+                    assert all(x == -1 for x in grow[len(gsel):]) and gsel == sorted(gsel)
+                    ok, e1 = _accept(csel, list(range(J)), sig, w.top_chunks)
+                    assert ok, f"chunk selection rejected at unit {(b, kvh, j)}"
+                    ok, e2 = _accept(gsel, gids, tau, w.top_groups)
+                    assert ok, f"group selection rejected at unit {(b, kvh, j)}: {gsel}"
+                    e = e1 + e2
+                else:
+                    e = check_route_unit(w, gs, cs, b, kvh, j, crow, grow)
+                pairs += e
+                units_ex += e > 0
+                n += 1
+    record_exemptions(name, pairs, units_ex, n)
+
+
+def chain_matches(w, gidx, ogidx, o_chain, lse_chain, o_ref, lse_ref) -> int:
+    """On every unit whose GPU selection equals the oracle's, the forward of the
+    chained path (GPU routing) and the forward given the oracle's selection must be
+    bit-identical (a unit's forward reads only its own selection).  Returns the
+    number of such units."""
+    G = w.group_size
+    n = 0
+    for b in range(w.batch):
+        for kvh in range(w.n_kv_heads):
+            for j in range(w.seg_len // 64):
+                if not np.array_equal(gidx[b, kvh, j], ogidx[b, kvh, j]):
+                    continue
+                sl = (b, slice(kvh * G, (kvh + 1) * G), slice(64 * j, 64 * j + 64))
+                assert np.array_equal(o_chain[sl], o_ref[sl]), f"chained O differs at unit {(b, kvh, j)}"
+                assert np.array_equal(lse_chain[sl], lse_ref[sl]), f"chained LSE differs at unit {(b, kvh, j)}"
+                n += 1
+    return n
 
 
 def oracle_route(w, gs, cs):
@@ -118,28 +182,74 @@ def fwd_errors(w, o_gpu, lse_gpu, gidx, units=None) -> Tuple[float, float]:
     return eo, el
 
 
+def _rel_l2_rows(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Relative L2 error of every leading-index slice ([..., rows, d] -> [...])."""
+    num = np.sqrt(((got - ref) ** 2).sum(axis=(-2, -1)))
+    den = np.maximum(np.sqrt((ref ** 2).sum(axis=(-2, -1))), 1e-30)
+    return num / den
+
+
 def bwd_errors(w, dq_gpu, dk_gpu, dv_gpu, gidx, units=None, chunks=None) -> Dict[str, float]:
-    """Relative-L2 errors of dQ, dK_active, dV_active against the oracle."""
+    """Relative-L2 errors of dQ, dK_active, dV_active against the oracle: over each
+    whole tensor ("dq", "dk", "dv") and the largest over 64-row pieces -- every
+    (sequence, query head, query block) of dQ ("dq_block_max") and every
+    (sequence, KV head, active chunk) of dK / dV ("dk_chunk_max", "dv_chunk_max"),
+    so that one wrong block or chunk cannot hide in a whole-tensor norm."""
     G = w.group_size
+    d = w.head_dim
     if units is None:
         dq, dk, dv = ora.attend_bwd(w.q, w.k_cache, w.v_cache, w.d_o, w.t_hist, gidx, w.softmax_scale, G)
-        return {"dq": rel_l2(dq_gpu, dq), "dk": rel_l2(dk_gpu, dk), "dv": rel_l2(dv_gpu, dv)}
+        nb = w.seg_len // 64
+        blk = lambda x: x.reshape(x.shape[0], x.shape[1], nb, 64, d)   # noqa: E731
+        return {"dq": rel_l2(dq_gpu, dq), "dk": rel_l2(dk_gpu, dk), "dv": rel_l2(dv_gpu, dv),
+                "dq_block_max": float(_rel_l2_rows(blk(dq_gpu), blk(dq)).max()),
+                "dk_chunk_max": float(_rel_l2_rows(blk(dk_gpu), blk(dk)).max()),
+                "dv_chunk_max": float(_rel_l2_rows(blk(dv_gpu), blk(dv)).max())}
     got, ref = [], []
     for (b, kvh, j) in units:
         r = ora.dq_unit(w.q, w.k_cache, w.v_cache, w.d_o, w.t_hist, gidx[b, kvh, j], b, kvh, j,
                         w.softmax_scale, G)
-        got.append(dq_gpu[b, kvh * G:(kvh + 1) * G, 64 * j:64 * j + 64].reshape(-1, w.head_dim))
+        got.append(dq_gpu[b, kvh * G:(kvh + 1) * G, 64 * j:64 * j + 64].reshape(-1, d))
         ref.append(r)
-    out = {"dq": rel_l2(np.concatenate(got), np.concatenate(ref))}
+    gq, rq = np.stack(got), np.stack(ref)
+    out = {"dq": rel_l2(gq, rq),
+           "dq_block_max": float(_rel_l2_rows(gq.reshape(-1, 64, d), rq.reshape(-1, 64, d)).max())}
     gk, gv, rk, rv = [], [], [], []
     for (b, kvh, cc) in chunks:
         dk, dv = ora.dkdv_active_chunk(w.q, w.k_cache, w.v_cache, w.d_o, w.t_hist, gidx, b, kvh, cc,
                                        w.softmax_scale, G)
         gk.append(dk_gpu[b, kvh, 64 * cc:64 * cc + 64]); rk.append(dk)
         gv.append(dv_gpu[b, kvh, 64 * cc:64 * cc + 64]); rv.append(dv)
-    out["dk"] = rel_l2(np.concatenate(gk), np.concatenate(rk))
-    out["dv"] = rel_l2(np.concatenate(gv), np.concatenate(rv))
+    gk, rk, gv, rv = np.stack(gk), np.stack(rk), np.stack(gv), np.stack(rv)
+    out["dk"] = rel_l2(gk, rk)
+    out["dv"] = rel_l2(gv, rv)
+    out["dk_chunk_max"] = float(_rel_l2_rows(gk, rk).max())
+    out["dv_chunk_max"] = float(_rel_l2_rows(gv, rv).max())
     return out
+
+
+def assert_grads(errs: Dict[str, float], tol: float = TOL_GRAD_REL_L2) -> None:
+    """Every whole-tensor and every per-block / per-chunk relative L2 within tol."""
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"gradient errors above {tol}: {bad}"
+
+
+# Near-tie exemptions of the selection acceptance rule, per test (appended by
+# record_exemptions, written out at the end of the session by conftest.py).
+EXEMPTIONS: Dict[str, Dict[str, int]] = {}
+# Largest share of checked units that may lean on a near-tie exemption: the
+# scores come from random data, so exact ties within 1e-5 relative are rare and
+# a larger share means the selection itself is off.
+MAX_EXEMPT_UNIT_SHARE = 0.02
+
+
+def record_exemptions(name: str, exempt_pairs: int, units_exempt: int, units: int) -> None:
+    """Record and bound the near-tie exemptions of one test."""
+    EXEMPTIONS[name] = {"exempt_pairs": int(exempt_pairs), "units_with_exemption": int(units_exempt),
+                        "units_checked": int(units)}
+    print(f"{name}: near-tie exemptions {exempt_pairs} pairs in {units_exempt} of {units} units", flush=True)
+    assert units_exempt <= max(1, MAX_EXEMPT_UNIT_SHARE * units), \
+        f"{name}: {units_exempt} of {units} units needed a near-tie exemption"
 
 
 def smoke_check() -> None:
@@ -172,5 +282,5 @@ def smoke_check() -> None:
     errs = bwd_errors(w, to_np(L.dq), to_np(L.dk), to_np(L.dv), ogidx)
     print(f"smoke: O max-abs {eo:.3e} LSE max-abs {el:.3e} grads rel-L2 {errs}", flush=True)
     assert eo <= TOL_O["bf16"] and el <= TOL_O["bf16"]
-    assert all(v <= TOL_GRAD_REL_L2 for v in errs.values())
+    assert_grads(errs)
     print("smoke: ok", flush=True)
