@@ -16,6 +16,8 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
  *    never allocates, frees or synchronizes; every call only enqueues kernels
  *    on `stream` (a hipStream_t handle; NULL = the default stream) and returns.
+ *    Scratch memory comes from the caller (workspace arguments), or for
+ *    hga_decode_step_noalloc from a static device array inside the library.
  *  - Tensors are dense, row-major, 16-byte aligned.  Float tensors (q, k, v, o,
  *    d_o, summaries, gradients) all have the element type shape->dtype
  *    (HGA_F32: IEEE float32; HGA_BF16: bfloat16).  lse and the optional score
@@ -30,7 +32,8 @@
  *    On error the call returns a negative hga_status, enqueues nothing and
  *    leaves all outputs untouched.  HGA_ERR_HIP means a launch was rejected by
  *    the HIP runtime (outputs then undefined).
- *  - Calls are re-entrant and thread-safe; the library holds no mutable state.
+ *  - Calls are re-entrant and thread-safe; the library holds no mutable state,
+ *    except hga_decode_step_noalloc's static device scratch (see there).
  */
 #ifndef HGA_H
 #define HGA_H
@@ -268,6 +271,34 @@ int hga_decode_attend(const hga_shape* shape, const void* q, const void* k_cache
                       const void* v_cache, int64_t t_cap, const int32_t* pos,
                       const int32_t* group_idx, void* o, float* lse, void* group_sum,
                       void* chunk_sum, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hga_decode_step_noalloc -- hga_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  It allocates and frees
+ * nothing: the generation step's workspace is a static device array inside the
+ * library, HGA_DECODE_NOALLOC_MAX_BYTES bytes on each GPU it runs on, held until
+ * the process ends.  Its device address is looked up on the first call on each
+ * device (with that device current), which also clears the array's arrival
+ * counters once, on that call's stream.
+ *
+ * Arguments, results and errors as hga_decode_step (with `stream` on the current
+ * device), except:
+ *  - HGA_ERR_WORKSPACE: the call needs more than the static array holds (more than
+ *    HGA_DECODE_NOALLOC_MAX_UNITS sequence x KV-head units, or a workspace of
+ *    hga_decode_workspace_size() plus the fixed counter area above
+ *    HGA_DECODE_NOALLOC_MAX_BYTES: e.g. 64 sequences x 8 KV heads at 131,072 tokens
+ *    and top-16 chunks / top-64 groups fit);
+ *  - every call on one GPU shares that GPU's array: calls that overlap in time on
+ *    one GPU (other streams, other threads) race and must be serialised by the
+ *    caller; calls in one stream are ordered and safe.
+ */
+#define HGA_DECODE_NOALLOC_MAX_BYTES (32u << 20)
+#define HGA_DECODE_NOALLOC_MAX_UNITS 16384
+int hga_decode_step_noalloc(const hga_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, void* chunk_sum, void* group_sum, int64_t t_cap,
+                            const int32_t* pos, int32_t* chunk_idx, int32_t* group_idx, void* o,
+                            float* lse, void* stream);
 
 /* Static description of a status code. */
 const char* hga_status_string(int status);

@@ -108,6 +108,7 @@ SIGNATURES = {
     "hga_decode_route": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "hga_decode_attend": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                          _P]),
+    "hga_decode_step_noalloc": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
     "hga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -309,7 +310,8 @@ def _decode_checks(fn, shape, dev, q, t_cap, pos, chunk_idx, group_idx, workspac
     _need(fn, "chunk_idx", chunk_idx, _I32, B * Hkv * shape.top_chunks, dev,
           optional=chunk_optional or shape.top_chunks == 0)
     _need(fn, "group_idx", group_idx, _I32, B * Hkv * shape.top_groups, dev, optional=shape.top_groups == 0)
-    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.device != dev
+                                  or not workspace.is_contiguous()):
         raise ValueError(f"{fn}: workspace must be a contiguous tensor on {dev}")
 
 
@@ -328,6 +330,24 @@ def hga_decode_step(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_c
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap,
         _ptr(pos), _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def hga_decode_step_noalloc(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            chunk_sum: torch.Tensor, group_sum: torch.Tensor, t_cap: int, pos: torch.Tensor,
+                            chunk_idx: Optional[torch.Tensor], group_idx: torch.Tensor, o: torch.Tensor,
+                            lse: torch.Tensor, stream=None) -> None:
+    """hga_decode_step with the library's static device scratch as its workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    fn = "hga_decode_step_noalloc"
+    dev = _dev_of(q, k_cache, v_cache)
+    B, Hq, _, d = _dims(shape)
+    _decode_checks(fn, shape, dev, q, t_cap, pos, chunk_idx, group_idx, None, chunk_optional=True)
+    _cache_checks(fn, shape, dev, t_cap, k_cache, v_cache, group_sum, chunk_sum)
+    _need(fn, "o", o, _float_dtype(shape), B * Hq * d, dev)
+    _need(fn, "lse", lse, _F32, B * Hq, dev)
+    _check(fn, lib().hga_decode_step_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap,
+        _ptr(pos), _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def hga_decode_route(shape: HgaShape, q: torch.Tensor, chunk_sum: torch.Tensor, group_sum: torch.Tensor,

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhga.so")
-SOURCES = ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "decode.hip", "hga_api.cpp"]
+SOURCES = ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "decode.hip", "noalloc.hip",
+           "hga_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -559,22 +559,25 @@ struct DecodeWs {
   size_t rcount, acount, keys, part, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-DecodeWs decode_ws(const Dims& d) {
+// Workspace layout: the two arrival-counter arrays first (counter_slots entries
+// each, at least one per unit), then the candidates and the partials.
+DecodeWs decode_ws(const Dims& d, size_t counter_slots) {
   const size_t units = (size_t)d.B * d.Hkv;
+  const size_t slots = counter_slots > units ? counter_slots : units;
   const size_t n_split = 1 + (d.kg + kSplitGroups - 1) / kSplitGroups;
   DecodeWs w;
   w.rcount = 0;
-  w.acount = align256(units * 4);
-  w.keys = w.acount + align256(units * 4);
+  w.acount = align256(slots * 4);
+  w.keys = w.acount + align256(slots * 4);
   const size_t n_slices = (size_t)((d.t_cap / kChunk + kSliceChunks - 1) / kSliceChunks);
   w.part = w.keys + align256(units * n_slices * (size_t)d.kc * 8);
   w.total = w.part + align256(units * n_split * (size_t)d.G * (d.D + 2) * 4);
   return w;
 }
 
-DecodeArgs make_args(const Dims& d, void* ws) {
+DecodeArgs make_args(const Dims& d, void* ws, size_t counter_slots) {
   DecodeArgs a = {};
-  const DecodeWs l = decode_ws(d);
+  const DecodeWs l = decode_ws(d, counter_slots);
   char* base = (char*)ws;
   a.rcount = (uint32_t*)(base + l.rcount);
   a.acount = (uint32_t*)(base + l.acount);
@@ -591,14 +594,15 @@ DecodeArgs make_args(const Dims& d, void* ws) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(const Dims& d) { return decode_ws(d).total; }
+size_t decode_workspace_bytes(const Dims& d, size_t counter_slots) { return decode_ws(d, counter_slots).total; }
+size_t decode_counter_bytes(size_t counter_slots) { return 2 * align256(counter_slots * 4); }
 
 hipError_t launch_decode(const Dims& d, bool bf16, bool route, bool attend, const void* q, const void* k,
                          const void* v, const void* chunk_sum, const void* group_sum, const int32_t* pos,
                          int32_t* chunk_idx, int32_t* group_idx, float* chunk_score, float* group_score,
                          void* o, float* lse, void* group_sum_out, void* chunk_sum_out, void* ws,
-                         hipStream_t s) {
-  DecodeArgs a = make_args(d, ws);
+                         hipStream_t s, size_t counter_slots) {
+  DecodeArgs a = make_args(d, ws, counter_slots);
   a.q = q; a.k = k; a.v = v; a.csum = chunk_sum; a.gsum = group_sum; a.pos = pos;
   a.cidx = chunk_idx; a.gidx = group_idx; a.gidx_in = group_idx; a.cscore = chunk_score; a.gscore = group_score;
   a.o = o; a.lse = lse; a.gsum_out = group_sum_out; a.csum_out = chunk_sum_out;

@@ -216,6 +216,31 @@ int hga_decode_step(const hga_shape* shape, const void* q, const void* k_cache, 
                                        chunk_sum, workspace, (hipStream_t)stream));
 }
 
+int hga_decode_step_noalloc(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                            void* chunk_sum, void* group_sum, int64_t t_cap, const int32_t* pos,
+                            int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, 0, 0, d);
+  if (st != HGA_OK) return st;
+  if (t_cap / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !chunk_sum || !group_sum || !pos || !o || !lse || (d.kg > 0 && !group_idx))
+    return HGA_ERR_NULL;
+  static_assert(hga::kNoallocScratchBytes == (size_t)HGA_DECODE_NOALLOC_MAX_BYTES, "header and library agree");
+  static_assert(hga::kNoallocCounterSlots == (size_t)HGA_DECODE_NOALLOC_MAX_UNITS, "header and library agree");
+  if ((size_t)d.B * d.Hkv > hga::kNoallocCounterSlots ||
+      hga::decode_workspace_bytes(d, hga::kNoallocCounterSlots) > hga::kNoallocScratchBytes)
+    return HGA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(chunk_sum) || !aligned16(group_sum) || (chunk_idx && !aligned16(chunk_idx)) ||
+      (group_idx && !aligned16(group_idx)))
+    return HGA_ERR_ALIGN;
+  void* ws = nullptr;
+  if (hga::noalloc_scratch(&ws, (hipStream_t)stream) != hipSuccess) return HGA_ERR_HIP;
+  return hip_status(hga::launch_decode(d, shape->dtype == HGA_BF16, true, true, q, k_cache, v_cache, chunk_sum,
+                                       group_sum, pos, chunk_idx, group_idx, nullptr, nullptr, o, lse, group_sum,
+                                       chunk_sum, ws, (hipStream_t)stream, hga::kNoallocCounterSlots));
+}
+
 int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                    const void* o, const float* lse, const void* d_o, int64_t t_cap, int64_t t_hist,
                    int64_t seg_len, const int32_t* group_idx, void* dq, void* dk_active, void* dv_active,

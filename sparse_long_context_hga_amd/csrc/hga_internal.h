@@ -55,12 +55,24 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
                              void* workspace, hipStream_t s, const hipEvent_t* events = nullptr);
 
 // Generation path (one token per sequence; pos [B] on the device): routing,
-// attention, or both (two launches); ws: decode_workspace_bytes(d) bytes.
-size_t decode_workspace_bytes(const Dims& d);
+// attention, or both (two launches); ws: decode_workspace_bytes(d) bytes.  The
+// workspace starts with two arrays of arrival counters, counter_slots entries each
+// (at least one per (sequence, KV head) unit; 0 means exactly one per unit), that
+// must be zero before the first call and that every call leaves at zero.
+size_t decode_workspace_bytes(const Dims& d, size_t counter_slots = 0);
+// Bytes of the two counter arrays at the start of such a workspace.
+size_t decode_counter_bytes(size_t counter_slots);
+
+// The entry point that allocates nothing takes the generation step's workspace from
+// a static device array of this size, laid out with this many counter slots.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+constexpr size_t kNoallocCounterSlots = (size_t)1 << 14;
+// Device address of the current device's array (looked up once per device).
+hipError_t noalloc_scratch(void** ptr, hipStream_t s);
 hipError_t launch_decode(const Dims& d, bool bf16, bool route, bool attend, const void* q, const void* k,
                          const void* v, const void* chunk_sum, const void* group_sum, const int32_t* pos,
                          int32_t* chunk_idx, int32_t* group_idx, float* chunk_score, float* group_score,
                          void* o, float* lse, void* group_sum_out, void* chunk_sum_out, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, size_t counter_slots = 0);
 
 }  // namespace hga

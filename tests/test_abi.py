@@ -31,6 +31,7 @@ def test_every_declared_symbol_is_exported(L):
     assert set(names) == {"hga_build_summaries", "hga_route", "hga_route_causal", "hga_attend_fwd",
                           "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_attend_bwd_timed",
                           "hga_decode_step", "hga_decode_route", "hga_decode_attend", "hga_decode_workspace_size",
+                          "hga_decode_step_noalloc",
                           "hga_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -177,3 +178,16 @@ def test_decode_validation(L):
     assert step(cidx=M) == -5
     assert step(nbytes=need - 1) == -6
     assert step(t_cap=64 * 8193, nbytes=1 << 40) == -3
+
+
+def test_decode_noalloc_validation(L):
+    """The entry point that allocates nothing rejects, before touching the device,
+    calls that need more than its static scratch holds."""
+    s = _shape(batch=8)
+    assert L.hga_decode_step_noalloc(None, A, A, A, A, A, 8192, A, A, A, A, A, None) == -1
+    assert L.hga_decode_step_noalloc(ctypes.byref(s), None, A, A, A, A, 8192, A, A, A, A, A, None) == -1
+    assert L.hga_decode_step_noalloc(ctypes.byref(s), M, A, A, A, A, 8192, A, A, A, A, A, None) == -5
+    big = _shape(batch=4096)                       # 32,768 (sequence, KV head) units: too many counters
+    assert L.hga_decode_step_noalloc(ctypes.byref(big), A, A, A, A, A, 8192, A, A, A, A, A, None) == -6
+    wide = _shape(batch=64, top_chunks=64, top_groups=512)   # candidates over 512K tokens: too large
+    assert L.hga_decode_step_noalloc(ctypes.byref(wide), A, A, A, A, A, 1 << 19, A, A, A, A, A, None) == -6
