@@ -50,8 +50,9 @@ def parse():
                         "rollout_131k the 64-segment forward rollout")
     p.add_argument("--routing", default="block", choices=["block", "causal"],
                    help="block: each block routes itself (hga_route); causal: the block before it routes it")
-    p.add_argument("--mark-every", type=int, default=8,
-                   help="put per-kernel timing marks on every N-th timed step (default 8)")
+    p.add_argument("--marked-steps", type=int, default=20,
+                   help="steps run after the timed region with every kernel timed from its own dispatch "
+                        "(HIP events recorded by the launches; default 20)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--cold", action="store_true",
                    help="write 512 MiB between timed steps (outside the timing) so that no step finds its "
@@ -114,6 +115,9 @@ def algorithmic_work(w, gidx):
         "summaries": {"bytes": sum_bytes, "flops": 0.0},
         "route": {"bytes": route_bytes, "flops": route_flops},
         "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops, "gather_bytes": kv_sel},
+        # routing and attention in one work-group per unit: Q is read once for both
+        "route_attend": {"bytes": route_bytes + fwd_bytes - q_bytes, "flops": route_flops + fwd_flops,
+                         "gather_bytes": kv_sel},
         "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops, "gather_bytes": kv_sel},
         "attend_bwd_dkdv": {"bytes": dkdv_bytes, "flops": dkdv_flops},
         # the work list and the partial sums are not part of the method
@@ -127,7 +131,8 @@ PMC_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_st
 MFMA_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_mfma.json")}
 CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 # kernel-name prefix -> step kernel (first match wins)
-KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_", "route"), ("attend_fwd_", "attend_fwd"),
+KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_attend_", "route_attend"), ("route_", "route"),
+               ("attend_fwd_", "attend_fwd"),
                ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_order_", "attend_bwd_order"),
                ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv"),
                ("decode_route_kernel", "decode_route"), ("decode_attend_kernel", "decode_attend")]
@@ -232,7 +237,7 @@ def measured_mfma(kernel, workload, ms):
 # Kernel sources each measured workload runs (device headers included).
 WORKLOAD_SOURCES = {
     "qwen3_8b_layer_ctx16k": ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "hga_device.h",
-                              "hga_select.h"],
+                              "hga_select.h", "route_phase.h"],
     "decode_b8_ctx32k": ["decode.hip", "summaries.hip", "hga_device.h", "hga_select.h"],
 }
 
@@ -450,7 +455,8 @@ def main_decode(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    marked = list(range(0, args.steps, max(1, args.mark_every)))
+    # timing marks go on extra steps after the timed region (ids args.steps ...)
+    marked = list(range(args.steps, args.steps + max(1, args.marked_steps)))
     ev = {i: [mk() for _ in range(3)] for i in marked}
     for e in [x for i in marked for x in ev[i]]:
         e.record(stream)
@@ -486,6 +492,9 @@ def main_decode(args):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_per_step = wall * 1e3 / args.steps
+    for i in marked:
+        step(i)
+    torch.cuda.synchronize()
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
     kern_ms = {"decode_route": avg((ev[i][0], ev[i][1]) for i in marked),
                "decode_attend": avg((ev[i][1], ev[i][2]) for i in marked)}
@@ -508,7 +517,8 @@ def main_decode(args):
                    "top_chunks": w.top_chunks, "top_groups": w.top_groups, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
-        "kernel_timing": f"HIP events between the two calls on {len(marked)} of the {args.steps} timed steps",
+        "kernel_timing": f"HIP events between the two calls (one kernel each) on {len(marked)} steps run after "
+                         f"the timed region",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w)
@@ -553,21 +563,14 @@ def main_rollout(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    ev = [[mk() for _ in range(4)] for _ in range(n_seg)]
-    for e in [x for row in ev for x in row]:
-        e.record(stream)
-    torch.cuda.synchronize()
+    ev = [[mk() for _ in range(hga.HGA_FWD_EVENTS)] for _ in range(n_seg)]
 
     def rollout(marks):
         for s_ in range(n_seg):
-            se = ev[s_] if marks else None
-            if se: se[0].record(stream)
-            hga.hga_build_summaries(shape, kc, T, s_ * S, (s_ + 1) * S, gsum, csum)
-            if se: se[1].record(stream)
-            hga.hga_route(shape, qs[s_], csum, gsum, T, s_ * S, S, cidx, gidx)
-            if se: se[2].record(stream)
-            hga.hga_attend_fwd(shape, qs[s_], kc, vc, T, s_ * S, S, gidx, o, lse)
-            if se: se[3].record(stream)
+            # summaries of the segment, then routing + attention (hga_forward); the marked
+            # rollout times every kernel from its own dispatch
+            hga.hga_forward(shape, qs[s_], kc, vc, csum, gsum, T, s_ * S, S, cidx, gidx, o, lse,
+                            events=ev[s_] if marks else None)
 
     for _ in range(args.warmup):
         rollout(False)
@@ -579,27 +582,26 @@ def main_rollout(args):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     rollout(True)                                   # one more, with timing marks
     torch.cuda.synchronize()
-    kern_ms = {"summaries": 0.0, "route": 0.0, "attend_fwd": 0.0}
+    kern_ms = {"summaries": 0.0, "route_attend": 0.0}
     for s_ in range(n_seg):
         kern_ms["summaries"] += ev[s_][0].elapsed_time(ev[s_][1])
-        kern_ms["route"] += ev[s_][1].elapsed_time(ev[s_][2])
-        kern_ms["attend_fwd"] += ev[s_][2].elapsed_time(ev[s_][3])
+        kern_ms["route_attend"] += ev[s_][2].elapsed_time(ev[s_][3])
     # algorithmic bytes of the whole rollout: every segment's summaries (its K read,
     # summaries written), route (Q and the candidate chunk summaries of every block,
     # the group summaries of its selected chunks) and forward (Q, gathered and own
     # K/V, O, LSE); every block selects min(16, J) chunks and then 64 groups once
     # J >= 8.
     el = 2
-    work = {"summaries": 0.0, "route": 0.0, "attend_fwd": 0.0}
+    work = {"summaries": 0.0, "route_attend": 0.0}
     for s_ in range(n_seg):
         work["summaries"] += Hkv * S * d * el + Hkv * (S // 8 + S // 64) * d * el
         J = np.arange(nb) + s_ * S // 64
         nc = np.minimum(16, J)
         ng = np.minimum(64, 8 * nc)
         q_bytes = Hq * S * d * el
-        work["route"] += q_bytes + Hkv * float(np.sum(J + 8 * nc)) * d * el
-        work["attend_fwd"] += (2 * q_bytes + Hkv * float(np.sum(8 * ng)) * d * el * 2
-                               + Hkv * nb * 64 * d * el * 2 + Hq * S * 4)
+        # routing reads the summaries; Q is read once for routing and attention
+        work["route_attend"] += (q_bytes + Hkv * float(np.sum(J + 8 * nc)) * d * el + q_bytes
+                                 + Hkv * float(np.sum(8 * ng)) * d * el * 2 + Hkv * nb * 64 * d * el * 2 + Hq * S * 4)
     kernels = {}
     for k_, ms in kern_ms.items():
         gbs = work[k_] / (ms * 1e-3) / 1e9
@@ -616,7 +618,8 @@ def main_rollout(args):
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom},
         "kernels": kernels,
-        "kernel_timing": "HIP events around every call of one extra, marked rollout (summed over the 64 segments)",
+        "kernel_timing": "every kernel timed from its own dispatch in one extra, marked rollout (summed over the "
+                         "64 segments)",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_rollout()
@@ -724,34 +727,33 @@ def main():
         route = L.route
     L.summaries(0, w.t_hist)                                  # history summaries: built once, untimed
     torch.cuda.synchronize()
+    # What the box reaches on plain library work; these sustained copies and GEMMs
+    # also bring the core clock up from idle before the warm-up steps.
+    achievable = None if args.no_calibration else achievable_rates()
 
-    # Timed region: K steps.  Every `--mark-every`-th step carries HIP timing marks on the
-    # stream the library launches on: events between the calls, and the backward's own
-    # kernels timed from their dispatches.  Marks cost GPU time, so the other steps carry none.
     stream = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
     n_bwd = hga.HGA_BWD_KERNELS
-    marked = list(range(0, args.steps, max(1, args.mark_every)))
-    ev = {i: [mk() for _ in range(4)] for i in marked}             # summaries | route | fwd | end
-    bev = {i: [mk() for _ in range(2 * n_bwd)] for i in marked}    # backward kernels
-    for e in [x for i in marked for x in ev[i] + bev[i]]:
-        e.record(stream)                                            # torch creates the HIP event here
-    torch.cuda.synchronize()
 
-    def step(i):
-        se, be = ev.get(i), bev.get(i)
-        if se: se[0].record(stream)
-        L.summaries(w.t_hist, w.t_hist + w.seg_len)
-        if se: se[1].record(stream)
-        route()
-        if se: se[2].record(stream)
-        L.fwd()
-        if se: se[3].record(stream)
+    def step(fev=None, bev=None):
+        if args.routing == "causal":
+            if fev:
+                fev[0].record(stream)
+            L.summaries(w.t_hist, w.t_hist + w.seg_len)
+            if fev:
+                fev[1].record(stream)
+                fev[2].record(stream)
+            route()
+            L.fwd()
+            if fev:
+                fev[3].record(stream)
+        else:
+            L.forward(events=fev)                     # summaries, then routing + attention
         if L.do is not None:
-            L.bwd(events=be)
+            L.bwd(events=bev)
 
-    for i in range(args.warmup):
-        step(-1 - i)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     if args.cold:
         # every step's inputs leave the MALL first: 512 MiB written between steps,
@@ -761,26 +763,35 @@ def main():
         for i in range(args.steps):
             flush.fill_(i & 255)
             sev[i][0].record(stream)
-            step(i)
+            step()
             sev[i][1].record(stream)
         torch.cuda.synchronize()
         ms_per_step = statistics.mean(a.elapsed_time(b) for a, b in sev)
     else:
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(i)
+            step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_per_step = wall * 1e3 / args.steps
+
+    # Per-kernel times: after the timed region, marked steps in which every kernel is
+    # timed from its own dispatch (start / stop events recorded by the launches, on the
+    # stream the library launches on); with --cold each is preceded by the flush too.
+    n_mark = max(1, args.marked_steps)
+    fev = [[mk() for _ in range(hga.HGA_FWD_EVENTS)] for _ in range(n_mark)]
+    bev = [[mk() for _ in range(2 * n_bwd)] for _ in range(n_mark)]
+    for i in range(n_mark):
+        if args.cold:
+            flush.fill_(i & 255)
+        step(fev[i], bev[i])
+    torch.cuda.synchronize()
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
-    kern_ms = {
-        "summaries": avg((ev[i][0], ev[i][1]) for i in marked),
-        "route": avg((ev[i][1], ev[i][2]) for i in marked),
-        "attend_fwd": avg((ev[i][2], ev[i][3]) for i in marked),
-    }
+    kern_ms = {"summaries": avg((e[0], e[1]) for e in fev),
+               "route_attend": avg((e[2], e[3]) for e in fev)}
     if L.do is not None:
         for k, name in enumerate(("attend_bwd_dq", "attend_bwd_order", "attend_bwd_dkdv", "attend_bwd_finalize")):
-            kern_ms[name] = avg((bev[i][2 * k], bev[i][2 * k + 1]) for i in marked)
+            kern_ms[name] = avg((e[2 * k], e[2 * k + 1]) for e in bev)
 
     gidx = L.gidx.cpu().numpy()
     work = algorithmic_work(w, gidx)
@@ -811,7 +822,6 @@ def main():
                     "frac": round(ach / HBM_PEAK_GBS, 4)}
     roofline["traffic"] = measured_traffic(dom, w.name) if args.routing == "block" and not args.cold else None
     roofline["kernel"] = dom
-    achievable = None if args.no_calibration else achievable_rates()
     if achievable is not None:
         roofline["frac_of_achievable"] = round(
             ach / (achievable["hbm_copy_GBps"] if roofline["bound"] == "hbm" else achievable["bf16_gemm_TFLOPs"]), 4)
@@ -831,8 +841,9 @@ def main():
         "roofline": roofline,
         "achievable": achievable,
         "kernels": kernels,
-        "kernel_timing": f"HIP events on {len(marked)} of the {args.steps} timed steps; backward kernels "
-                         f"timed from their dispatches, the other calls between events on the stream",
+        "kernel_timing": f"every kernel timed from its own dispatch (HIP events recorded by the launch) in "
+                         f"{n_mark} steps run after the timed region",
+        "kernel_sum_ms": round(sum(kern_ms.values()), 5),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_prev_np)

@@ -170,6 +170,33 @@ int hga_attend_fwd(const hga_shape* shape, const void* q, const void* k_cache,
                    const void* v_cache, int64_t t_cap, int64_t t_hist, int64_t seg_len,
                    const int32_t* group_idx, void* o, float* lse, void* stream);
 
+/*
+ * hga_forward -- the forward of one segment in one call: the summaries of the
+ * active segment's chunks (as hga_build_summaries over [t_hist, t_hist + seg_len)),
+ * then the routing of every query block (as hga_route) and the attention (as
+ * hga_attend_fwd).  With bf16 and 4 query heads per KV head the routing and the
+ * attention of a (sequence, KV head, query block) run in one work-group: the query
+ * rows are read once for both, and the selection feeds the K/V gather from on-chip
+ * memory; other shapes run the two kernels of hga_route and hga_attend_fwd.
+ * Outputs equal those of the three separate calls (bit for bit).
+ *
+ *   q, k_cache, v_cache, t_cap, t_hist, seg_len: as hga_attend_fwd; the history's
+ *              summaries (chunks below t_hist / 64) must already be built
+ *   chunk_sum, group_sum: read, and written for the active segment's chunks
+ *   chunk_idx, group_idx, o, lse: written, as hga_route and hga_attend_fwd
+ *   events     NULL, or HGA_FWD_EVENTS hipEvent_t handles created by the caller
+ *              (NULL entries skipped), recorded by the dispatches themselves:
+ *              [0] / [1] at the start / end of the summaries kernel, [2] / [3] at
+ *              the start of the routing and the end of the attention.
+ * Requirements and errors as hga_route (chunk_idx and group_idx may not be NULL
+ * while k_c resp. k_g is positive).
+ */
+#define HGA_FWD_EVENTS 4
+int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                void* chunk_sum, void* group_sum, int64_t t_cap, int64_t t_hist, int64_t seg_len,
+                int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse, void* const* events,
+                void* stream);
+
 /* Bytes of device workspace hga_attend_bwd needs (16-byte aligned); 0 on bad shape. */
 size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len);
 

@@ -97,6 +97,7 @@ SIGNATURES = {
     "hga_route": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "hga_route_causal": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "hga_attend_fwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "hga_forward": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "hga_attend_bwd_workspace_size": (ctypes.c_size_t, [_SHAPE, _I64, _I64]),
     "hga_attend_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                       _P, ctypes.c_size_t, _P]),
@@ -240,6 +241,36 @@ def hga_attend_fwd(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_ca
         _ptr(group_idx), _ptr(o), _ptr(lse), _stream(stream)))
 
 
+HGA_FWD_EVENTS = 4
+
+
+def _event_handles(events, n, stream):
+    """ctypes array of n HIP event handles from torch.cuda.Event objects (None
+    entries stay NULL); torch creates an event's HIP handle on its first record."""
+    if len(events) != n:
+        raise ValueError(f"need {n} events, got {len(events)}")
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record(stream if stream is not None else torch.cuda.current_stream())
+    return (ctypes.c_void_p * n)(*[None if e is None else ctypes.c_void_p(e.cuda_event) for e in events])
+
+
+def hga_forward(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                chunk_sum: torch.Tensor, group_sum: torch.Tensor, t_cap: int, t_hist: int, seg_len: int,
+                chunk_idx: Optional[torch.Tensor], group_idx: Optional[torch.Tensor], o: torch.Tensor,
+                lse: torch.Tensor, events=None, stream=None) -> None:
+    """Summaries of the active segment, routing and attention in one call (events:
+    None or HGA_FWD_EVENTS torch.cuda.Event / None entries, recorded by the dispatches)."""
+    fn = "hga_forward"
+    dev = _dev_of(q, k_cache, v_cache)
+    _route_checks(fn, shape, dev, q, chunk_sum, group_sum, t_cap, seg_len, chunk_idx, group_idx, None, None)
+    _attend_checks(fn, shape, dev, q, k_cache, v_cache, t_cap, seg_len, group_idx, o, lse)
+    handles = None if events is None else _event_handles(events, HGA_FWD_EVENTS, stream)
+    _check(fn, lib().hga_forward(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist,
+        seg_len, _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), handles, _stream(stream)))
+
+
 def hga_attend_bwd_workspace_size(shape: HgaShape, t_hist: int, seg_len: int) -> int:
     return int(lib().hga_attend_bwd_workspace_size(ctypes.byref(shape), t_hist, seg_len))
 
@@ -284,11 +315,7 @@ def hga_attend_bwd_timed(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_ca
     dev = _dev_of(q, k_cache, v_cache)
     _bwd_checks(fn, shape, dev, q, k_cache, v_cache, o, lse, d_o, t_cap, seg_len, group_idx, dq, dk_active,
                 dv_active, workspace)
-    for e in events:
-        if e is not None and not e.cuda_event:
-            e.record(stream if stream is not None else torch.cuda.current_stream())  # creates it
-    handles = (ctypes.c_void_p * (2 * HGA_BWD_KERNELS))(
-        *[None if e is None else ctypes.c_void_p(e.cuda_event) for e in events])
+    handles = _event_handles(events, 2 * HGA_BWD_KERNELS, stream)
     _check(fn, lib().hga_attend_bwd_timed(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(d_o),
         t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(dq), _ptr(dk_active), _ptr(dv_active),

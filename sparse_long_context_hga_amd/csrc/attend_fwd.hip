@@ -17,9 +17,14 @@
 //     and 32 of the 64 keys, so the online-softmax statistics live in the lane;
 //   * O^T += V^T P^T: P (bf16) is already in operand-B layout thanks to rho, and
 //     V^T comes from the row-major tile through ds_read_b64_tr_b16.
+// The same attention also runs right after the routing of the unit in one
+// work-group (route_attend_bf16_kernel, 4 query heads per KV head): the query rows
+// are loaded once for both, and the selection goes from LDS to the tile copies
+// without a round trip through memory or a kernel boundary.
 // fp32 path: one thread per query row, plain fp32 loops (exact-precision mode).
 #include "hga_device.h"
 #include "hga_internal.h"
+#include "route_phase.h"
 
 #include <math.h>
 
@@ -40,38 +45,24 @@ struct FwdArgs {
   float scale;
 };
 
-// HPW query heads of the G sharing a KV head per work-group (2 waves of 32 rows each);
-// the G / HPW work-groups of a unit gather the same tiles (the repeats hit L2: their
-// ids are consecutive, hence on one XCD) but run unsynchronised, so one group's
-// softmax overlaps another's MFMAs on the same CU.
-template <int D, int G, int HPW>
-__global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) void attend_fwd_bf16_kernel(FwdArgs a) {
+// Attention of this work-group's HPW query heads of unit `unit` (head offset
+// sub * HPW within the KV group) over the selected groups sgid[0 .. n_valid)
+// (ascending, in LDS) plus the own chunk; qf: the lane's query row fragments (row
+// n of the wave's 32).  KB(B) / VB(B) give the K / V tile buffer set B (distinct
+// LDS arrays); sets 0 and 1 also serve as the waves' output regions at the end.
+template <int D, int G, int HPW, int NSTAGE, typename KBuf, typename VBuf>
+__device__ __forceinline__ void attend_unit_bf16(const FwdArgs& a, int unit, int sub, const bf16x8 (&qf)[D / 16],
+                                                 const int* sgid, int n_valid, const KBuf& KB, const VBuf& VB) {
   constexpr int NW = 2 * HPW;
-  constexpr int kStagesHere = HPW == G ? kStages : 2;
   constexpr int KS = D / 16;       // k-steps over the head dimension
   constexpr int DT = D / 32;       // 32-wide column tiles of O^T
-  // Tile buffer sets as distinct arrays: the compiler can then see that reads of one
-  // never alias the asynchronous copies into another.
-  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
-  __shared__ __align__(16) uint16_t k2[64 * D], v2[64 * D], k3[64 * D], v3[64 * D];
-  auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (B() == 0) return k0; else if constexpr (B() == 1) return k1;
-    else if constexpr (B() == 2) return k2; else return k3;
-  };
-  auto VB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (B() == 0) return v0; else if constexpr (B() == 1) return v1;
-    else if constexpr (B() == 2) return v2; else return v3;
-  };
-
-  const int item = xcd_unit(blockIdx.x, gridDim.x);
-  if (item >= a.n_units * (G / HPW)) return;
-  const int unit = item / (G / HPW);
+  (void)KS;
   const int j = unit % a.nb;
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int J = (int)(a.t_hist / kChunk) + j;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
-  const int hh = (item % (G / HPW)) * HPW + (w >> 1);   // query head within the KV group
+  const int hh = sub * HPW + (w >> 1);    // query head within the KV group
   const int pos = 32 * (w & 1) + n;       // this lane's query position in the block
   // First row of this wave's 32 (wave-uniform) and this lane's row.
   const int64_t qrow0 = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + 32 * (w & 1);
@@ -82,22 +73,10 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
   // 32-row LDS region of wave wv in the first two tile buffer sets (for O after the
   // last tile).
   auto row_region = [&](int wv) __attribute__((always_inline)) -> uint16_t* {
-    uint16_t* base = (wv >> 1) == 0 ? k0 : (wv >> 1) == 1 ? v0 : (wv >> 1) == 2 ? k1 : v1;
+    uint16_t* base = (wv >> 1) == 0 ? KB(ic<0>{}) : (wv >> 1) == 1 ? VB(ic<0>{}) : (wv >> 1) == 2 ? KB(ic<1>{})
+                                                                                                : VB(ic<1>{});
     return base + (wv & 1) * 32 * D;
   };
-
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + qrow * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
-  }
-
-  // The group list (k_g <= 512) goes to LDS once; its valid entries (ascending, -1
-  // only trails) are counted on the way.
-  __shared__ int sgid[512];
-  const int n_valid = __builtin_amdgcn_readfirstlane(
-      count_valid<128 * HPW>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
 
@@ -222,7 +201,7 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
     });
   };
 
-  pipeline<kStagesHere, 2 * BPW>(n_tiles, issue, compute);
+  pipeline<NSTAGE, 2 * BPW>(n_tiles, issue, compute);
 
   // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
   // O leaves through this wave's 32-row LDS region as whole rows; the barrier keeps
@@ -235,6 +214,87 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
                                 oacc[dt][4 * g + 3] * inv);
   });
   if (h == 0) a.lse[qrow] = (m2 + log2f(ltot)) * kLn2;
+}
+
+// HPW query heads of the G sharing a KV head per work-group (2 waves of 32 rows each);
+// the G / HPW work-groups of a unit gather the same tiles (the repeats hit L2: their
+// ids are consecutive, hence on one XCD) but run unsynchronised, so one group's
+// softmax overlaps another's MFMAs on the same CU.
+template <int D, int G, int HPW>
+__global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) void attend_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int kStagesHere = HPW == G ? kStages : 2;
+  constexpr int KS = D / 16;       // k-steps over the head dimension
+  // Tile buffer sets as distinct arrays: the compiler can then see that reads of one
+  // never alias the asynchronous copies into another.
+  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
+  __shared__ __align__(16) uint16_t k2[64 * D], v2[64 * D], k3[64 * D], v3[64 * D];
+  __shared__ int sgid[512];
+  auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return k0; else if constexpr (B() == 1) return k1;
+    else if constexpr (B() == 2) return k2; else return k3;
+  };
+  auto VB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return v0; else if constexpr (B() == 1) return v1;
+    else if constexpr (B() == 2) return v2; else return v3;
+  };
+
+  const int item = xcd_unit(blockIdx.x, gridDim.x);
+  if (item >= a.n_units * (G / HPW)) return;
+  const int unit = item / (G / HPW);
+  const int j = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int w = threadIdx.x >> 6, h = (threadIdx.x & 63) >> 5, n = threadIdx.x & 31;
+  const int hh = (item % (G / HPW)) * HPW + (w >> 1);   // query head within the KV group
+  const int64_t qrow = (((int64_t)b * a.Hq + kvh * G + hh) * a.seg_len) + (int64_t)j * kQBlock + 32 * (w & 1) + n;
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + qrow * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+  }
+
+  // The group list (k_g <= 512) goes to LDS once; its valid entries (ascending, -1
+  // only trails) are counted on the way.
+  const int n_valid = __builtin_amdgcn_readfirstlane(
+      count_valid<128 * HPW>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
+  attend_unit_bf16<D, G, HPW, kStagesHere>(a, unit, item % (G / HPW), qf, sgid, n_valid, KB, VB);
+}
+
+// Route, then attend, in one work-group per unit (4 query heads per KV head: 8
+// waves).  The routing waves hold row tiles {w % 4, w % 4 + 4}; wave w attends with
+// row tile w, one of the two, so the query rows are read once for both phases.  The
+// summary batch buffers of the routing are the attention's tile buffer sets 0 and 1.
+template <int D>
+__global__ __launch_bounds__(512, 1) void route_attend_bf16_kernel(RouteArgs ra, FwdArgs a) {
+  constexpr int G = 4;
+  constexpr int KS = D / 16;
+  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
+  __shared__ RouteShared<route_threads<G>()> sm;
+  __shared__ int sgid[512];
+  auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return k0; else return k1;
+  };
+  auto VB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (B() == 0) return v0; else return v1;
+  };
+  auto tile = [&](auto B, auto T) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (T() == 0) return KB(B); else return VB(B);
+  };
+  const int unit = xcd_unit(blockIdx.x, gridDim.x);
+  if (unit >= a.n_units) return;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  bf16x8 qr[route_row_tiles_per_wave<G>()][KS];
+  int nc, ng;
+  route_unit_bf16<D, G>(ra, unit, tile, sm, qr, nc, ng);
+  // The selected groups as ids (ascending), for the tile copies.
+  for (int i = tid; i < ng; i += 512) sgid[i] = 8 * sm.csel[sm.gsel[i] >> 3] + (sm.gsel[i] & 7);
+  __syncthreads();
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = w < 4 ? qr[0][ks] : qr[1][ks];
+  attend_unit_bf16<D, G, G, kStages>(a, unit, 0, qf, sgid, __builtin_amdgcn_readfirstlane(ng), KB, VB);
 }
 
 // ---------------------------------------------------------------- fp32 (SIMT)
@@ -285,34 +345,68 @@ __global__ __launch_bounds__(512) void attend_fwd_f32_kernel(FwdArgs a, int G) {
 }
 
 template <int D, int G>
-hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per work-group
-  return launch_kernel(attend_fwd_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))), dim3(128 * HPW),
-                       s, a);
+  return launch_kernel_timed(attend_fwd_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))),
+                             dim3(128 * HPW), s, start, stop, a);
 }
 template <int D>
-hipError_t launch_bf16_g(const FwdArgs& a, int G, hipStream_t s) {
+hipError_t launch_bf16_g(const FwdArgs& a, int G, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   switch (G) {
-    case 1: return launch_bf16<D, 1>(a, s);
-    case 2: return launch_bf16<D, 2>(a, s);
-    case 4: return launch_bf16<D, 4>(a, s);
-    default: return launch_bf16<D, 8>(a, s);
+    case 1: return launch_bf16<D, 1>(a, s, start, stop);
+    case 2: return launch_bf16<D, 2>(a, s, start, stop);
+    case 4: return launch_bf16<D, 4>(a, s, start, stop);
+    default: return launch_bf16<D, 8>(a, s, start, stop);
   }
 }
 
-}  // namespace
-
-hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
-                             const int32_t* group_idx, void* o, float* lse, hipStream_t s) {
+FwdArgs fwd_args(const Dims& d, const void* q, const void* k, const void* v, const int32_t* group_idx, void* o,
+                 float* lse) {
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.gidx = group_idx; a.o = o; a.lse = lse;
   a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.kg = d.kg; a.nb = d.nb; a.n_units = d.B * d.Hkv * d.nb;
   a.scale = d.scale;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
+                             const int32_t* group_idx, void* o, float* lse, hipStream_t s, hipEvent_t start,
+                             hipEvent_t stop) {
+  const FwdArgs a = fwd_args(d, q, k, v, group_idx, o, lse);
   const int grid = xcd_grid(a.n_units);
-  if (bf16) return d.D == 128 ? launch_bf16_g<128>(a, d.G, s) : launch_bf16_g<64>(a, d.G, s);
-  return d.D == 128 ? launch_kernel(attend_fwd_f32_kernel<128>, dim3(grid), dim3(64 * d.G), s, a, d.G)
-                    : launch_kernel(attend_fwd_f32_kernel<64>, dim3(grid), dim3(64 * d.G), s, a, d.G);
+  if (bf16) return d.D == 128 ? launch_bf16_g<128>(a, d.G, s, start, stop) : launch_bf16_g<64>(a, d.G, s, start, stop);
+  return d.D == 128
+             ? launch_kernel_timed(attend_fwd_f32_kernel<128>, dim3(grid), dim3(64 * d.G), s, start, stop, a, d.G)
+             : launch_kernel_timed(attend_fwd_f32_kernel<64>, dim3(grid), dim3(64 * d.G), s, start, stop, a, d.G);
+}
+
+hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* k, const void* v, void* chunk_sum,
+                          void* group_sum, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
+                          hipStream_t s, const hipEvent_t* ev) {
+  const hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  const hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+  hipError_t e = launch_summaries(d, bf16, k, d.t_hist, d.t_hist + d.seg_len, group_sum, chunk_sum, s, e0, e1);
+  if (e != hipSuccess) return e;
+  if (!(bf16 && d.G == 4)) {
+    e = launch_route(d, bf16, q, nullptr, false, chunk_sum, group_sum, chunk_idx, group_idx, nullptr, nullptr, s,
+                     e2, nullptr);
+    if (e != hipSuccess) return e;
+    return launch_attend_fwd(d, bf16, q, k, v, group_idx, o, lse, s, nullptr, e3);
+  }
+  RouteArgs ra;
+  ra.q = q; ra.q_prev = nullptr; ra.lag = 0;
+  ra.csum = chunk_sum; ra.gsum = group_sum;
+  ra.cidx = chunk_idx; ra.gidx = group_idx; ra.cscore = nullptr; ra.gscore = nullptr;
+  ra.t_cap = d.t_cap; ra.t_hist = d.t_hist; ra.seg_len = d.seg_len;
+  ra.Hq = d.Hq; ra.Hkv = d.Hkv; ra.kc = d.kc; ra.kg = d.kg; ra.nb = d.nb;
+  ra.n_units = d.B * d.Hkv * d.nb;
+  const FwdArgs a = fwd_args(d, q, k, v, group_idx, o, lse);
+  const dim3 grid(xcd_grid(a.n_units));
+  return d.D == 128 ? launch_kernel_timed(route_attend_bf16_kernel<128>, grid, dim3(512), s, e2, e3, ra, a)
+                    : launch_kernel_timed(route_attend_bf16_kernel<64>, grid, dim3(512), s, e2, e3, ra, a);
 }
 
 }  // namespace hga

@@ -118,6 +118,26 @@ int hga_attend_fwd(const hga_shape* shape, const void* q, const void* k_cache, c
                                            lse, (hipStream_t)stream));
 }
 
+int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache, void* chunk_sum,
+                void* group_sum, int64_t t_cap, int64_t t_hist, int64_t seg_len, int32_t* chunk_idx,
+                int32_t* group_idx, void* o, float* lse, void* const* events, void* stream) {
+  hga::Dims d;
+  int st = resolve(shape, t_cap, t_hist, seg_len, d);
+  if (st != HGA_OK) return st;
+  if (seg_len == 0) return HGA_ERR_SHAPE;
+  if ((t_hist + seg_len) / 64 > HGA_MAX_CHUNKS) return HGA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !chunk_sum || !group_sum || !o || !lse || (d.kc > 0 && !chunk_idx) ||
+      (d.kg > 0 && !group_idx))
+    return HGA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(chunk_sum) ||
+      !aligned16(group_sum) || !aligned16(o) || !aligned16(lse) || (chunk_idx && !aligned16(chunk_idx)) ||
+      (group_idx && !aligned16(group_idx)))
+    return HGA_ERR_ALIGN;
+  return hip_status(hga::launch_forward(d, shape->dtype == HGA_BF16, q, k_cache, v_cache, chunk_sum, group_sum,
+                                        chunk_idx, group_idx, o, lse, (hipStream_t)stream,
+                                        (const hipEvent_t*)events));
+}
+
 size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len) {
   hga::Dims d;
   if (resolve(shape, t_hist + seg_len > 0 ? t_hist + seg_len : 64, t_hist, seg_len, d) != HGA_OK) return 0;

@@ -35,16 +35,29 @@ struct Dims {
   float scale;   // softmax scale
 };
 
+// Optional start / stop events are recorded by the dispatches themselves.
 hipError_t launch_summaries(const Dims& d, bool bf16, const void* k, int64_t t_begin, int64_t t_end,
-                            void* group_sum, void* chunk_sum, hipStream_t s);
+                            void* group_sum, void* chunk_sum, hipStream_t s, hipEvent_t start = nullptr,
+                            hipEvent_t stop = nullptr);
 
 // causal: block j is routed by the rows of block j-1 (q_prev [B,Hq,64,d] for j = 0).
 hipError_t launch_route(const Dims& d, bool bf16, const void* q, const void* q_prev, bool causal,
                         const void* chunk_sum, const void* group_sum, int32_t* chunk_idx,
-                        int32_t* group_idx, float* chunk_score, float* group_score, hipStream_t s);
+                        int32_t* group_idx, float* chunk_score, float* group_score, hipStream_t s,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void* k, const void* v,
-                             const int32_t* group_idx, void* o, float* lse, hipStream_t s);
+                             const int32_t* group_idx, void* o, float* lse, hipStream_t s, hipEvent_t start = nullptr,
+                             hipEvent_t stop = nullptr);
+
+// The forward of a segment: summaries of the active segment [t_hist, t_hist +
+// seg_len), then routing and attention (one kernel that does both per unit for
+// bf16 with 4 query heads per KV head, else the route and attention kernels).
+// ev: null, or 4 events: [0], [1] around the summaries, [2] at the start of the
+// routing and [3] at the end of the attention.
+hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* k, const void* v, void* chunk_sum,
+                          void* group_sum, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
+                          hipStream_t s, const hipEvent_t* ev);
 
 // Workspace: one float per query row (rowsum(dO * O)).
 size_t bwd_workspace_bytes(const Dims& d);

@@ -84,24 +84,24 @@ __global__ __launch_bounds__(2 * D) void summaries_kernel(const T* __restrict__ 
 
 template <typename T, int D>
 hipError_t launch_t(const Dims& d, const void* k, int64_t t_begin, int64_t t_end, void* gs, void* cs,
-                    hipStream_t s) {
+                    hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int64_t nch = (t_end - t_begin) / kChunk;
   if (nch == 0) return hipSuccess;
   dim3 grid((unsigned)nch, (unsigned)d.Hkv, (unsigned)d.B);
-  return launch_kernel(summaries_kernel<T, D>, grid, dim3(2 * D), s, (const T*)k, d.t_cap, t_begin / kChunk,
-                       (T*)gs, (T*)cs);
+  return launch_kernel_timed(summaries_kernel<T, D>, grid, dim3(2 * D), s, start, stop, (const T*)k, d.t_cap,
+                             t_begin / kChunk, (T*)gs, (T*)cs);
 }
 
 }  // namespace
 
 hipError_t launch_summaries(const Dims& d, bool bf16, const void* k, int64_t t_begin, int64_t t_end,
-                            void* gs, void* cs, hipStream_t s) {
+                            void* gs, void* cs, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   if (bf16) {
-    return d.D == 128 ? launch_t<uint16_t, 128>(d, k, t_begin, t_end, gs, cs, s)
-                      : launch_t<uint16_t, 64>(d, k, t_begin, t_end, gs, cs, s);
+    return d.D == 128 ? launch_t<uint16_t, 128>(d, k, t_begin, t_end, gs, cs, s, start, stop)
+                      : launch_t<uint16_t, 64>(d, k, t_begin, t_end, gs, cs, s, start, stop);
   }
-  return d.D == 128 ? launch_t<float, 128>(d, k, t_begin, t_end, gs, cs, s)
-                    : launch_t<float, 64>(d, k, t_begin, t_end, gs, cs, s);
+  return d.D == 128 ? launch_t<float, 128>(d, k, t_begin, t_end, gs, cs, s, start, stop)
+                    : launch_t<float, 64>(d, k, t_begin, t_end, gs, cs, s, start, stop);
 }
 
 }  // namespace hga

@@ -90,6 +90,12 @@ class HGALayerBuffers:
         L.hga_attend_fwd(self.shape, self.q, self.k, self.v, self.t_cap, self.t_hist, self.seg_len,
                          self.gidx if gidx is None else gidx, self.o, self.lse)
 
+    def forward(self, events=None):
+        """Summaries of the active segment, routing and attention in one call
+        (hga_forward); events: None or HGA_FWD_EVENTS torch.cuda.Event entries."""
+        L.hga_forward(self.shape, self.q, self.k, self.v, self.csum, self.gsum, self.t_cap, self.t_hist,
+                      self.seg_len, self.cidx, self.gidx, self.o, self.lse, events)
+
     def bwd(self, gidx: Optional[torch.Tensor] = None, events=None):
         g = self.gidx if gidx is None else gidx
         if events is None:
@@ -100,10 +106,9 @@ class HGALayerBuffers:
                                    self.t_hist, self.seg_len, g, self.dq, self.dk, self.dv, self.ws, events)
 
     def step(self):
-        """One pass of the hot path: active-segment summaries, route, forward, backward."""
-        self.summaries(self.t_hist, self.t_hist + self.seg_len)
-        self.route()
-        self.fwd()
+        """One pass of the hot path: active-segment summaries, route and forward
+        (hga_forward), then the backward."""
+        self.forward()
         if self.do is not None:
             self.bwd()
 
@@ -132,16 +137,18 @@ class HGAKVCache:
         self.q_last: Optional[torch.Tensor] = None      # [B, Hq, 64, d] of the committed history
         self._q_pending: Optional[torch.Tensor] = None
 
-    def write(self, k_seg: torch.Tensor, v_seg: torch.Tensor, shape: L.HgaShape) -> int:
-        """Place a segment's K/V at [length, length+S) and build its summaries.
-        Returns the position where it starts (the history length for the segment)."""
+    def write(self, k_seg: torch.Tensor, v_seg: torch.Tensor, shape: L.HgaShape, summaries: bool = True) -> int:
+        """Place a segment's K/V at [length, length+S) and build its summaries (unless
+        the caller builds them, as hga_forward does).  Returns the position where it
+        starts (the history length for the segment)."""
         S = k_seg.shape[2]
         t0 = self.length
         if t0 + S > self.t_cap:
             raise ValueError("KV cache capacity exceeded")
         self.k[:, :, t0:t0 + S].copy_(k_seg.detach())
         self.v[:, :, t0:t0 + S].copy_(v_seg.detach())
-        L.hga_build_summaries(shape, self.k, self.t_cap, t0, t0 + S, self.gsum, self.csum)
+        if summaries:
+            L.hga_build_summaries(shape, self.k, self.t_cap, t0, t0 + S, self.gsum, self.csum)
         return t0
 
     def keep_last_query_block(self, q: torch.Tensor):
@@ -192,19 +199,22 @@ class _HGAAttentionFn(torch.autograd.Function):
         if causal_routing and cache.length > 0 and (cache.q_last is None or cache.q_last.shape[1] != Hq):
             raise ValueError("causal routing over history needs the previous segment's last query block "
                              "(route every segment of the cache causally)")
-        t_hist = cache.write(k_seg, v_seg, shape)
         nb = S // 64
         cidx = torch.empty(B, cache.n_kv_heads, nb, top_chunks, dtype=torch.int32, device=q.device)
         gidx = torch.empty(B, cache.n_kv_heads, nb, top_groups, dtype=torch.int32, device=q.device)
-        if causal_routing:
-            L.hga_route_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.csum, cache.gsum,
-                               cache.t_cap, t_hist, S, cidx, gidx)
-        else:
-            L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
-        cache.keep_last_query_block(q)
         o = torch.empty_like(q)
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
-        L.hga_attend_fwd(shape, q, cache.k, cache.v, cache.t_cap, t_hist, S, gidx, o, lse)
+        if causal_routing:
+            t_hist = cache.write(k_seg, v_seg, shape)
+            L.hga_route_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.csum, cache.gsum,
+                               cache.t_cap, t_hist, S, cidx, gidx)
+            L.hga_attend_fwd(shape, q, cache.k, cache.v, cache.t_cap, t_hist, S, gidx, o, lse)
+        else:
+            # summaries of the segment, routing and attention in one call
+            t_hist = cache.write(k_seg, v_seg, shape, summaries=False)
+            L.hga_forward(shape, q, cache.k, cache.v, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx,
+                          o, lse)
+        cache.keep_last_query_block(q)
         ctx.save_for_backward(q, o, lse, gidx)
         ctx.cache, ctx.shape, ctx.t_hist = cache, shape, t_hist
         ctx.mark_non_differentiable(lse, gidx)
