@@ -65,45 +65,6 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e)
 };
 
-// ------------------------------------------------ exchange between work-groups
-// Device-scope coherent stores and loads (relaxed atomics at agent scope).
-__device__ __forceinline__ void put(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t get(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t get(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival of a work-group at its unit's counter, after its put()s; true in the last
-// of the n that arrive.  Every wave waits for its stores to complete first, so a
-// work-group that sees the final count also sees every put() of the others.  The
-// last one resets the counter for the next launch.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, int n, int* flag) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  wait_dma();   // s_waitcnt vmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = old == (uint32_t)(n - 1);
-    if (*flag) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  return *flag != 0;
-}
-
 // 8 consecutive elements of a row (16 B of bf16, 32 B of fp32), widened to fp32.
 template <typename T> struct Vec8;
 template <> struct Vec8<uint16_t> {

@@ -63,6 +63,51 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Wait until every vector memory access issued by this wave has completed: loads,
+// stores and global->LDS copies (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ------------------------------------------------ exchange between work-groups
+// Values that a work-group of the same launch reads (possibly on another XCD, whose
+// L2 is not coherent with this one) are written and read with these.
+// Device-scope coherent stores and loads (relaxed atomics at agent scope).
+__device__ __forceinline__ void put(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival of a work-group at a counter, after its put()s; true in the last of the n
+// that arrive.  Every wave waits for its stores to complete first, so a work-group
+// that sees the final count also sees every put() of the others.  The last one
+// resets the counter for the next launch.  All threads of the work-group call it.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int n, int* flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_dma();   // s_waitcnt vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == (uint32_t)(n - 1);
+    if (*flag) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 // ------------------------------------------------------------ unit placement
 // Work-groups are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
 // Launch 8*ceil(n/8) blocks and renumber so that consecutive unit ids (which
@@ -367,8 +412,6 @@ __device__ __forceinline__ void store_rows32(uint16_t* region, uint16_t* dst, Va
   }
 }
 
-// Wait until every global->LDS copy issued by this wave has landed.
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
 // s_waitcnt lgkmcnt(0) alone: this wave's LDS accesses have completed.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }

@@ -214,7 +214,7 @@ def test_full_chain_and_determinism(chk, cases, name):
 @pytest.mark.parametrize("name", ["bf16_g4_d128_ragged", "f32_g4_d128"])
 def test_timed_backward_matches(chk, cases, name):
     """hga_attend_bwd_timed writes the same bits as hga_attend_bwd and records its
-    events in launch order (dQ, plan, dK/dV, finalize)."""
+    events in launch order (dQ, work list, dK/dV, partial sums)."""
     import sparse_long_context_hga_amd as hga
     w, _, _, _, gidx = cases[name]
     print(f"case {name}", flush=True)
@@ -240,3 +240,33 @@ def test_timed_backward_matches(chk, cases, name):
     for e0, e1 in zip(marks, marks[1:]):
         assert e0.elapsed_time(e1) >= 0.0
     assert ev[0].elapsed_time(ev[1]) > 0.0 and ev[4].elapsed_time(ev[5]) > 0.0
+
+
+def test_backward_workspace_reused_across_shapes(chk, cases):
+    """One workspace serves backward calls of different shapes in turn (everything in
+    it is written before it is read within a call): the results equal those of a
+    workspace of their own each time."""
+    import sparse_long_context_hga_amd as hga
+    names = ["bf16_g8_full_coverage", "bf16_g4_d128_ragged", "bf16_g8_full_coverage"]
+    layers = {}
+    need = 0
+    for name in set(names):
+        w, _, _, _, gidx = cases[name]
+        L = chk.DeviceLayer(w)
+        L.fwd(torch.from_numpy(gidx).cuda())
+        L.bwd(torch.from_numpy(gidx).cuda())          # reference, own fresh workspace
+        layers[name] = (L, torch.from_numpy(gidx).cuda())
+        need = max(need, L.ws.numel())
+    torch.cuda.synchronize()
+    ref = {n: [chk.to_np(t).copy() for t in (L.dq, L.dk, L.dv)] for n, (L, _) in layers.items()}
+    shared = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for name in names:
+        print(f"case {name} on the shared workspace", flush=True)
+        L, g = layers[name]
+        for t in (L.dq, L.dk, L.dv):
+            t.zero_()
+        hga.hga_attend_bwd(L.shape, L.q, L.k, L.v, L.o, L.lse, L.do, L.t_cap, L.t_hist, L.seg_len, g, L.dq, L.dk,
+                           L.dv, shared)
+        torch.cuda.synchronize()
+        for a, b_ in zip(ref[name], (L.dq, L.dk, L.dv)):
+            assert np.array_equal(a, chk.to_np(b_)), name
