@@ -252,6 +252,66 @@ def hga_attention(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cac
     return _HGAAttentionFn.apply(q, k_seg, v_seg, cache, top_chunks, top_groups, scale, causal_routing)
 
 
+class HGAStack:
+    """Segment-wise truncated backpropagation through a stack of HGA attention
+    layers, the pages' training scheme (adnankhan.ai note, "Raw Abstract /
+    Excerpt": only the active segment is differentiable, older K/V detached;
+    seventnews, "HGA的不同之处": 2,048-token segments, each with its own forward
+    and backward).  Every layer has its own K/V cache with summary tables.
+
+    layers[l] supplies the model around the attention of layer l:
+        qkv(h) -> (q [B,Hq,S,d], k [B,Hkv,S,d], v [B,Hkv,S,d])   differentiable
+        out(h, o) -> h_next                                       differentiable
+    run_segment(h, loss_fn) runs one segment: for each layer, qkv, routed attention
+    over that layer's cache (history) and the segment itself, out; then
+    loss_fn(h_last).backward(); then every cache commits the segment, whose K/V
+    become detached history for the next segment (no gradient ever reaches them).
+    budgets: one (top_chunks, top_groups) pair for every layer, or a list of them.
+    """
+
+    def __init__(self, layers, batch: int, n_kv_heads: int, head_dim: int, t_cap: int, budgets=(16, 64),
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", softmax_scale: Optional[float] = None,
+                 causal_routing: bool = False):
+        self.layers = list(layers)
+        n = len(self.layers)
+        if isinstance(budgets[0], (tuple, list)):
+            if len(budgets) != n:
+                raise ValueError(f"{len(budgets)} budgets for {n} layers")
+            self.budgets = [tuple(b) for b in budgets]
+        else:
+            self.budgets = [tuple(budgets)] * n
+        self.caches = [HGAKVCache(batch, n_kv_heads, head_dim, t_cap, dtype, device) for _ in range(n)]
+        self.softmax_scale = softmax_scale
+        self.causal_routing = causal_routing
+        self.segments = 0
+
+    @property
+    def length(self) -> int:
+        """Tokens already committed as history."""
+        return self.caches[0].length if self.caches else 0
+
+    def run_segment(self, h, loss_fn):
+        """Forward, backward and detach of one segment.  Returns (loss value, and per
+        layer (o, lse, group_idx) of the segment, detached)."""
+        outs = []
+        seg_len = None
+        for layer, cache, (kc, kg) in zip(self.layers, self.caches, self.budgets):
+            q, k, v = layer.qkv(h)
+            if seg_len is None:
+                seg_len = q.shape[2]
+            elif q.shape[2] != seg_len:
+                raise ValueError("every layer must see the same segment length")
+            o, lse, gidx = hga_attention(q, k, v, cache, kc, kg, self.softmax_scale, self.causal_routing)
+            outs.append((o.detach(), lse, gidx))
+            h = layer.out(h, o)
+        loss = loss_fn(h)
+        loss.backward()
+        for cache in self.caches:
+            cache.commit(seg_len)
+        self.segments += 1
+        return loss.detach(), outs
+
+
 class HGADecoder:
     """Generation steps over `cache`: every sequence adds one token per step.
 

@@ -76,3 +76,12 @@ def test_decoder_step_rejects_mismatches():
         dec.step(torch.zeros(2, 4, 64, dtype=torch.bfloat16), kv[:1], kv, pos)
     with pytest.raises(ValueError, match="pos"):
         dec.step(torch.zeros(2, 4, 64, dtype=torch.bfloat16), kv, kv, pos.long())
+
+
+def test_stack_checks_budgets():
+    from sparse_long_context_hga_amd.layer import HGAStack
+    layers = [object(), object()]
+    with pytest.raises(ValueError, match="budgets"):
+        HGAStack(layers, batch=1, n_kv_heads=1, head_dim=64, t_cap=256, budgets=[(2, 8)], device="cpu")
+    st = HGAStack(layers, batch=1, n_kv_heads=1, head_dim=64, t_cap=256, budgets=(2, 8), device="cpu")
+    assert st.budgets == [(2, 8), (2, 8)] and st.length == 0 and len(st.caches) == 2
