@@ -197,6 +197,43 @@ int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, cons
                 int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse, void* const* events,
                 void* stream);
 
+/*
+ * Host-RAM history tier.  The pages keep older K/V in RAM or on NVMe and bring
+ * only what the routing selects (adnankhan.ai note, "Raw Abstract / Excerpt";
+ * seventnews, "HGA的不同之处").  With this tier the detached history's K/V live in
+ * pinned host memory, the summary tables stay in HBM (routing reads only them),
+ * and after hga_route this call copies the selected history groups of every
+ * (sequence, KV head) into a compact staging cache in HBM and renumbers the
+ * selection for it; hga_attend_fwd / hga_attend_bwd then run on the staging cache
+ * unchanged, with results bit-identical to the same calls on a cache that holds
+ * the whole history in HBM.
+ *
+ *   k_host, v_host   [B, Hkv, host_t_cap, d] pinned host memory (hipHostMalloc, or
+ *                    a pinned torch tensor) holding the history at [0, t_hist); read
+ *                    by the GPU over the host link (HGA_ERR_UNSUPPORTED if not pinned)
+ *   group_idx        [B, Hkv, seg_len/64, k_g] int32, as hga_route wrote it       read
+ *   k_stage, v_stage [B, Hkv, stage_cap, d] device memory.  Written: rows [0, stage_hist):
+ *                    slot s = the s-th distinct history group that any block of the
+ *                    (sequence, KV head) selected (ascending ids), tokens 8s .. 8s+7;
+ *                    rows of unused slots are not touched.  The caller places the
+ *                    active segment's K/V at [stage_hist, stage_hist + seg_len).
+ *   group_idx_stage  [B, Hkv, seg_len/64, k_g] int32 written: history id x -> its slot,
+ *                    active id x -> stage_hist/8 + (x - t_hist/8), -1 -> -1; still
+ *                    ascending.  Pass it, stage_cap as t_cap and stage_hist as t_hist
+ *                    to hga_attend_fwd / hga_attend_bwd.
+ *   stage_hist       a multiple of 64 of at least hga_stage_history_min() (enough for
+ *                    every possible selection); stage_hist + seg_len <= stage_cap
+ *                    (HGA_ERR_CAPACITY otherwise).
+ * With k_g == 0 nothing is selected and the call does nothing.
+ */
+int hga_stage_history(const hga_shape* shape, const void* k_host, const void* v_host, int64_t host_t_cap,
+                      int64_t t_hist, int64_t seg_len, const int32_t* group_idx, void* k_stage,
+                      void* v_stage, int64_t stage_cap, int64_t stage_hist, int32_t* group_idx_stage,
+                      void* stream);
+/* Smallest valid stage_hist for hga_stage_history: min(t_hist, 8 * seg_len/64 * k_g)
+ * rounded up to a multiple of 64 (-1 on a bad shape). */
+int64_t hga_stage_history_min(const hga_shape* shape, int64_t t_hist, int64_t seg_len);
+
 /* Bytes of device workspace hga_attend_bwd needs (16-byte aligned); 0 on bad shape. */
 size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len);
 

@@ -98,6 +98,8 @@ SIGNATURES = {
     "hga_route_causal": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "hga_attend_fwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "hga_forward": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "hga_stage_history": (ctypes.c_int, [_SHAPE, _P, _P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P]),
+    "hga_stage_history_min": (ctypes.c_int64, [_SHAPE, _I64, _I64]),
     "hga_attend_bwd_workspace_size": (ctypes.c_size_t, [_SHAPE, _I64, _I64]),
     "hga_attend_bwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                       _P, ctypes.c_size_t, _P]),
@@ -269,6 +271,33 @@ def hga_forward(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     _check(fn, lib().hga_forward(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist,
         seg_len, _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), handles, _stream(stream)))
+
+
+def hga_stage_history_min(shape: HgaShape, t_hist: int, seg_len: int) -> int:
+    return int(lib().hga_stage_history_min(ctypes.byref(shape), t_hist, seg_len))
+
+
+def hga_stage_history(shape: HgaShape, k_host: torch.Tensor, v_host: torch.Tensor, host_t_cap: int, t_hist: int,
+                      seg_len: int, group_idx: torch.Tensor, k_stage: torch.Tensor, v_stage: torch.Tensor,
+                      stage_cap: int, stage_hist: int, group_idx_stage: torch.Tensor, stream=None) -> None:
+    """Copy the selected history groups from pinned host memory into the staging cache
+    and renumber the selection for it (the host-RAM history tier)."""
+    fn = "hga_stage_history"
+    dev = _dev_of(k_stage, v_stage)
+    B, _, Hkv, d = _dims(shape)
+    ft = _float_dtype(shape)
+    for name, t in (("k_host", k_host), ("v_host", v_host)):
+        _need(fn, name, t, ft, B * Hkv * host_t_cap * d, None)
+        if t.device.type != "cpu" or not t.is_pinned():
+            raise ValueError(f"{fn}: {name} must be pinned host memory")
+    _need(fn, "k_stage", k_stage, ft, B * Hkv * stage_cap * d, dev)
+    _need(fn, "v_stage", v_stage, ft, B * Hkv * stage_cap * d, dev)
+    n_ids = B * Hkv * (seg_len // 64) * shape.top_groups
+    _need(fn, "group_idx", group_idx, _I32, n_ids, dev, optional=shape.top_groups == 0)
+    _need(fn, "group_idx_stage", group_idx_stage, _I32, n_ids, dev, optional=shape.top_groups == 0)
+    _check(fn, lib().hga_stage_history(
+        ctypes.byref(shape), _ptr(k_host), _ptr(v_host), host_t_cap, t_hist, seg_len, _ptr(group_idx), _ptr(k_stage),
+        _ptr(v_stage), stage_cap, stage_hist, _ptr(group_idx_stage), _stream(stream)))
 
 
 def hga_attend_bwd_workspace_size(shape: HgaShape, t_hist: int, seg_len: int) -> int:

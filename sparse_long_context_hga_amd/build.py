@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhga.so")
 SOURCES = ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "decode.hip", "noalloc.hip",
-           "hga_api.cpp"]
+           "stage.hip", "hga_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -138,6 +138,44 @@ int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, cons
                                         (const hipEvent_t*)events));
 }
 
+int64_t hga_stage_history_min(const hga_shape* shape, int64_t t_hist, int64_t seg_len) {
+  hga::Dims d;
+  if (resolve(shape, t_hist + seg_len > 0 ? t_hist + seg_len : 64, t_hist, seg_len, d) != HGA_OK) return -1;
+  const int64_t sel = (int64_t)8 * d.nb * d.kg;                 // at most this many selected history tokens
+  const int64_t need = t_hist < sel ? t_hist : sel;
+  return (need + 63) / 64 * 64;
+}
+
+int hga_stage_history(const hga_shape* shape, const void* k_host, const void* v_host, int64_t host_t_cap,
+                      int64_t t_hist, int64_t seg_len, const int32_t* group_idx, void* k_stage, void* v_stage,
+                      int64_t stage_cap, int64_t stage_hist, int32_t* group_idx_stage, void* stream) {
+  // (k_host / v_host: pinned host memory; the kernel reads it through its device mapping)
+  hga::Dims d;
+  int st = resolve(shape, t_hist + seg_len > 0 ? t_hist + seg_len : 64, t_hist, seg_len, d);
+  if (st != HGA_OK) return st;
+  if (seg_len == 0) return HGA_ERR_SHAPE;
+  if (host_t_cap < t_hist || host_t_cap % 64 != 0 || stage_cap % 64 != 0 || stage_hist % 64 != 0 ||
+      stage_hist < 0)
+    return HGA_ERR_SHAPE;
+  if (t_hist / 8 > (int64_t)HGA_MAX_CHUNKS * 8 || (t_hist + seg_len) / 64 > HGA_MAX_CHUNKS)
+    return HGA_ERR_UNSUPPORTED;
+  if (stage_hist < hga_stage_history_min(shape, t_hist, seg_len) || stage_hist + seg_len > stage_cap)
+    return HGA_ERR_CAPACITY;
+  if (d.kg == 0) return HGA_OK;   // nothing selected, nothing to stage or renumber
+  if (!k_host || !v_host || !group_idx || !k_stage || !v_stage || !group_idx_stage) return HGA_ERR_NULL;
+  if (!aligned16(k_host) || !aligned16(v_host) || !aligned16(group_idx) || !aligned16(k_stage) ||
+      !aligned16(v_stage) || !aligned16(group_idx_stage))
+    return HGA_ERR_ALIGN;
+  void* kd = nullptr;
+  void* vd = nullptr;
+  if (hipHostGetDevicePointer(&kd, const_cast<void*>(k_host), 0) != hipSuccess ||
+      hipHostGetDevicePointer(&vd, const_cast<void*>(v_host), 0) != hipSuccess)
+    return HGA_ERR_UNSUPPORTED;   // not pinned host memory
+  return hip_status(hga::launch_stage_history(d, shape->dtype == HGA_BF16, kd, vd, host_t_cap, group_idx, k_stage,
+                                              v_stage, stage_cap, stage_hist, group_idx_stage,
+                                              (hipStream_t)stream));
+}
+
 size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len) {
   hga::Dims d;
   if (resolve(shape, t_hist + seg_len > 0 ? t_hist + seg_len : 64, t_hist, seg_len, d) != HGA_OK) return 0;

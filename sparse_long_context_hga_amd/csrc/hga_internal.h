@@ -59,6 +59,12 @@ hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* k
                           void* group_sum, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
                           hipStream_t s, const hipEvent_t* ev);
 
+// Host-RAM history tier: the selected history groups of every (sequence, KV head)
+// copied from host memory into a staging cache, and the selection renumbered for it.
+hipError_t launch_stage_history(const Dims& d, bool bf16, const void* k_host, const void* v_host, int64_t host_t_cap,
+                                const int32_t* group_idx, void* k_stage, void* v_stage, int64_t stage_cap,
+                                int64_t stage_hist, int32_t* group_idx_stage, hipStream_t s);
+
 // Workspace: one float per query row (rowsum(dO * O)).
 size_t bwd_workspace_bytes(const Dims& d);
 

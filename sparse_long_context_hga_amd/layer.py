@@ -11,6 +11,9 @@ stream; every step of the computation runs in libhga.so.
   hga_attention    -- autograd op for one active segment: forward routes and
                       attends; backward returns dQ, dK, dV of the active segment
                       only (the history is detached).
+  HGAHostKVCache   -- the same with the detached history's K/V in pinned host
+                      memory (host-RAM tier): HBM holds the summary tables, the
+                      active segment and a staging cache for the selected groups.
   HGAStack         -- segment-wise truncated backpropagation through a stack of
                       HGA layers, each with its own cache (forward, backward,
                       detach, next segment).
@@ -161,6 +164,77 @@ class HGAKVCache:
         self.q_last, self._q_pending = self._q_pending, None
 
 
+class HGAHostKVCache:
+    """K/V of one layer with the detached history in pinned host memory.
+
+    HBM holds the group/chunk summary tables of the whole capacity (routing reads
+    only those), the active segment, and a staging cache into which
+    hga_stage_history copies, per segment, the history groups that the segment's
+    query blocks selected.  Segments have a fixed length seg_len and a fixed
+    budget (top_groups), which bound the staging cache: at most 8 * seg_len/64 *
+    top_groups history tokens.  The attention runs on the staging cache with
+    results bit-identical to HGAKVCache's; committing a segment copies its K/V
+    to host memory.
+    """
+
+    def __init__(self, batch: int, n_kv_heads: int, head_dim: int, t_cap: int, seg_len: int, n_q_heads: int,
+                 top_chunks: int, top_groups: int, dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        if t_cap % 64 or seg_len % 64 or seg_len <= 0:
+            raise ValueError("t_cap and seg_len must be multiples of 64")
+        self.batch, self.n_kv_heads, self.head_dim, self.t_cap = batch, n_kv_heads, head_dim, t_cap
+        self.seg_len, self.dtype = seg_len, dtype
+        self.k_host = torch.zeros(batch, n_kv_heads, t_cap, head_dim, dtype=dtype, pin_memory=True)
+        self.v_host = torch.zeros_like(self.k_host, pin_memory=True)
+        self.gsum = torch.zeros(batch, n_kv_heads, t_cap // 8, head_dim, dtype=dtype, device=device)
+        self.csum = torch.zeros(batch, n_kv_heads, t_cap // 64, head_dim, dtype=dtype, device=device)
+        shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, top_chunks, top_groups, _dtype_name(dtype))
+        # one staging position for every segment: enough for any selection of the longest history
+        self.stage_hist = max(64, L.hga_stage_history_min(shape, max(t_cap - seg_len, 0), seg_len))
+        self.stage_cap = self.stage_hist + seg_len
+        self.k_stage = torch.zeros(batch, n_kv_heads, self.stage_cap, head_dim, dtype=dtype, device=device)
+        self.v_stage = torch.zeros_like(self.k_stage)
+        self._gs_seg = torch.zeros(batch, n_kv_heads, self.stage_cap // 8, head_dim, dtype=dtype, device=device)
+        self._cs_seg = torch.zeros(batch, n_kv_heads, self.stage_cap // 64, head_dim, dtype=dtype, device=device)
+        self.length = 0
+        self.q_last = None
+        self.k = self.k_stage        # the device tensor the segment's checks compare devices with
+
+    def write(self, k_seg: torch.Tensor, v_seg: torch.Tensor, shape: L.HgaShape) -> int:
+        """The active segment into the staging cache and its summaries into the
+        tables (at its global position).  Returns the history length."""
+        S = k_seg.shape[2]
+        t0 = self.length
+        if S != self.seg_len:
+            raise ValueError(f"segments of this cache have {self.seg_len} tokens, got {S}")
+        if t0 + S > self.t_cap:
+            raise ValueError("KV cache capacity exceeded")
+        sh = self.stage_hist
+        self.k_stage[:, :, sh:sh + S].copy_(k_seg.detach())
+        self.v_stage[:, :, sh:sh + S].copy_(v_seg.detach())
+        L.hga_build_summaries(shape, self.k_stage, self.stage_cap, sh, sh + S, self._gs_seg, self._cs_seg)
+        self.gsum[:, :, t0 // 8:(t0 + S) // 8].copy_(self._gs_seg[:, :, sh // 8:(sh + S) // 8])
+        self.csum[:, :, t0 // 64:(t0 + S) // 64].copy_(self._cs_seg[:, :, sh // 64:(sh + S) // 64])
+        return t0
+
+    def stage(self, shape: L.HgaShape, t_hist: int, gidx: torch.Tensor) -> torch.Tensor:
+        """The selected history groups into the staging cache; returns the selection
+        renumbered for it."""
+        gst = torch.empty_like(gidx)
+        L.hga_stage_history(shape, self.k_host, self.v_host, self.t_cap, t_hist, self.seg_len, gidx, self.k_stage,
+                            self.v_stage, self.stage_cap, self.stage_hist, gst)
+        return gst
+
+    def keep_last_query_block(self, q: torch.Tensor):
+        pass
+
+    def commit(self, seg_len: int):
+        """The segment becomes history: its K/V go to host memory."""
+        t0, sh = self.length, self.stage_hist
+        self.k_host[:, :, t0:t0 + seg_len].copy_(self.k_stage[:, :, sh:sh + seg_len])
+        self.v_host[:, :, t0:t0 + seg_len].copy_(self.v_stage[:, :, sh:sh + seg_len])
+        self.length += seg_len
+
+
 def _check_segment(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cache: "HGAKVCache"):
     """Host-side agreement of a segment's tensors with the cache they are attended
     against (dtype, head size, batch, KV heads, device): the library reads the
@@ -204,6 +278,21 @@ class _HGAAttentionFn(torch.autograd.Function):
         gidx = torch.empty(B, cache.n_kv_heads, nb, top_groups, dtype=torch.int32, device=q.device)
         o = torch.empty_like(q)
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
+        if isinstance(cache, HGAHostKVCache):
+            # host-RAM tier: route over the tables in HBM, stage the selected history
+            # groups, attend on the staging cache
+            if causal_routing:
+                raise ValueError("the host-RAM tier routes blocks by their own rows")
+            t_hist = cache.write(k_seg, v_seg, shape)
+            L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
+            gst = cache.stage(shape, t_hist, gidx)
+            L.hga_attend_fwd(shape, q, cache.k_stage, cache.v_stage, cache.stage_cap, cache.stage_hist, S, gst, o,
+                             lse)
+            ctx.save_for_backward(q, o, lse, gst)
+            ctx.cache, ctx.shape = cache, shape
+            ctx.kv = (cache.k_stage, cache.v_stage, cache.stage_cap, cache.stage_hist)
+            ctx.mark_non_differentiable(lse, gidx)
+            return o, lse, gidx
         if causal_routing:
             t_hist = cache.write(k_seg, v_seg, shape)
             L.hga_route_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.csum, cache.gsum,
@@ -216,22 +305,23 @@ class _HGAAttentionFn(torch.autograd.Function):
                           o, lse)
         cache.keep_last_query_block(q)
         ctx.save_for_backward(q, o, lse, gidx)
-        ctx.cache, ctx.shape, ctx.t_hist = cache, shape, t_hist
+        ctx.cache, ctx.shape = cache, shape
+        ctx.kv = (cache.k, cache.v, cache.t_cap, t_hist)
         ctx.mark_non_differentiable(lse, gidx)
         return o, lse, gidx
 
     @staticmethod
     def backward(ctx, d_o, _lse, _g):
         q, o, lse, gidx = ctx.saved_tensors
-        cache, shape, t_hist = ctx.cache, ctx.shape, ctx.t_hist
+        cache, shape = ctx.cache, ctx.shape
+        k, v, t_cap, t_hist = ctx.kv
         B, Hq, S, d = q.shape
         dq = torch.empty_like(q)
         dk = torch.empty(B, cache.n_kv_heads, S, d, dtype=q.dtype, device=q.device)
         dv = torch.empty_like(dk)
         ws = torch.empty(max(L.hga_attend_bwd_workspace_size(shape, t_hist, S), 16), dtype=torch.uint8,
                          device=q.device)
-        L.hga_attend_bwd(shape, q, cache.k, cache.v, o, lse, d_o.contiguous(), cache.t_cap, t_hist, S, gidx,
-                         dq, dk, dv, ws)
+        L.hga_attend_bwd(shape, q, k, v, o, lse, d_o.contiguous(), t_cap, t_hist, S, gidx, dq, dk, dv, ws)
         return dq, dk, dv, None, None, None, None, None
 
 

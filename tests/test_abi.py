@@ -28,7 +28,8 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert set(names) == {"hga_build_summaries", "hga_forward", "hga_route", "hga_route_causal", "hga_attend_fwd",
+    assert set(names) == {"hga_build_summaries", "hga_forward", "hga_stage_history", "hga_stage_history_min",
+                          "hga_route", "hga_route_causal", "hga_attend_fwd",
                           "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_attend_bwd_timed",
                           "hga_decode_step", "hga_decode_route", "hga_decode_attend", "hga_decode_workspace_size",
                           "hga_decode_step_noalloc",
