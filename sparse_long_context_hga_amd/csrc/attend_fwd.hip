@@ -31,8 +31,6 @@
 namespace hga {
 namespace {
 
-constexpr int kStages = 2;   // K/V tile buffer sets (tiles in flight + 1); two measured 2% faster than three
-
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -45,12 +43,29 @@ struct FwdArgs {
   float scale;
 };
 
+// Copies of the own chunk's 64 K and V rows of unit `unit` into tile buffers kt / vt
+// (NW waves; asynchronous: the attention below waits for them).  The own chunk does
+// not depend on the selection, so a caller issues them as early as it likes.
+template <int D, int NW>
+__device__ __forceinline__ void issue_own_tile(const FwdArgs& a, int unit, uint16_t* kt, uint16_t* vt) {
+  const int j = unit % a.nb;
+  const int bh = unit / a.nb;
+  const int64_t row0 = (int64_t)bh * a.t_cap + (a.t_hist / kChunk + j) * kChunk;
+  const uint16_t* kp = (const uint16_t*)a.k + row0 * D;
+  const uint16_t* vp = (const uint16_t*)a.v + row0 * D;
+  dma_tile<D, NW>(kt, [&](int r) { return kp + (int64_t)r * D; });
+  dma_tile<D, NW>(vt, [&](int r) { return vp + (int64_t)r * D; });
+}
+
 // Attention of this work-group's HPW query heads of unit `unit` (head offset
-// sub * HPW within the KV group) over the selected groups sgid[0 .. n_valid)
-// (ascending, in LDS) plus the own chunk; qf: the lane's query row fragments (row
-// n of the wave's 32).  KB(B) / VB(B) give the K / V tile buffer set B (distinct
-// LDS arrays); sets 0 and 1 also serve as the waves' output regions at the end.
-template <int D, int G, int HPW, int NSTAGE, typename KBuf, typename VBuf>
+// sub * HPW within the KV group) over its own chunk (causally) and the selected
+// groups sgid[0 .. n_valid) (ascending, in LDS); qf: the lane's query row fragments
+// (row n of the wave's 32).  KB(B) / VB(B) give the K / V tile buffer set B
+// (distinct LDS arrays): the own chunk is tile 0, already in flight into set 2
+// (issue_own_tile, the only copies this wave has outstanding); the selected groups
+// follow, 8 per tile, through sets 0 and 1, which also serve as the waves' output
+// regions at the end.
+template <int D, int G, int HPW, typename KBuf, typename VBuf>
 __device__ __forceinline__ void attend_unit_bf16(const FwdArgs& a, int unit, int sub, const bf16x8 (&qf)[D / 16],
                                                  const int* sgid, int n_valid, const KBuf& KB, const VBuf& VB) {
   constexpr int NW = 2 * HPW;
@@ -80,30 +95,30 @@ __device__ __forceinline__ void attend_unit_bf16(const FwdArgs& a, int unit, int
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
 
-  // Group of slot s (0..7) of tile t (wave-uniform): the selection, then the own
-  // chunk as the last tile.  Slots past the selection repeat the own chunk's first
-  // group (masked later).
+  // Groups of slot s (0..7) of selected tile t >= 1 (wave-uniform): groups
+  // 8(t-1) .. of the selection; slots past it repeat the own chunk's first group
+  // (masked later).
   GroupCopier<D, NW> copier;
   auto prepare = [&](int t_) __attribute__((always_inline)) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
     copier.fetch([&](int s) __attribute__((always_inline)) -> int {
-      if (t < n_sel_tiles) {
-        const int i = 8 * t + s;
-        const int v = __builtin_amdgcn_readfirstlane(sgid[min(i, n_valid - 1)]);   // n_valid >= 1 here
-        return i < n_valid ? v : 8 * J;
-      }
-      return 8 * J + s;
+      const int i = 8 * (t - 1) + s;
+      const int v = __builtin_amdgcn_readfirstlane(sgid[min(i, n_valid - 1)]);   // n_valid >= 1 here
+      return i < n_valid ? v : 8 * J;
     });
   };
-  // Tiles are copied in order 0, 1, 2, ...: this wave's K blocks, then its V blocks;
-  // then the next tile's groups are fetched.
+  // Tiles are copied in order: this wave's K blocks, then its V blocks; then the
+  // next tile's groups are fetched.
   constexpr int BPW = GroupCopier<D, NW>::BPW;
   auto issue = [&](int t, auto B) __attribute__((always_inline)) {
     static_for<0, BPW>([&](auto K) { copier.template copy_one<K()>(KB(B), kb); });
     static_for<0, BPW>([&](auto K) { copier.template copy_one<K()>(VB(B), vb); });
     if (t + 1 < n_tiles) prepare(t + 1);
   };
-  prepare(0);
+  if (n_sel_tiles > 0) {   // the first selected tile travels while the own chunk is computed
+    prepare(1);
+    issue(1, ic<0>{});
+  }
 
   RowOffsets<D> kro;      // K rows rho(n) (and 32 + rho(n): +32 rows as an immediate)
   kro.init(rho(n), h);
@@ -144,10 +159,10 @@ __device__ __forceinline__ void attend_unit_bf16(const FwdArgs& a, int unit, int
     // Mask (only the own chunk and a partial last group tile need it), then the
     // online softmax in the log2 domain: max of the raw scores, scaled once
     // (scale > 0), and exp2(score * c2 - m) as one FMA per key.
-    const bool local = t == n_sel_tiles;
-    const bool full = !local && 8 * (t + 1) <= n_valid;
+    const bool local = t == 0;
+    const bool full = !local && 8 * t <= n_valid;
     if (!full) {
-      const int kv_lim = local ? pos : 8 * (n_valid - 8 * t) - 1;   // last valid key index
+      const int kv_lim = local ? pos : 8 * (n_valid - 8 * (t - 1)) - 1;   // last valid key index
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -201,7 +216,14 @@ __device__ __forceinline__ void attend_unit_bf16(const FwdArgs& a, int unit, int
     });
   };
 
-  pipeline<NSTAGE, 2 * BPW>(n_tiles, issue, compute);
+  // the own chunk (its copies were issued before the first selected tile's)
+  if (n_sel_tiles > 0) wait_vmcnt<2 * BPW>(); else wait_vmcnt<0>();
+  tile_barrier();
+  compute(0, ic<2>{});
+  // the selected tiles 1 .. n_sel_tiles through sets 0 and 1 (the first already issued)
+  pipeline<2, 2 * BPW, /*PREISSUED=*/true>(
+      n_sel_tiles, [&](int t, auto B) __attribute__((always_inline)) { issue(t + 1, B); },
+      [&](int t, auto B) __attribute__((always_inline)) { compute(t + 1, B); });
 
   // Epilogue: lane holds row `pos`, columns 32dt + 8g + 4h + i (i = 0..3) for r = 4g + i.
   // O leaves through this wave's 32-row LDS region as whole rows; the barrier keeps
@@ -222,7 +244,6 @@ __device__ __forceinline__ void attend_unit_bf16(const FwdArgs& a, int unit, int
 // softmax overlaps another's MFMAs on the same CU.
 template <int D, int G, int HPW>
 __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) void attend_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int kStagesHere = HPW == G ? kStages : 2;
   constexpr int KS = D / 16;       // k-steps over the head dimension
   // Tile buffer sets as distinct arrays: the compiler can then see that reads of one
   // never alias the asynchronous copies into another.
@@ -259,25 +280,27 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
   // only trails) are counted on the way.
   const int n_valid = __builtin_amdgcn_readfirstlane(
       count_valid<128 * HPW>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
-  attend_unit_bf16<D, G, HPW, kStagesHere>(a, unit, item % (G / HPW), qf, sgid, n_valid, KB, VB);
+  issue_own_tile<D, 2 * HPW>(a, unit, k2, v2);
+  attend_unit_bf16<D, G, HPW>(a, unit, item % (G / HPW), qf, sgid, n_valid, KB, VB);
 }
 
 // Route, then attend, in one work-group per unit (4 query heads per KV head: 8
 // waves).  The routing waves hold row tiles {w % 4, w % 4 + 4}; wave w attends with
 // row tile w, one of the two, so the query rows are read once for both phases.  The
-// summary batch buffers of the routing are the attention's tile buffer sets 0 and 1.
+// summary batch buffers of the routing are the attention's tile buffer sets 0 and 1;
+// the own chunk's tile is copied into set 2 once the chunk scores are in.
 template <int D>
 __global__ __launch_bounds__(512, 1) void route_attend_bf16_kernel(RouteArgs ra, FwdArgs a) {
   constexpr int G = 4;
   constexpr int KS = D / 16;
-  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D];
+  __shared__ __align__(16) uint16_t k0[64 * D], v0[64 * D], k1[64 * D], v1[64 * D], k2[64 * D], v2[64 * D];
   __shared__ RouteShared<route_threads<G>()> sm;
   __shared__ int sgid[512];
   auto KB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (B() == 0) return k0; else return k1;
+    if constexpr (B() == 0) return k0; else if constexpr (B() == 1) return k1; else return k2;
   };
   auto VB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (B() == 0) return v0; else return v1;
+    if constexpr (B() == 0) return v0; else if constexpr (B() == 1) return v1; else return v2;
   };
   auto tile = [&](auto B, auto T) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (T() == 0) return KB(B); else return VB(B);
@@ -287,14 +310,16 @@ __global__ __launch_bounds__(512, 1) void route_attend_bf16_kernel(RouteArgs ra,
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   bf16x8 qr[route_row_tiles_per_wave<G>()][KS];
   int nc, ng;
-  route_unit_bf16<D, G>(ra, unit, tile, sm, qr, nc, ng);
+  // The own chunk's K / V travel while the chunks are selected and the groups scored.
+  route_unit_bf16<D, G>(ra, unit, tile, sm, qr, nc, ng,
+                        [&]() __attribute__((always_inline)) { issue_own_tile<D, 8>(a, unit, k2, v2); });
   // The selected groups as ids (ascending), for the tile copies.
   for (int i = tid; i < ng; i += 512) sgid[i] = 8 * sm.csel[sm.gsel[i] >> 3] + (sm.gsel[i] & 7);
   __syncthreads();
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = w < 4 ? qr[0][ks] : qr[1][ks];
-  attend_unit_bf16<D, G, G, kStages>(a, unit, 0, qf, sgid, __builtin_amdgcn_readfirstlane(ng), KB, VB);
+  attend_unit_bf16<D, G, G>(a, unit, 0, qf, sgid, __builtin_amdgcn_readfirstlane(ng), KB, VB);
 }
 
 // ---------------------------------------------------------------- fp32 (SIMT)

@@ -88,12 +88,17 @@ struct RouteShared {
 // sm.gsel[0 .. ng) the chosen group slots ascending (slot s = group 8 csel[s/8] +
 // s%8, so ascending slots are ascending ids); chunk_idx / group_idx (and the
 // optional scores) of the unit are written.  The selections are visible to every
-// thread on return, and no wave reads the batch buffers any more.
-template <int D, int G, typename Tile>
+// thread on return, and no wave reads the batch buffers any more.  after_chunks()
+// runs in every thread once the chunk scores are complete (before the selection):
+// a caller may issue its own asynchronous copies there.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int D, int G, typename Tile, typename AfterChunks = NoHook>
 __device__ __forceinline__ void route_unit_bf16(const RouteArgs& a, int unit, const Tile& tile,
                                                 RouteShared<route_threads<G>()>& sm,
                                                 bf16x8 (&qf)[route_row_tiles_per_wave<G>()][D / 16], int& nc_out,
-                                                int& ng_out) {
+                                                int& ng_out, const AfterChunks& after_chunks = AfterChunks{}) {
   constexpr int NT = route_threads<G>();
   constexpr int KS = D / 16;
   constexpr int NRT = 2 * G;                      // 32-row tiles in the block
@@ -204,6 +209,7 @@ __device__ __forceinline__ void route_unit_bf16(const RouteArgs& a, int unit, co
   __syncthreads();
   if (J > 0) score_rows(J, chunk_row, ckeys);
   __syncthreads();
+  after_chunks();
   // ascending chunk ids: one wave's bit search up to 512 candidates; above, every
   // wave keeps the best k_c of its share and one wave selects among those
   const int nc = (J == 0 || a.kc == 0) ? 0
