@@ -48,6 +48,10 @@ def parse():
                             "decode_b8_ctx32k", "rollout_131k"],
                    help="decode_b8_ctx32k times the generation path (hga_decode_route + hga_decode_attend); "
                         "rollout_131k the 64-segment forward rollout")
+    p.add_argument("--history", default="hbm", choices=["hbm", "host"],
+                   help="hbm: the detached history is resident in HBM; host: in pinned host memory, with the "
+                        "selected groups staged into HBM after routing (hga_stage_history); the step rate then "
+                        "includes the host link")
     p.add_argument("--routing", default="block", choices=["block", "causal"],
                    help="block: each block routes itself (hga_route); causal: the block before it routes it")
     p.add_argument("--marked-steps", type=int, default=20,
@@ -127,6 +131,7 @@ def algorithmic_work(w, gidx):
 
 
 PMC_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_hbm_traffic.json"),
+                 "planted_b8_ctx32k": os.path.join(ROOT, "profiles", "hga_step_planted_b8_ctx32k_hbm_traffic.json"),
                  "decode_b8_ctx32k": os.path.join(ROOT, "profiles", "hga_decode_ctx32k_hbm_traffic.json")}
 MFMA_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_mfma.json")}
 CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
@@ -238,6 +243,8 @@ def measured_mfma(kernel, workload, ms):
 WORKLOAD_SOURCES = {
     "qwen3_8b_layer_ctx16k": ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "hga_device.h",
                               "hga_select.h", "route_phase.h"],
+    "planted_b8_ctx32k": ["summaries.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip", "hga_device.h",
+                          "hga_select.h", "route_phase.h"],
     "decode_b8_ctx32k": ["decode.hip", "summaries.hip", "hga_device.h", "hga_select.h"],
 }
 
@@ -283,38 +290,45 @@ def make_workload(name):
             "planted_b8_ctx32k": hi.planted_batch}[name]()
 
 
-def achievable_rates():
+def achievable_rates(seconds=0.15):
     """What this machine reaches on plain library work, for context next to the spec
     peaks: a device copy of 512 MiB (torch copy_: reads and writes 512 MiB) and a
-    dense 8192^3 bf16 GEMM (torch.matmul, hipBLASLt); best of 10 after warm-up."""
+    dense 8192^3 bf16 GEMM (torch.matmul, hipBLASLt); the best of repetitions run
+    for about `seconds` each (at least 10) after 3 warm-ups.  Run before a
+    benchmark's warm-up steps, this sustained load also brings the core clock from
+    idle to the level it holds under load."""
     import torch
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
 
-    def best(fn, n=10):
+    def best(fn):
         for _ in range(3):
             fn()
         ts = []
-        for _ in range(n):
+        t_end = time.perf_counter() + seconds
+        while len(ts) < 10 or time.perf_counter() < t_end:
             e0, e1 = mk(), mk()
             e0.record()
             fn()
             e1.record()
             e1.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
-        return min(ts)
+        return min(ts), len(ts)
     n = 512 << 20
     x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     y = torch.empty_like(x)
-    copy_gbs = 2 * n / best(lambda: y.copy_(x)) / 1e9
+    t_copy, n_copy = best(lambda: y.copy_(x))
+    copy_gbs = 2 * n / t_copy / 1e9
     del x, y
     m = 8192
     a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16).contiguous()
     b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16).contiguous()
-    gemm_tfs = 2 * m ** 3 / best(lambda: torch.matmul(a, b)) / 1e12
+    t_gemm, n_gemm = best(lambda: torch.matmul(a, b))
+    gemm_tfs = 2 * m ** 3 / t_gemm / 1e12
     del a, b
     torch.cuda.empty_cache()
     return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tfs, 1),
-            "how": "best of 10: torch copy_ of 512 MiB (bytes read + written); torch.matmul 8192^3 bf16"}
+            "how": f"best of {n_copy} torch copy_ of 512 MiB (bytes read + written) and of {n_gemm} torch.matmul "
+                   f"8192^3 bf16, each repeated for about {seconds} s"}
 
 
 def cpu_model():
@@ -665,6 +679,111 @@ def cpu_baseline_rollout(max_reps=3, min_seconds=10.0):
                       f"block, forward), {len(times)} repetitions, median {t:.2f} s"}
 
 
+# ------------------------------------------------------------------ host-RAM tier
+def main_host_tier(args):
+    """The layer step with the detached history in pinned host memory: the active
+    segment's summaries (built in the staging cache, copied into the tables at their
+    global position), routing over the tables in HBM, staging of the selected history
+    groups over the host link (hga_stage_history), then the forward and backward on
+    the staging cache.  Inputs are in place before timing (history in host memory,
+    the segment in HBM); the step rate includes the host-link transfers."""
+    import numpy as np
+    import torch
+    import sparse_long_context_hga_amd as hga
+
+    w = make_workload(args.workload)
+    B, Hq, Hkv, d, S, th = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seg_len, w.t_hist
+    T = th + S
+    nb = S // 64
+    dt = torch.bfloat16
+    shape = hga.make_shape(B, Hq, Hkv, d, w.top_chunks, w.top_groups, w.dtype, w.softmax_scale)
+    print(f"[bench] workload {w.name}, history in host memory: B={B} Hq={Hq} Hkv={Hkv} d={d} t_hist={th} S={S}",
+          file=sys.stderr, flush=True)
+    k_full = torch.from_numpy(w.k_cache).to(dt)
+    v_full = torch.from_numpy(w.v_cache).to(dt)
+    k_host = k_full.pin_memory()
+    v_host = v_full.pin_memory()
+    gsum = torch.zeros(B, Hkv, T // 8, d, dtype=dt, device="cuda")
+    csum = torch.zeros(B, Hkv, T // 64, d, dtype=dt, device="cuda")
+    kd = k_full.cuda()                                        # history summaries: built once, untimed
+    hga.hga_build_summaries(shape, kd, T, 0, th, gsum, csum)
+    torch.cuda.synchronize()
+    del kd
+    sh = hga.hga_stage_history_min(shape, th, S)
+    cap = sh + S
+    k_st = torch.zeros(B, Hkv, cap, d, dtype=dt, device="cuda")
+    v_st = torch.zeros_like(k_st)
+    k_st[:, :, sh:] = k_full[:, :, th:T].cuda()              # the active segment: in HBM before timing
+    v_st[:, :, sh:] = v_full[:, :, th:T].cuda()
+    gs_seg = torch.zeros(B, Hkv, cap // 8, d, dtype=dt, device="cuda")
+    cs_seg = torch.zeros(B, Hkv, cap // 64, d, dtype=dt, device="cuda")
+    dev = lambda x: torch.from_numpy(x).to("cuda").to(dt).contiguous()   # noqa: E731
+    q, d_o = dev(w.q), dev(w.d_o)
+    cidx = torch.empty(B, Hkv, nb, w.top_chunks, dtype=torch.int32, device="cuda")
+    gidx = torch.empty(B, Hkv, nb, w.top_groups, dtype=torch.int32, device="cuda")
+    gst = torch.empty_like(gidx)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, S, dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dk = torch.empty(B, Hkv, S, d, dtype=dt, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = torch.empty(hga.hga_attend_bwd_workspace_size(shape, sh, S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def step(ev=None):
+        hga.hga_build_summaries(shape, k_st, cap, sh, sh + S, gs_seg, cs_seg)
+        gsum[:, :, th // 8:T // 8].copy_(gs_seg[:, :, sh // 8:cap // 8])
+        csum[:, :, th // 64:T // 64].copy_(cs_seg[:, :, sh // 64:cap // 64])
+        hga.hga_route(shape, q, csum, gsum, T, th, S, cidx, gidx)
+        if ev:
+            ev[0].record(stream)
+        hga.hga_stage_history(shape, k_host, v_host, T, th, S, gidx, k_st, v_st, cap, sh, gst)
+        if ev:
+            ev[1].record(stream)
+        hga.hga_attend_fwd(shape, q, k_st, v_st, cap, sh, S, gst, o, lse)
+        hga.hga_attend_bwd(shape, q, k_st, v_st, o, lse, d_o, cap, sh, S, gst, dq, dk, dv, ws)
+
+    achievable = None if args.no_calibration else achievable_rates()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    n_mark = max(1, args.marked_steps)
+    evs = [[mk(), mk()] for _ in range(n_mark)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    stage_ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    g = gidx.cpu().numpy()
+    staged = 0
+    for b in range(B):
+        for h in range(Hkv):
+            ids = g[b, h].ravel()
+            staged += len(set(int(x) for x in ids if 0 <= x < th // 8))
+    staged_bytes = staged * 8 * d * 2 * 2                      # K and V rows of every staged group
+    out = {
+        "metric": METRIC + " -- history in host RAM (host-link-inclusive)", "value": round(B * S / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "t_hist": th,
+                   "seg_len": S, "top_chunks": w.top_chunks, "top_groups": w.top_groups,
+                   "history": "pinned host memory; selected groups staged into HBM",
+                   "staging_tokens": sh, "parallelism": "none (1 GPU)"},
+        "stage": {"ms": round(stage_ms, 5), "groups_staged": staged, "bytes": staged_bytes,
+                  "host_link_GB/s": round(staged_bytes / (stage_ms * 1e-3) / 1e9, 1),
+                  "of_history": round(staged / (B * Hkv * th // 8), 4)},
+        "achievable": achievable,
+        "kernel_timing": f"staging call timed with HIP events on {n_mark} steps run after the timed region",
+    }
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -683,8 +802,8 @@ def main():
         print(json.dumps(summ, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the HGA layer path has no multi-GPU mode "
-              "(sharding is by sequence and KV head, see the design notes).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the HGA layer path has no multi-GPU mode (it would shard "
+              "by sequence and KV head, with no communication inside the layer).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -699,6 +818,8 @@ def main():
         return main_decode(args)
     if args.workload == "rollout_131k":
         return main_rollout(args)
+    if args.history == "host":
+        return main_host_tier(args)
     w = make_workload(args.workload)
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
           f"t_hist={w.t_hist} S={w.seg_len} k_c={w.top_chunks} k_g={w.top_groups}", file=sys.stderr, flush=True)
@@ -737,13 +858,16 @@ def main():
 
     def step(fev=None, bev=None):
         if args.routing == "causal":
+            # three kernels: summaries, causal routing, attention forward (events
+            # between the calls, on the stream the library launches on)
             if fev:
                 fev[0].record(stream)
             L.summaries(w.t_hist, w.t_hist + w.seg_len)
             if fev:
                 fev[1].record(stream)
-                fev[2].record(stream)
             route()
+            if fev:
+                fev[2].record(stream)
             L.fwd()
             if fev:
                 fev[3].record(stream)
@@ -787,8 +911,12 @@ def main():
         step(fev[i], bev[i])
     torch.cuda.synchronize()
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
-    kern_ms = {"summaries": avg((e[0], e[1]) for e in fev),
-               "route_attend": avg((e[2], e[3]) for e in fev)}
+    if args.routing == "causal":
+        kern_ms = {"summaries": avg((e[0], e[1]) for e in fev), "route": avg((e[1], e[2]) for e in fev),
+                   "attend_fwd": avg((e[2], e[3]) for e in fev)}
+    else:
+        kern_ms = {"summaries": avg((e[0], e[1]) for e in fev),
+                   "route_attend": avg((e[2], e[3]) for e in fev)}
     if L.do is not None:
         for k, name in enumerate(("attend_bwd_dq", "attend_bwd_order", "attend_bwd_dkdv", "attend_bwd_finalize")):
             kern_ms[name] = avg((e[2 * k], e[2 * k + 1]) for e in bev)
@@ -841,8 +969,10 @@ def main():
         "roofline": roofline,
         "achievable": achievable,
         "kernels": kernels,
-        "kernel_timing": f"every kernel timed from its own dispatch (HIP events recorded by the launch) in "
-                         f"{n_mark} steps run after the timed region",
+        "kernel_timing": (f"every kernel timed from its own dispatch (HIP events recorded by the launch) in "
+                          f"{n_mark} steps run after the timed region" if args.routing == "block" else
+                          f"HIP events between the calls (one kernel each) on the library's stream, in {n_mark} "
+                          f"steps run after the timed region"),
         "kernel_sum_ms": round(sum(kern_ms.values()), 5),
     }
     if not args.no_cpu_baseline:
