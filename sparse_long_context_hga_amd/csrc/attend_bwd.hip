@@ -12,7 +12,8 @@
 // bf16 path: four kernels, deterministic (no floating-point atomics):
 //  * dq (query-major, one work-group per (sequence, KV head, query block) and
 //    query-head slice): the forward's gathered tiles again; recomputes P from
-//    LSE; writes dQ and D = rowsum(dO * O) (workspace) for the dK/dV kernel.  It
+//    LSE; writes dQ, and D = rowsum(dO * O) and -LSE log2(e) (workspace) for the
+//    dK/dV kernel.  It
 //    also inverts the selection for the active chunk of its own block -- the
 //    ascending list of query blocks that attend the chunk -- and cuts the
 //    chunk's work into 1..8 items of about 12 or 16 "rounds" (one round = the 64 rows
@@ -62,6 +63,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;      // [B, Hq, S] rowsum(dO * O)            (workspace)
+  float* nlse;      // [B, Hq, S] -LSE * log2(e), the exponent offset of P in base 2 (workspace)
   int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
   int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
   int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
@@ -226,8 +228,11 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
     }
   }
   const float Dr = half_sum(dpart);
-  if (h == 0) a.dvec[qrow] = Dr;
   const float lse2 = a.lse[qrow] * kLog2e;
+  if (h == 0) {
+    a.dvec[qrow] = Dr;
+    a.nlse[qrow] = -lse2;
+  }
 
   const int n_valid = __builtin_amdgcn_readfirstlane(
       count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
@@ -342,7 +347,8 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 
 struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) vector
   static size_t up(size_t x) { return (x + 255) & ~(size_t)255; }
-  static size_t flags_off(size_t rows) { return up(rows * 4); }
+  static size_t nlse_off(size_t rows) { return up(rows * 4); }
+  static size_t flags_off(size_t rows) { return up(nlse_off(rows) + rows * 4); }
   static size_t nvis_off(size_t rows, size_t units) { return up(flags_off(rows) + units * 4); }
   static size_t first_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
   static size_t vis_off(size_t rows, size_t units) { return up(first_off(rows, units) + units * kMaxParts * 4); }
@@ -454,13 +460,13 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   auto round_row0 = [&](int r, int jj) __attribute__((always_inline)) -> int64_t {
     return (((int64_t)b * a.Hq + kvh * G + r % G) * a.seg_len) + (int64_t)jj * kQBlock;
   };
-  // Round: the 64 rows of one query head of one attending block -> Q, dO tiles, LSE, D.
-  // Every wave copies the 64 LSE and D values itself (identical data), so that all
+  // Round: the 64 rows of one query head of one attending block -> Q, dO tiles,
+  // -LSE log2(e), D.  Every wave copies the 64 values of each itself (identical data), so that all
   // waves issue the same number of copies per round.
   auto issue_rows = [&](int64_t row0, auto B) __attribute__((always_inline)) {
     dma_tile<D, 4>(QB(B), [&](int rr) { return qg + (row0 + rr) * D; });
     dma_tile<D, 4>(OB(B), [&](int rr) { return dg + (row0 + rr) * D; });
-    __builtin_amdgcn_global_load_lds((const void*)(a.lse + row0 + l), (lds_void_t*)LB(B), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(a.nlse + row0 + l), (lds_void_t*)LB(B), 4, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(a.dvec + row0 + l), (lds_void_t*)RB(B), 4, 0, 0);
   };
   auto issue = [&](int i, auto B) __attribute__((always_inline)) {
@@ -518,17 +524,28 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   f32x16 dvacc[DT], dkacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) { dvacc[dt] = f32x16{}; dkacc[dt] = f32x16{}; }
+  // Per-lane LDS offsets of the fragment reads, computed once: row reads of this
+  // wave's rows 32 rh + rho(n); transposing reads of its 32-row half (the swizzle
+  // repeats every 16 rows, so the half is a plain shift of the offsets).
+  RowOffsets<D> rowo;
+  rowo.init(32 * rh + rho(n), h);
+  ColOffsets<D> colo;
+  colo.init(l);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) colo.o[i] += 2 * 32 * rh * D;
 
   auto compute = [&](int i, auto B) __attribute__((always_inline)) {
     const uint16_t* tq = QB(B);
     const uint16_t* tdo = OB(B);
-    const float* ls = LB(B);
+    const float* nls = LB(B);
     const float* drv = RB(B);
     const int vi = (r_lo + i) / G;
-    const bool own = vlist[vi] == cc;
-    const bool key_on = ((vmask[vi] >> (key >> 3)) & 1u) != 0u;
-    const RowReader<D> rowrd(32 * rh + rho(n));
-    const ColReader<D> colrd;
+    // the round's block and group mask are the same for every lane
+    const bool own = __builtin_amdgcn_readfirstlane(vlist[vi]) == cc;
+    const uint32_t vm = (uint32_t)__builtin_amdgcn_readfirstlane((int)vmask[vi]);
+    const bool key_on = ((vm >> (key >> 3)) & 1u) != 0u;
+    rowo.refresh();
+    colo.refresh();
     f32x16 s = {}, dpv = {};
     {
       // All row fragments first, then the MFMAs: the reads overlap each other and the
@@ -536,8 +553,8 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
       bf16x8 qa[KS], da[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qa[ks] = rowrd(tq, 16 * ks + 8 * h);
-        da[ks] = rowrd(tdo, 16 * ks + 8 * h);
+        qa[ks] = rowo.read(tq, ks);
+        da[ks] = rowo.read(tdo, ks);
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -549,29 +566,31 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {                 // rows 16ks .. 16ks+15 of the wave's 32
+    static_for<0, 2>([&](auto KSI) {                 // rows 16ks .. 16ks+15 of the wave's 32
+      constexpr int ks = KSI();
       // Transposed fragments of dO and Q for these rows (independent of P: issued first).
       bf16x8 fo[DT], fq[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        fo[dt] = colrd(tdo, 32 * rh + 16 * ks, 32 * dt);
-        fq[dt] = colrd(tq, 32 * rh + 16 * ks, 32 * dt);
+        fo[dt] = colo.template read<ks>(tdo, dt);
+        fq[dt] = colo.template read<ks>(tq, dt);
       }
-      // LSE and D of the 8 consecutive rows this lane holds (two 16-byte LDS reads each).
+      // -LSE log2(e) and D of the 8 consecutive rows this lane holds (two 16-byte LDS reads each).
       const int row0 = 32 * rh + 16 * ks + 8 * h;
-      const f32x4v l0 = *reinterpret_cast<const f32x4v*>(ls + row0);
-      const f32x4v l1 = *reinterpret_cast<const f32x4v*>(ls + row0 + 4);
+      const f32x4v l0 = *reinterpret_cast<const f32x4v*>(nls + row0);
+      const f32x4v l1 = *reinterpret_cast<const f32x4v*>(nls + row0 + 4);
       const f32x4v d0 = *reinterpret_cast<const f32x4v*>(drv + row0);
       const f32x4v d1 = *reinterpret_cast<const f32x4v*>(drv + row0 + 4);
+      // Row row0 + e sees this lane's key iff e >= thr: in the own block causally
+      // (key <= row), in a later block when the key's group is selected.
+      const int thr = own ? key - row0 : key_on ? 0 : 8;
       float p[8], ds[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float lse = e < 4 ? l0[e & 3] : l1[e & 3];
+        const float nl = e < 4 ? l0[e & 3] : l1[e & 3];
         const float dr = e < 4 ? d0[e & 3] : d1[e & 3];
-        const bool valid = own ? key <= row0 + e : key_on;
-        const float pe = fast_exp2(fmaf(s[8 * ks + e], c2, -lse * kLog2e));
-        p[e] = valid ? pe : 0.f;
+        const float pe = fast_exp2(fmaf(s[8 * ks + e], c2, nl));
+        p[e] = e >= thr ? pe : 0.f;
         ds[e] = p[e] * (dpv[8 * ks + e] - dr);
       }
       const bf16x8 pf = f32x8_to_bf16x8(p);
@@ -581,7 +600,7 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
         dvacc[dt] = mfma32(fo[dt], pf, dvacc[dt]);
         dkacc[dt] = mfma32(fq[dt], dsf, dkacc[dt]);
       }
-    }
+    });
   };
 
   pipeline<3, L, /*PREISSUED=*/true>(r_hi - r_lo, issue, compute);
@@ -854,7 +873,7 @@ hipError_t launch_bf16_g(const BwdArgs& a, int G, const Launcher& run) {
 }  // namespace
 
 size_t bwd_workspace_bytes(const Dims& d) {
-  // rowsum(dO*O) per query row, one flag per (sequence, KV head, active chunk), and
+  // rowsum(dO*O) and -LSE log2(e) per query row, one flag per (sequence, KV head, active chunk), and
   // G fp32 dK/dV partials per active chunk (bf16 path only).
   const size_t rows = (size_t)d.B * d.Hq * (size_t)d.seg_len;
   const size_t units = (size_t)d.B * d.Hkv * (size_t)d.nb;
@@ -873,6 +892,7 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   {
     const size_t rows = (size_t)d.B * d.Hq * (size_t)d.seg_len;
     const size_t units = (size_t)d.B * d.Hkv * (size_t)d.nb;
+    a.nlse = (float*)((char*)workspace + DkdvLayout::nlse_off(rows));
     a.flags = (int*)((char*)workspace + DkdvLayout::flags_off(rows));
     a.nvis = (int*)((char*)workspace + DkdvLayout::nvis_off(rows, units));
     a.first = (int*)((char*)workspace + DkdvLayout::first_off(rows, units));
