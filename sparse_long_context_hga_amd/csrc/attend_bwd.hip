@@ -543,6 +543,8 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
     // the round's block and group mask are the same for every lane
     const bool own = __builtin_amdgcn_readfirstlane(vlist[vi]) == cc;
     const uint32_t vm = (uint32_t)__builtin_amdgcn_readfirstlane((int)vmask[vi]);
+    // A later block that selected none of this wave's 4 groups adds nothing to its keys.
+    if (!own && ((vm >> (4 * kh)) & 0xFu) == 0u) return;
     const bool key_on = ((vm >> (key >> 3)) & 1u) != 0u;
     rowo.refresh();
     colo.refresh();
