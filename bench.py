@@ -933,7 +933,7 @@ def main():
         if "gather_bytes" in wk:
             kernels[k]["gather_GB/s"] = round(wk["gather_bytes"] / (ms * 1e-3) / 1e9, 1)
         if args.routing == "block" and not args.cold:
-            mc = measured_mfma(k, w.name, ms)
+            mc = measured_mfma(k, args.workload, ms)
             if mc is not None:
                 kernels[k]["mfma_counters"] = mc
     dom = max(kern_ms, key=lambda k: kern_ms[k])
@@ -948,7 +948,7 @@ def main():
         ach = wk["bytes"] / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roofline["traffic"] = measured_traffic(dom, w.name) if args.routing == "block" and not args.cold else None
+    roofline["traffic"] = measured_traffic(dom, args.workload) if args.routing == "block" and not args.cold else None
     roofline["kernel"] = dom
     if achievable is not None:
         roofline["frac_of_achievable"] = round(
