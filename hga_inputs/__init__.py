@@ -224,37 +224,43 @@ ROLLOUT_SEG = 2048
 def planted_batch(batch: int = 8, t_total: int = 32768, seg_len: int = 2048,
                   n_q_heads: int = 32, n_kv_heads: int = 8, head_dim: int = 128,
                   n_planted: int = 4, cos: float = 0.9, q_plant: float = 1.0,
-                  seed: int = 55, top_chunks: int = 16, top_groups: int = 64) -> Workload:
+                  seed: int = 55, top_chunks: int = 16, top_groups: int = 64,
+                  n_decoys: int = 0) -> Workload:
     """batch x 32,768-token sequences; fwd+bwd of the last 2,048-token segment.
     Per sequence: a random unit direction u; n_planted distinct history chunks
     whose keys (every KV head, every token) have cosine `cos` with u at their
-    own norm; every query of the active segment gets + q_plant * u."""
+    own norm; every query of the active segment gets + q_plant * u.  With
+    n_decoys > 0, that many further distinct chunks get cosine -cos with u (a
+    control for direction sensitivity: their summaries are as large as the
+    planted ones but point away from the queries)."""
     t_hist = t_total - seg_len
     w = random_layer(seed=seed, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                      head_dim=head_dim, t_hist=t_hist, seg_len=seg_len, top_chunks=top_chunks,
                      top_groups=top_groups, dtype="f32", name="planted")
     rp = _streams(seed + 1000, batch)
     planted = np.zeros((batch, n_planted), np.int64)
+    decoys = np.zeros((batch, n_decoys), np.int64)
     q = w.q
     k = w.k_cache
     for b in range(batch):
         u = _normal(rp[b], (head_dim,)).astype(np.float64)
         u /= np.linalg.norm(u)
-        chunks = np.sort(rp[b].choice(t_hist // CHUNK, size=n_planted, replace=False))
-        planted[b] = chunks
-        for c in chunks:
+        picks = rp[b].choice(t_hist // CHUNK, size=n_planted + n_decoys, replace=False)
+        planted[b] = np.sort(picks[:n_planted])
+        decoys[b] = np.sort(picks[n_planted:])
+        for c, cs in [(c, cos) for c in planted[b]] + [(c, -cos) for c in decoys[b]]:
             g = k[b, :, c * CHUNK:(c + 1) * CHUNK].astype(np.float64)       # [Hkv,64,d]
             gn = np.linalg.norm(g, axis=-1, keepdims=True)
             wperp = g - (g @ u)[..., None] * u
             wperp /= np.linalg.norm(wperp, axis=-1, keepdims=True)
-            k[b, :, c * CHUNK:(c + 1) * CHUNK] = (gn * (cos * u + math.sqrt(1 - cos * cos) * wperp)).astype(np.float32)
+            k[b, :, c * CHUNK:(c + 1) * CHUNK] = (gn * (cs * u + math.sqrt(1 - cs * cs) * wperp)).astype(np.float32)
         q[b] = (q[b].astype(np.float64) + q_plant * u).astype(np.float32)
     return Workload(name=f"planted_b{batch}_ctx{t_total}", batch=batch, n_q_heads=n_q_heads,
                     n_kv_heads=n_kv_heads, head_dim=head_dim, t_hist=t_hist, seg_len=seg_len,
                     t_cap=t_total, top_chunks=top_chunks, top_groups=top_groups, dtype="bf16",
                     softmax_scale=1.0 / math.sqrt(head_dim), backward=True,
                     q=round_to_bf16(q), k_cache=round_to_bf16(k), v_cache=round_to_bf16(w.v_cache),
-                    d_o=round_to_bf16(w.d_o), extra={"planted_chunks": planted})
+                    d_o=round_to_bf16(w.d_o), extra={"planted_chunks": planted, "decoy_chunks": decoys})
 
 
 NAMED = {

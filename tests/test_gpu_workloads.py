@@ -222,6 +222,31 @@ def test_planted_b8_ctx32k_recall(chk, planted):
     print("planted recall 1.0 on all units", flush=True)
 
 
+def test_planted_with_decoys_route(chk):
+    """Direction control on the GPU: 2 sequences of 8,192 tokens (32/8/128, bf16)
+    with 4 planted chunks and 4 decoy chunks (keys at cosine -0.9 with the planted
+    direction) each.  The fused routing + attention call's selection is accepted
+    against the oracle on every unit and holds every planted chunk and group."""
+    w = hi.planted_batch(batch=2, t_total=8192, seg_len=2048, seed=56, n_decoys=4)
+    print(f"workload {w.name} with decoys", flush=True)
+    L = chk.DeviceLayer(w)
+    L.summaries(0, w.t_hist)
+    L.forward()
+    torch.cuda.synchronize()
+    cidx, gidx = L.cidx.cpu().numpy(), L.gidx.cpu().numpy()
+    gs, cs = chk.oracle_summaries(w)
+    ocidx, _, tables = chk.oracle_route(w, gs, cs)
+    chk.accept_all_units(w, gs, cs, cidx, gidx, "planted_decoys", ocidx, tables)
+    for b in range(w.batch):
+        pc = set(int(c) for c in w.extra["planted_chunks"][b])
+        pg = {8 * c + u for c in pc for u in range(8)}
+        for kvh in range(w.n_kv_heads):
+            for j in range(w.seg_len // 64):
+                assert pc <= set(int(c) for c in cidx[b, kvh, j]), (b, kvh, j)
+                assert pg <= set(int(g) for g in gidx[b, kvh, j]), (b, kvh, j)
+    print("planted recall 1.0 with decoys present", flush=True)
+
+
 def test_planted_b8_ctx32k_route(chk, planted):
     P = planted
     chk.accept_all_units(P.w, P.gs, P.cs, P.cidx, P.gidx, P.w.name, P.ocidx, P.tables)

@@ -143,6 +143,33 @@ def test_planted_chunks_are_recalled():
             assert pg <= set(int(g) for g in gidx[0, kvh, j])
 
 
+def test_planted_chunks_outrank_decoys():
+    """Direction control for the planted workload: 4 further chunks whose keys point
+    away from the queries' planted direction (cosine -0.9) have summaries as large
+    as the planted ones.  The block score is a maximum over 256 rows, so a decoy can
+    come close when one row happens to point far enough away from the direction;
+    on this input every planted chunk still ranks above every decoy in every block
+    (a router scoring |q.S|, or the summary norm, would not), and every planted
+    chunk is recalled."""
+    w = hi.planted_batch(batch=1, t_total=8192, seg_len=512, n_q_heads=8, n_kv_heads=2,
+                         head_dim=64, seed=55, n_decoys=4)
+    gs, cs = _summaries(w)
+    planted = [int(c) for c in w.extra["planted_chunks"][0]]
+    decoys = [int(c) for c in w.extra["decoy_chunks"][0]]
+    assert len(decoys) == 4 and not set(planted) & set(decoys)
+    # the decoys' summaries are as large as the planted ones
+    norm = lambda c: float(np.linalg.norm(cs[0, 0, c]))                 # noqa: E731
+    assert min(norm(c) for c in decoys) > 0.8 * max(norm(c) for c in planted)
+    margin = np.inf
+    for kvh in range(2):
+        for j in range(w.seg_len // 64):
+            c_sel, _, sig, _, _ = ora.route_unit(w.q, cs, gs, w.t_hist, 0, kvh, j, 16, 64, w.group_size)
+            assert set(planted) <= set(c_sel)
+            margin = min(margin, min(sig[c] for c in planted) - max(sig[c] for c in decoys))
+    assert margin > 0, margin
+    print(f"planted chunks outrank decoys by at least {margin:.2f} in every block")
+
+
 # ---------------------------------------------------------------------------
 # Strictly causal routing (R-causal): a block is routed by the query block before it.
 # ---------------------------------------------------------------------------
