@@ -183,6 +183,7 @@ class HGAHostKVCache:
             raise ValueError("t_cap and seg_len must be multiples of 64")
         self.batch, self.n_kv_heads, self.head_dim, self.t_cap = batch, n_kv_heads, head_dim, t_cap
         self.seg_len, self.dtype = seg_len, dtype
+        self.n_q_heads, self.top_chunks, self.top_groups = n_q_heads, top_chunks, top_groups
         self.k_host = torch.zeros(batch, n_kv_heads, t_cap, head_dim, dtype=dtype, pin_memory=True)
         self.v_host = torch.zeros_like(self.k_host, pin_memory=True)
         self.gsum = torch.zeros(batch, n_kv_heads, t_cap // 8, head_dim, dtype=dtype, device=device)
@@ -283,6 +284,9 @@ class _HGAAttentionFn(torch.autograd.Function):
             # groups, attend on the staging cache
             if causal_routing:
                 raise ValueError("the host-RAM tier routes blocks by their own rows")
+            if Hq != cache.n_q_heads or top_groups > cache.top_groups:
+                raise ValueError(f"this host-tier cache was sized for {cache.n_q_heads} query heads and at most "
+                                 f"{cache.top_groups} groups per block, got {Hq} and {top_groups}")
             t_hist = cache.write(k_seg, v_seg, shape)
             L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
             gst = cache.stage(shape, t_hist, gidx)

@@ -127,3 +127,16 @@ def test_host_tier_equals_hbm_history(hga, name):
         for label, a, b_ in zip(("o", "lse", "group_idx", "dq", "dk", "dv"), *res):
             assert torch.equal(a, b_), f"{name}, segment {s}: {label} differs between the tiers"
     print(f"case {name}: {n_seg} segments bit-identical", flush=True)
+
+
+def test_host_tier_rejects_a_larger_budget(hga):
+    """The staging area is sized for the cache's budget: a call with more groups per
+    block is refused before anything is written or launched."""
+    from sparse_long_context_hga_amd.layer import HGAHostKVCache, hga_attention
+    cache = HGAHostKVCache(1, 2, 64, 512, 128, 4, 2, 8, torch.bfloat16)
+    q = torch.zeros(1, 4, 128, 64, dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="sized for"):
+        hga_attention(q, kv, kv, cache, 2, 16)
+    assert cache.length == 0
+
