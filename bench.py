@@ -45,8 +45,9 @@ def parse():
                         "milliseconds of sustained work, so the timed steps see its steady state")
     p.add_argument("--workload", default="qwen3_8b_layer_ctx16k",
                    choices=["qwen3_8b_layer_ctx16k", "qwen3_8b_layer_ctx4k", "planted_b8_ctx32k",
-                            "decode_b8_ctx32k", "rollout_131k"],
-                   help="decode_b8_ctx32k times the generation path (hga_decode_route + hga_decode_attend); "
+                            "decode_b8_ctx32k", "decode_b64_ctx16k", "rollout_131k"],
+                   help="decode_b8_ctx32k / decode_b64_ctx16k time the generation path (hga_decode_route + "
+                        "hga_decode_attend) for 8 sequences at 32K / 64 at 16K; "
                         "rollout_131k the 64-segment forward rollout")
     p.add_argument("--history", default="hbm", choices=["hbm", "host"],
                    help="hbm: the detached history is resident in HBM; host: in pinned host memory, with the "
@@ -379,7 +380,9 @@ def cpu_baseline(w, q_prev=None, min_seconds=10.0, max_reps=5):
 
 
 # ------------------------------------------------------------------ generation
-DECODE_METRIC = "HGA decode tokens/s at 32K ctx (one new token per sequence per step); % of HBM roofline"
+def decode_metric(t_cap):
+    return (f"HGA decode tokens/s at {t_cap // 1024}K ctx (one new token per sequence per step); "
+            f"% of HBM roofline")
 
 
 def decode_work(w, cidx, gidx):
@@ -440,7 +443,7 @@ def main_decode(args):
     import hga_inputs as hi
     import sparse_long_context_hga_amd as hga
 
-    w = hi.decode_b8_ctx32k()
+    w = {"decode_b8_ctx32k": hi.decode_b8_ctx32k, "decode_b64_ctx16k": hi.decode_b64_ctx16k}[args.workload]()
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
           f"t_cap={w.t_cap} pos={list(w.pos)} k_c={w.top_chunks} k_g={w.top_groups}", file=sys.stderr, flush=True)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -523,7 +526,7 @@ def main_decode(args):
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, w.name), "kernel": dom}
     n_tok = int((np.asarray(w.pos) >= 0).sum())
     out = {
-        "metric": DECODE_METRIC, "value": round(n_tok / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "metric": decode_metric(w.t_cap), "value": round(n_tok / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,

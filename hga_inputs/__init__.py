@@ -175,6 +175,16 @@ def decode_b8_ctx32k(seed: int = 66) -> DecodeWorkload:
                         top_chunks=16, top_groups=64, chunk_mean_var=0.5, name="decode_b8_ctx32k")
 
 
+def decode_b64_ctx16k(seed: int = 67) -> DecodeWorkload:
+    """Generation at serving batch size: 64 sequences of the Qwen3-8B layer shape at
+    16K context, each adding one token in the last chunks of its 16,384-token cache
+    (ragged own-chunk lengths; every 64th position completes a chunk), block-structured
+    keys.  Timing only: at 8 sequences the generation kernels cannot fill the chip."""
+    pos = [16383 - 9 * b for b in range(64)]
+    return decode_batch(seed=seed, batch=64, n_q_heads=32, n_kv_heads=8, head_dim=128, t_cap=16384, pos=pos,
+                        top_chunks=16, top_groups=64, chunk_mean_var=0.5, name="decode_b64_ctx16k")
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------
