@@ -17,7 +17,7 @@ def pytest_configure(config):
 def pytest_sessionfinish(session, exitstatus):
     """Write the near-tie exemptions that the GPU parity tests recorded (test name ->
     exempt pairs, units that needed one, units checked) to $HGA_PARITY_RECORD, or to
-    gpurun_out/parity_exemptions.json when that folder exists."""
+    parity_exemptions.json in the run's output folder when that folder exists."""
     chk = sys.modules.get("tests.hga_check")
     if chk is None or not getattr(chk, "EXEMPTIONS", None):
         return
