@@ -410,7 +410,8 @@ class HGADecoder:
     """Generation steps over `cache`: every sequence adds one token per step.
 
     step(q, k_new, v_new, pos) writes the new tokens' K/V at positions pos (a [B]
-    int32 device tensor; a negative entry marks an idle slot), routes each token
+    int32 device tensor; an entry outside [0, t_cap) marks an idle slot, whose
+    outputs are O = 0, LSE = -inf and no selection), routes each token
     with its own query heads, attends, and builds the summaries of every chunk
     whose last token this step wrote.  Returns (o [B,Hq,d], lse [B,Hq], group_idx).
     The cache's `length` is not used: positions come from `pos`.
@@ -441,7 +442,7 @@ class HGADecoder:
                 raise ValueError(f"{name} must be [{B}, {Hkv}, {d}], got {list(t.shape)}")
         if tuple(pos.shape) != (B,) or pos.dtype != torch.int32 or pos.device != c.k.device:
             raise ValueError(f"pos must be a [{B}] int32 tensor on {c.k.device}")
-        live = pos >= 0
+        live = (pos >= 0) & (pos < c.t_cap)      # the library treats the other slots as idle
         bi, p = self._b[live], pos[live].long()
         c.k[bi, :, p] = k_new[live].to(c.dtype)
         c.v[bi, :, p] = v_new[live].to(c.dtype)
