@@ -280,3 +280,27 @@ def test_generation_loop_through_the_decoder(chk):
         ora.build_summaries(w.k_cache[b:b + 1], 0, 64 * nf, "bf16", gs, cs)
         np.testing.assert_array_equal(chk.to_np(cache.gsum[b:b + 1]), gs)
         np.testing.assert_array_equal(chk.to_np(cache.csum[b:b + 1]), cs)
+
+
+def test_decoder_positions_outside_the_cache_are_idle(chk):
+    """A decoder slot whose position is negative or at/after the cache capacity is
+    idle: nothing is written into the cache, its O rows are 0, its LSE -inf and its
+    selection empty, while the other slot's step is unaffected."""
+    from sparse_long_context_hga_amd.layer import HGADecoder, HGAKVCache
+    B, Hq, Hkv, d, T = 3, 4, 1, 64, 256
+    cache = HGAKVCache(B, Hkv, d, T, torch.bfloat16)
+    cache.k.normal_()
+    cache.v.normal_()
+    k_before = cache.k.clone()
+    dec = HGADecoder(cache, Hq, 2, 8)
+    q = torch.randn(B, Hq, d, device="cuda").to(torch.bfloat16)
+    kv = torch.randn(B, Hkv, d, device="cuda").to(torch.bfloat16)
+    pos = torch.tensor([T, -1, 70], dtype=torch.int32, device="cuda")
+    o, lse, gidx = dec.step(q, kv, kv, pos)
+    torch.cuda.synchronize()
+    for b in (0, 1):
+        assert torch.equal(cache.k[b], k_before[b])
+        assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b]))
+        assert torch.all(gidx[b] == -1)
+    assert torch.equal(cache.k[2, :, 70], kv[2])
+    assert torch.all(torch.isfinite(lse[2]))
