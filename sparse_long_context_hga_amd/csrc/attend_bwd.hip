@@ -306,13 +306,18 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
         kt_fr[1][dt] = kco.template read<2 * kt + 1>(K, dt);
       }
 
+      // Mask only the own chunk and a partial last tile (a score of -inf gives P = 0).
+      // The empty asm keeps this a branch, so that full tiles skip the compares.
+      if (!full) {
+        asm volatile("" ::: "memory");
+        const int thr = kv_lim - 32 * kt - 8 * h;   // out_row(r, h) + 32 kt > kv_lim  <=>  out_row(r, 0) > thr
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (out_row(r, 0) > thr) s[r] = -INFINITY;
+      }
       float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], c2, -lse2));
-        if (!full && 32 * kt + out_row(r, h) > kv_lim) p = 0.f;
-        ds[r] = p * (dpv[r] - Dr);
-      }
+      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(fmaf(s[r], c2, -lse2)) * (dpv[r] - Dr);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const bf16x8 dsf = f32x8_to_bf16x8(ds + 8 * half);
