@@ -92,6 +92,49 @@ def test_stage_history_mapping_and_rows(hga):
     print(f"staged {n_staged} history groups for {len(slots)} (sequence, KV head) pairs", flush=True)
 
 
+def test_stage_history_at_the_maximum_history(hga):
+    """Staging at the library's largest cache (8,192 chunks: 524,160 history tokens,
+    65,520 history groups, every word of the selection bitmap in use): route two
+    blocks over all 8,190-8,191 earlier chunks, stage, and check every index and row."""
+    B, Hq, Hkv, d, S = 1, 2, 1, 64, 128
+    T = 64 * 8192
+    th = T - S
+    rng = np.random.default_rng(77)
+    kc = hi.round_to_bf16(rng.standard_normal((B, Hkv, T, d), dtype=np.float32))
+    vc = hi.round_to_bf16(rng.standard_normal((B, Hkv, T, d), dtype=np.float32))
+    q = hi.round_to_bf16(rng.standard_normal((B, Hq, S, d), dtype=np.float32))
+    shape = hga.make_shape(B, Hq, Hkv, d, 16, 64, "bf16")
+    dt = torch.bfloat16
+    k = torch.from_numpy(kc).to("cuda").to(dt).contiguous()
+    gs = torch.zeros(B, Hkv, T // 8, d, dtype=dt, device="cuda")
+    cs = torch.zeros(B, Hkv, T // 64, d, dtype=dt, device="cuda")
+    hga.hga_build_summaries(shape, k, T, 0, T, gs, cs)
+    cidx = torch.empty(B, Hkv, S // 64, 16, dtype=torch.int32, device="cuda")
+    gidx = torch.empty(B, Hkv, S // 64, 64, dtype=torch.int32, device="cuda")
+    hga.hga_route(shape, torch.from_numpy(q).to("cuda").to(dt).contiguous(), cs, gs, T, th, S, cidx, gidx)
+    del k
+    k_host = torch.from_numpy(kc).to(dt).pin_memory()
+    v_host = torch.from_numpy(vc).to(dt).pin_memory()
+    sh = hga.hga_stage_history_min(shape, th, S)
+    cap = sh + S
+    k_st = torch.full((B, Hkv, cap, d), 7.0, dtype=dt, device="cuda")
+    v_st = torch.full_like(k_st, 7.0)
+    gst = torch.empty_like(gidx)
+    hga.hga_stage_history(shape, k_host, v_host, T, th, S, gidx, k_st, v_st, cap, sh, gst)
+    torch.cuda.synchronize()
+    g = gidx.cpu().numpy()
+    assert g.max() >= 8 * 4096, "the selection should reach the second half of the history"
+    want, slots = _expected_stage(g, th, sh)
+    np.testing.assert_array_equal(gst.cpu().numpy(), want)
+    ks, vs = k_st.cpu(), v_st.cpu()
+    hist = slots[(0, 0)]
+    for s_, grp in enumerate(hist):
+        assert torch.equal(ks[0, 0, 8 * s_:8 * s_ + 8], k_host[0, 0, 8 * grp:8 * grp + 8])
+        assert torch.equal(vs[0, 0, 8 * s_:8 * s_ + 8], v_host[0, 0, 8 * grp:8 * grp + 8])
+    assert torch.all(ks[0, 0, 8 * len(hist):sh] == 7.0)
+    print(f"staged {len(hist)} of {th // 8} history groups, highest id {max(hist)}", flush=True)
+
+
 CASES = {
     # the staging area holds the whole history (512 tokens)
     "g4_d128_s256": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, seg_len=256, n_seg=3,
