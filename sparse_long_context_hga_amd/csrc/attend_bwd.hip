@@ -478,9 +478,11 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
     issue_rows(round_row0(r_lo + i, vlist[(r_lo + i) / G]), B);
   };
   // Everything the first round needs travels at once: the visit list (into
-  // registers), the first round's rows, the chunk's K and V rows (coalesced copies
-  // into buffer set 2, which the third round uses later), then the second round's
-  // rows, whose blocks also come with the work-list entry.
+  // registers), the first round's rows and the chunk's K and V rows (coalesced copies
+  // into buffer set 2, which the third round uses later).  The second round's rows,
+  // whose block also comes with the work-list entry, follow once these have landed:
+  // every CU loads at the same moment, and copies still in flight would share the
+  // bandwidth with the ones the first round waits for.
   int vv[kMaxBlocks / 256];
 #pragma unroll
   for (int k = 0; k < kMaxBlocks / 256; ++k) {
@@ -496,7 +498,6 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   }
   constexpr int L = 2 * dma_per_wave<D, 4>() + 2;   // copies per wave per round
   const bool two = r_hi - r_lo > 1;
-  if (two) issue_rows(round_row0(r_lo + 1, (int)(first >> 16)), ic<1>{});
 #pragma unroll
   for (int k = 0; k < kMaxBlocks / 256; ++k) {
     const int i = tid + 256 * k;
@@ -508,11 +509,12 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
       vmask[i] = jj < a.nb ? (uint32_t)vv[k] >> 16 : 0u;
     }
   }
-  // This wave's share of the K/V copies has landed (only the second round's may still
-  // be in flight); after the barrier every wave's share and the visit list are in LDS.
-  if (two) wait_vmcnt<L>(); else wait_vmcnt<0>();
+  // This wave's share of the copies has landed; after the barrier every wave's share
+  // and the visit list are in LDS.
+  wait_vmcnt<0>();
   wait_lgkmcnt0();
   tile_barrier();
+  if (two) issue_rows(round_row0(r_lo + 1, (int)(first >> 16)), ic<1>{});
   bf16x8 kf[KS], vf[KS];
   {
     RowOffsets<D> kvo;   // key row 32 kh + n
