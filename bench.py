@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--mfma-summary", metavar="COUNTER_CSV",
                    help="no GPU work: reduce a rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 counter_collection.csv "
                         "into the MFMA summary under profiles/")
+    p.add_argument("--stall-summary", nargs="+", metavar="COUNTER_CSV",
+                   help="no GPU work: reduce rocprofv3 --pmc counter_collection.csv files of SQ wave counters "
+                        "(SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_*, ...) into the "
+                        "wave-state summary under profiles/")
     p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: reduce two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                         "WRITE_SIZE) of a --copy-calibration-mib run into the traffic summary under profiles/")
@@ -135,6 +139,7 @@ PMC_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_st
                  "planted_b8_ctx32k": os.path.join(ROOT, "profiles", "hga_step_planted_b8_ctx32k_hbm_traffic.json"),
                  "decode_b8_ctx32k": os.path.join(ROOT, "profiles", "hga_decode_ctx32k_hbm_traffic.json")}
 MFMA_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_mfma.json")}
+STALL_SUMMARIES = {"qwen3_8b_layer_ctx16k": os.path.join(ROOT, "profiles", "hga_step_ctx16k_stalls.json")}
 CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 # kernel-name prefix -> step kernel (first match wins)
 KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_attend_", "route_attend"), ("route_", "route"),
@@ -218,6 +223,51 @@ def mfma_summary(counter_csv, workload):
             "mfma_bf16_flops_per_launch": round(statistics.mean(cnt["MfmaFlopsBF16"]))
             if cnt.get("MfmaFlopsBF16") else None,
         }
+    return out
+
+
+def stall_summary(counter_csvs, workload):
+    """Where each step kernel's waves spend their time, from SQ counter passes (per
+    dispatch, averaged over the step's dispatches of each kernel).  The wave-cycle
+    counters (SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_*) share
+    one unit (4 cycles), so their ratios are fractions of the waves' lifetime:
+    waiting on an s_waitcnt or a data dependency (SQ_WAIT_ANY), ready but not issued
+    because the unit or the issue slot is taken (SQ_WAIT_INST_ANY), and issuing each
+    instruction type (SQ_ACTIVE_INST_*).  SQ_VALU_MFMA_COEXEC_CYCLES over
+    SQ_VALU_MFMA_BUSY_CYCLES is the share of matrix-busy cycles in which a vector
+    instruction issued as well."""
+    import csv
+    import collections
+    groups = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in counter_csvs:
+        for r in csv.DictReader(open(path)):
+            short = _short_name(r["Kernel_Name"])
+            key = next((k for pre, k in KERNEL_KEYS if short.startswith(pre)), None)
+            if key is not None:
+                groups[(key, r["Grid_Size"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    best = {}
+    for (key, _grid), cnt in groups.items():
+        n = max(len(v) for v in cnt.values())
+        if key not in best or n > best[key][0]:
+            best[key] = (n, cnt)
+    out = {"workload": workload, "source_sha256": kernel_source_digest(workload), "kernels": {}}
+    for key, (_n, cnt) in sorted(best.items()):
+        m = {c: statistics.mean(v) for c, v in cnt.items()}
+        k = {"launches": max(len(v) for v in cnt.values()), "counters_per_launch": {c: round(v) for c, v in m.items()}}
+        wc = m.get("SQ_WAVE_CYCLES")
+        if wc:
+            for c, label in (("SQ_WAIT_ANY", "wait_dependency"), ("SQ_WAIT_INST_ANY", "wait_issue"),
+                             ("SQ_ACTIVE_INST_ANY", "active_any"), ("SQ_ACTIVE_INST_VALU", "active_valu"),
+                             ("SQ_ACTIVE_INST_LDS", "active_lds"), ("SQ_ACTIVE_INST_SCA", "active_scalar"),
+                             ("SQ_WAIT_INST_LDS", "wait_issue_lds")):
+                if c in m:
+                    k[f"{label}_frac"] = round(m[c] / wc, 4)
+        if m.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            k["valu_coissue_frac_of_mfma_busy"] = round(m.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0)
+                                                        / m["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+        if m.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in m:
+            k["lds_bank_conflict_frac"] = round(m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"], 4)
+        out["kernels"][key] = k
     return out
 
 
@@ -793,6 +843,12 @@ def main():
     if args.mfma_summary:
         summ = mfma_summary(args.mfma_summary, args.workload)
         with open(MFMA_SUMMARIES[args.workload], "w") as f:
+            json.dump(summ, f, indent=1)
+        print(json.dumps(summ, indent=1))
+        return
+    if args.stall_summary:
+        summ = stall_summary(args.stall_summary, args.workload)
+        with open(STALL_SUMMARIES[args.workload], "w") as f:
             json.dump(summ, f, indent=1)
         print(json.dumps(summ, indent=1))
         return

@@ -74,6 +74,29 @@ def test_mfma_summary_averages_each_kernel(tmp_path):
     assert s["kernels"]["summaries"]["mfma_bf16_flops_per_launch"] == 0
 
 
+def test_stall_summary_gives_fractions_of_wave_cycles(tmp_path):
+    a = [(DQ, 131072, "SQ_WAVE_CYCLES", 1000.0), (DQ, 131072, "SQ_WAIT_ANY", 400.0),
+         (DQ, 131072, "SQ_WAIT_INST_ANY", 300.0), (DQ, 131072, "SQ_ACTIVE_INST_ANY", 300.0),
+         (DQ, 131072, "SQ_WAVE_CYCLES", 3000.0), (DQ, 131072, "SQ_WAIT_ANY", 1200.0),
+         (DQ, 131072, "SQ_WAIT_INST_ANY", 900.0), (DQ, 131072, "SQ_ACTIVE_INST_ANY", 900.0),
+         (SUM, 458752, "SQ_WAVE_CYCLES", 50.0), (SUM, 65536, "SQ_WAVE_CYCLES", 10.0),
+         (SUM, 65536, "SQ_WAIT_ANY", 8.0), (SUM, 65536, "SQ_WAVE_CYCLES", 10.0), (SUM, 65536, "SQ_WAIT_ANY", 8.0)]
+    b = [(DQ, 131072, "SQ_VALU_MFMA_BUSY_CYCLES", 800.0), (DQ, 131072, "SQ_VALU_MFMA_COEXEC_CYCLES", 200.0),
+         (DQ, 131072, "SQ_LDS_IDX_ACTIVE", 100.0), (DQ, 131072, "SQ_LDS_BANK_CONFLICT", 5.0)]
+    _write(tmp_path / "a.csv", a)
+    _write(tmp_path / "b.csv", b)
+    s = bench.stall_summary([str(tmp_path / "a.csv"), str(tmp_path / "b.csv")], "qwen3_8b_layer_ctx16k")
+    dq = s["kernels"]["attend_bwd_dq"]
+    assert dq["launches"] == 2
+    assert dq["counters_per_launch"]["SQ_WAVE_CYCLES"] == 2000
+    assert (dq["wait_dependency_frac"], dq["wait_issue_frac"], dq["active_any_frac"]) == (0.4, 0.3, 0.3)
+    assert dq["valu_coissue_frac_of_mfma_busy"] == 0.25
+    assert dq["lds_bank_conflict_frac"] == 0.05
+    # the step's summaries launches (the most frequent grid), not the one-off history build
+    assert s["kernels"]["summaries"]["launches"] == 2
+    assert s["kernels"]["summaries"]["wait_dependency_frac"] == 0.8
+
+
 def test_summaries_are_tied_to_the_kernel_sources(tmp_path, monkeypatch):
     summ = {"workload": "qwen3_8b_layer_ctx16k", "source_sha256": bench.kernel_source_digest("qwen3_8b_layer_ctx16k"),
             "kernels": {"attend_bwd_dq": {"hbm_bytes_per_launch": 123, "mfma_util_pct": 40.0,
