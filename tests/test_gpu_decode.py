@@ -195,6 +195,43 @@ def test_decode_step_equals_route_then_attend(chk, name):
     _check_attend(chk, w, chk.to_np(d2.o), d2.lse.cpu().numpy(), d2.gidx.cpu().numpy())
 
 
+@pytest.mark.parametrize("name", ["bf16_g4_d128", "bf16_g8_d128", "f32_g4_d64"])
+def test_decode_step_reads_nothing_after_each_position(chk, name):
+    """K, V and summary rows after each sequence's position (all of them in an idle
+    slot) set to NaN change no selection, output or LSE, and no summary row the step
+    keeps or rebuilds: the step reads only what precedes the new token."""
+    w = hi.decode_batch(name=name, **CASES[name])
+    print(f"case {name} pos={list(w.pos)}", flush=True)
+    gs, cs = _summaries(w)
+    clean, pois = Dev(chk, w, gs, cs), Dev(chk, w, gs, cs)
+    nan = float("nan")
+    for b, p in enumerate(int(x) for x in w.pos):
+        if p < 0:
+            pois.k[b], pois.v[b], pois.gs[b], pois.cs[b] = nan, nan, nan, nan
+        else:
+            pois.k[b, :, p + 1:] = nan
+            pois.v[b, :, p + 1:] = nan
+            pois.gs[b, :, 8 * (p // 64):] = nan
+            pois.cs[b, :, p // 64:] = nan
+    clean.step()
+    pois.step()
+    torch.cuda.synchronize()
+    def same(a, b_):   # equal, NaN where the other is NaN
+        nan_a, nan_b = torch.isnan(a), torch.isnan(b_)
+        return torch.equal(nan_a, nan_b) and torch.equal(a[~nan_a], b_[~nan_b])
+
+    for label in ("cidx", "gidx"):
+        assert torch.equal(getattr(clean, label), getattr(pois, label)), f"{label} differs"
+    for label in ("o", "lse"):
+        assert same(getattr(clean, label).float(), getattr(pois, label).float()), f"{label} differs"
+    for b, p in enumerate(int(x) for x in w.pos):
+        if p < 0:
+            continue
+        c = p // 64 + (1 if (p + 1) % 64 == 0 else 0)   # chunks the step keeps or completes
+        assert torch.equal(clean.gs[b, :, : 8 * c], pois.gs[b, :, : 8 * c]), f"sequence {b}: group summaries"
+        assert torch.equal(clean.cs[b, :, :c], pois.cs[b, :, :c]), f"sequence {b}: chunk summaries"
+
+
 def test_decode_workspace_reuse(chk):
     """Two layers of different shapes share one workspace, alternating: every repeat
     is bit-identical and the arrival counters are back at zero after each call."""
