@@ -169,7 +169,7 @@ def test_decode_attend_on_oracle_selection_and_summaries(chk, name):
 
 @pytest.mark.parametrize("name", ["bf16_g4_d128", "bf16_g1_d64", "f32_g4_d64"])
 def test_decode_step_equals_route_then_attend(chk, name):
-    """The one-launch step gives bit-exactly what the two separate calls give (same
+    """The one-call step (hga_decode_step) gives bit-exactly what the two separate calls give (same
     selection, output, LSE and summaries), and repeats bit-exactly."""
     w = hi.decode_batch(name=name, **CASES[name])
     print(f"case {name} pos={list(w.pos)}", flush=True)
