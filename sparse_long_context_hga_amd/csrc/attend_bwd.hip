@@ -67,7 +67,7 @@ struct BwdArgs {
   int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
   int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
   int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
-  int* first;       // [B, Hkv, S/64, kMaxParts] per item: block of its first round | block of its second << 16
+  int* first;       // [B, Hkv, S/64, kMaxParts] per item: the block of its first round
   int* order;       // [4 + 4*B*Hkv*S/64*kMaxParts] number of work items (padded to 16 bytes), then the
                     // items heaviest first, each {unit * kMaxParts + part, parts of the unit, visits of the unit,
                     // the item's entry of `first`}
@@ -139,15 +139,12 @@ __device__ __forceinline__ void plan_chunk(const BwdArgs& a, int bh, int cc, con
     n += __popcll(bal);
   }
   // G rounds (query heads) per attending block (n >= 1: the own block), cut into np
-  // items of about a.target_rounds; item k starts at round k * rounds / np.  The blocks
-  // of every item's first two rounds go into the work list, so that the dK/dV kernel
-  // can start their copies before it has read the visit list.
+  // items of about a.target_rounds; item k starts at round k * rounds / np.  The block
+  // of every item's first round goes into the work list, so that the dK/dV kernel can
+  // start its copies before it has read the visit list.
   const int rounds = G * n;
   const int np = min(kMaxParts, (rounds + a.target_rounds - 1) / a.target_rounds);
-  if (l < np) {
-    const int r0 = l * rounds / np, r1 = min(r0 + 1, rounds - 1);
-    a.first[(int64_t)unit * kMaxParts + l] = (int)(mask[cc + r0 / G] | (mask[cc + r1 / G] << 16));
-  }
+  if (l < np) a.first[(int64_t)unit * kMaxParts + l] = (int)mask[cc + (l * rounds / np) / G];
   if (l == 0) {
     a.nvis[unit] = n;
     a.flags[unit] = np;
@@ -348,7 +345,9 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 // the finalize kernel (deterministic; no atomics).
 // Inside a work-group: 4 waves; wave w owns keys 32*(w&1) .. +31 of the chunk
 // and rows 32*(w>>1) .. +31 of every round; each round's Q/dO rows are copied
-// into LDS two rounds ahead of their use (three buffer sets).
+// into LDS one round ahead of their use (two buffer sets: a deeper prefetch puts
+// more copies in flight per CU, and those delay the ones the current round waits
+// for).
 
 struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) vector
   static size_t up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -413,21 +412,21 @@ template <int D, int G>
 __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __align__(16) uint16_t q0[64 * D], do0[64 * D], q1[64 * D], do1[64 * D], q2[64 * D], do2[64 * D];
-  __shared__ __align__(16) float ls0[64], dr0[64], ls1[64], dr1[64], ls2[64], dr2[64];
+  __shared__ __align__(16) uint16_t q0[64 * D], do0[64 * D], q1[64 * D], do1[64 * D];
+  __shared__ __align__(16) float ls0[64], dr0[64], ls1[64], dr1[64];
   __shared__ uint32_t vmask[kMaxBlocks];   // group mask of the i-th attending block
   __shared__ int vlist[kMaxBlocks];        // i-th attending block
   auto QB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (B() == 0) return q0; else if constexpr (B() == 1) return q1; else return q2;
+    if constexpr (B() == 0) return q0; else return q1;
   };
   auto OB = [&](auto B) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (B() == 0) return do0; else if constexpr (B() == 1) return do1; else return do2;
+    if constexpr (B() == 0) return do0; else return do1;
   };
   auto LB = [&](auto B) __attribute__((always_inline)) -> float* {
-    if constexpr (B() == 0) return ls0; else if constexpr (B() == 1) return ls1; else return ls2;
+    if constexpr (B() == 0) return ls0; else return ls1;
   };
   auto RB = [&](auto B) __attribute__((always_inline)) -> float* {
-    if constexpr (B() == 0) return dr0; else if constexpr (B() == 1) return dr1; else return dr2;
+    if constexpr (B() == 0) return dr0; else return dr1;
   };
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
@@ -446,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   const int part = item % kMaxParts;
   const int unit = item / kMaxParts;
   if (unit >= a.n_units || part >= np || n_visits > a.nb) return;   // not an item of this selection
-  if ((int)(first & 0xFFFFu) >= a.nb || (int)(first >> 16) >= a.nb) return;
+  if ((int)first >= a.nb) return;
   const int cc = unit % a.nb;                      // active chunk == its own query block
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
@@ -478,26 +477,25 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
     issue_rows(round_row0(r_lo + i, vlist[(r_lo + i) / G]), B);
   };
   // Everything the first round needs travels at once: the visit list (into
-  // registers), the first round's rows and the chunk's K and V rows (coalesced copies
-  // into buffer set 2, which the third round uses later).  The second round's rows,
-  // whose block also comes with the work-list entry, follow once these have landed:
-  // every CU loads at the same moment, and copies still in flight would share the
-  // bandwidth with the ones the first round waits for.
+  // registers), the first round's rows (its block comes with the work-list entry) and
+  // the chunk's K and V rows (coalesced copies into buffer set 1, which the second
+  // round uses later).  The second round's rows follow once these have landed, from
+  // the pipeline: every CU loads at the same moment, and copies still in flight would
+  // share the bandwidth with the ones the first round waits for.
   int vv[kMaxBlocks / 256];
 #pragma unroll
   for (int k = 0; k < kMaxBlocks / 256; ++k) {
     const int i = tid + 256 * k;
     vv[k] = i < n_visits ? a.vis[(int64_t)unit * a.nb + i] : 0;
   }
-  issue_rows(round_row0(r_lo, (int)(first & 0xFFFFu)), ic<0>{});
+  issue_rows(round_row0(r_lo, (int)first), ic<0>{});
   {
     const uint16_t* kp = (const uint16_t*)a.k + ((int64_t)bh * a.t_cap + cglob * kChunk) * D;
     const uint16_t* vp = (const uint16_t*)a.v + ((int64_t)bh * a.t_cap + cglob * kChunk) * D;
-    dma_tile<D, 4>(q2, [&](int rr) { return kp + (int64_t)rr * D; });
-    dma_tile<D, 4>(do2, [&](int rr) { return vp + (int64_t)rr * D; });
+    dma_tile<D, 4>(q1, [&](int rr) { return kp + (int64_t)rr * D; });
+    dma_tile<D, 4>(do1, [&](int rr) { return vp + (int64_t)rr * D; });
   }
   constexpr int L = 2 * dma_per_wave<D, 4>() + 2;   // copies per wave per round
-  const bool two = r_hi - r_lo > 1;
 #pragma unroll
   for (int k = 0; k < kMaxBlocks / 256; ++k) {
     const int i = tid + 256 * k;
@@ -514,18 +512,17 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   wait_vmcnt<0>();
   wait_lgkmcnt0();
   tile_barrier();
-  if (two) issue_rows(round_row0(r_lo + 1, (int)(first >> 16)), ic<1>{});
   bf16x8 kf[KS], vf[KS];
   {
     RowOffsets<D> kvo;   // key row 32 kh + n
     kvo.init(key, h);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = kvo.read(q2, ks);
-      vf[ks] = kvo.read(do2, ks);
+      kf[ks] = kvo.read(q1, ks);
+      vf[ks] = kvo.read(do1, ks);
     }
   }
-  wait_lgkmcnt0();   // read before the pipeline's first barrier lets set 2 be refilled
+  wait_lgkmcnt0();   // read before the pipeline's first barrier lets set 1 be refilled
 
   const float c2 = a.scale * kLog2e;
   f32x16 dvacc[DT], dkacc[DT];
@@ -612,7 +609,7 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
     });
   };
 
-  pipeline<3, L, /*PREISSUED=*/true>(r_hi - r_lo, issue, compute);
+  pipeline<2, L, /*PREISSUED=*/true>(r_hi - r_lo, issue, compute);
 
   // Sum the two row halves (waves 2,3 -> waves 0,1) through LDS; waves 0,1 then put
   // the sums, row-major by key, in their own halves' buffers, and all four waves
