@@ -376,8 +376,19 @@ __global__ __launch_bounds__(kOrderThreads) void attend_bwd_order_kernel(BwdArgs
   auto size_of = [&](int np_u, int r_u, int k) __attribute__((always_inline)) {
     return min(kBuckets - 1, (k + 1) * r_u / np_u - k * r_u / np_u);
   };
+  // A thread's first unit (every unit when there are at most kOrderThreads) is read
+  // once, counts and item entries together, and kept for the scatter below.
+  int np0 = 0, nv0 = 0;
+  int fst0[kMaxParts] = {};
+  static_assert(kMaxParts == 8, "two int4 per unit");
+  if (tid < a.n_units) {
+    np0 = a.flags[tid];
+    nv0 = a.nvis[tid];
+    *reinterpret_cast<int4*>(fst0) = reinterpret_cast<const int4*>(a.first)[2 * tid];
+    *reinterpret_cast<int4*>(fst0 + 4) = reinterpret_cast<const int4*>(a.first)[2 * tid + 1];
+  }
   for (int u = tid; u < a.n_units; u += kOrderThreads) {
-    const int np_u = a.flags[u], r_u = G * a.nvis[u];
+    const int np_u = u == tid ? np0 : a.flags[u], r_u = G * (u == tid ? nv0 : a.nvis[u]);
     for (int k = 0; k < np_u; ++k) atomicAdd(&cnt[size_of(np_u, r_u, k)], 1);
   }
   __syncthreads();
@@ -394,12 +405,17 @@ __global__ __launch_bounds__(kOrderThreads) void attend_bwd_order_kernel(BwdArgs
   }
   __syncthreads();
   for (int u = tid; u < a.n_units; u += kOrderThreads) {
-    const int np_u = a.flags[u], r_u = G * a.nvis[u];
-    const int nv_u = a.nvis[u];
-    int fst[kMaxParts];   // loaded whole, with the counts (entries k >= np_u unused)
-    *reinterpret_cast<int4*>(fst) = reinterpret_cast<const int4*>(a.first)[2 * u];
-    *reinterpret_cast<int4*>(fst + 4) = reinterpret_cast<const int4*>(a.first)[2 * u + 1];
-    static_assert(kMaxParts == 8, "two int4 per unit");
+    int np_u = np0, nv_u = nv0;
+    int fst[kMaxParts];   // loaded whole (entries k >= np_u unused)
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) fst[k] = fst0[k];
+    if (u != tid) {
+      np_u = a.flags[u];
+      nv_u = a.nvis[u];
+      *reinterpret_cast<int4*>(fst) = reinterpret_cast<const int4*>(a.first)[2 * u];
+      *reinterpret_cast<int4*>(fst + 4) = reinterpret_cast<const int4*>(a.first)[2 * u + 1];
+    }
+    const int r_u = G * nv_u;
 #pragma unroll
     for (int k = 0; k < kMaxParts; ++k)
       if (k < np_u)
