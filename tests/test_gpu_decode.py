@@ -13,6 +13,7 @@ Expected values come only from the oracle.
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, given, settings, strategies as st
 
 import hga_inputs as hi
 from oracle import hga_oracle as ora
@@ -341,3 +342,57 @@ def test_decoder_positions_outside_the_cache_are_idle(chk):
         assert torch.all(gidx[b] == -1)
     assert torch.equal(cache.k[2, :, 70], kv[2])
     assert torch.all(torch.isfinite(lse[2]))
+
+
+@st.composite
+def _small_generation_steps(draw):
+    G = draw(st.sampled_from([1, 2, 4, 8]))
+    hkv = draw(st.integers(1, 2))
+    t_cap = 64 * draw(st.integers(1, 32))
+    batch = draw(st.integers(1, 4))
+    kc = draw(st.integers(0, 6))
+    # positions anywhere in the cache, the last of a chunk (its summaries are built),
+    # or idle (-1)
+    pos = draw(st.lists(st.one_of(st.integers(0, t_cap - 1), st.sampled_from([t_cap - 1, 63, -1])),
+                        min_size=batch, max_size=batch))
+    return dict(seed=draw(st.integers(0, 2 ** 16)), batch=batch, n_q_heads=G * hkv, n_kv_heads=hkv,
+                head_dim=draw(st.sampled_from([64, 128])), t_cap=t_cap, pos=pos, top_chunks=kc,
+                top_groups=draw(st.integers(0, 8 * kc)), dtype=draw(st.sampled_from(["bf16", "f32"])),
+                chunk_mean_var=draw(st.sampled_from([0.0, 0.5])))
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(kw=_small_generation_steps())
+def test_decode_random_small_steps(chk, kw):
+    """Small generation steps whose shapes and positions Hypothesis draws (derandomized):
+    routing accepted, attention on the oracle's selection, the summaries of every
+    completed chunk rebuilt bit for bit, and the one-call step equal to the two calls."""
+    w = hi.decode_batch(name="hypothesis", **kw)
+    print(f"case {kw}", flush=True)
+    gs, cs = _summaries(w)
+    d = Dev(chk, w, gs, cs)
+    d.route()
+    torch.cuda.synchronize()
+    _check_route(chk, w, gs, cs, d.cidx.cpu().numpy(), d.gidx.cpu().numpy(), d.cscore.cpu().numpy())
+    _, ogidx, _ = ora.decode_route(w.q, cs, gs, w.pos, w.top_chunks, w.top_groups, w.group_size)
+    gs_in, cs_in = gs.copy(), cs.copy()
+    for b in range(w.batch):
+        p = int(w.pos[b])
+        if p >= 0 and (p + 1) % 64 == 0:
+            gs_in[b, :, 8 * (p // 64):8 * (p // 64) + 8] = 0
+            cs_in[b, :, p // 64] = 0
+    a = Dev(chk, w, gs_in, cs_in)
+    a.attend(torch.from_numpy(ogidx).cuda(), a.gs, a.cs)
+    torch.cuda.synchronize()
+    _check_attend(chk, w, chk.to_np(a.o), a.lse.cpu().numpy(), ogidx)
+    np.testing.assert_array_equal(chk.to_np(a.gs), gs)
+    np.testing.assert_array_equal(chk.to_np(a.cs), cs)
+    d1, d2 = Dev(chk, w, gs_in, cs_in), Dev(chk, w, gs_in, cs_in)
+    d1.route()
+    d1.attend(None, d1.gs, d1.cs)
+    d2.step()
+    torch.cuda.synchronize()
+    for x, y in ((d1.cidx, d2.cidx), (d1.gidx, d2.gidx), (d1.o, d2.o), (d1.lse, d2.lse), (d1.gs, d2.gs),
+                 (d1.cs, d2.cs)):
+        assert torch.equal(x, y)
