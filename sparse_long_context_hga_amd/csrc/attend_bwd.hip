@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   const int part = item % kMaxParts;
   const int unit = item / kMaxParts;
   if (unit >= a.n_units || part >= np || n_visits > a.nb) return;   // not an item of this selection
-  if ((int)first >= a.nb) return;
+  if (first >= (uint32_t)a.nb) return;             // (unsigned: no negative block either)
   const int cc = unit % a.nb;                      // active chunk == its own query block
   const int bh = unit / a.nb;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
