@@ -10,6 +10,8 @@ above the candidate count, and contexts of 2,047 and 4,095 candidate chunks
 acceptance rule; attention on the oracle's own selection; summaries bit-exactly.
 Expected values come only from the oracle.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -363,7 +365,7 @@ def _small_generation_steps(draw):
                 chunk_mean_var=draw(st.sampled_from([0.0, 0.5])))
 
 
-@settings(max_examples=60, deadline=None, derandomize=True, database=None,
+@settings(max_examples=int(os.environ.get("HGA_HYPOTHESIS_EXAMPLES", 60)), deadline=None, derandomize=True, database=None,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 @given(kw=_small_generation_steps())
 def test_decode_random_small_steps(chk, kw):

@@ -9,7 +9,11 @@ block-structured keys.  Each example checks every step against the oracle:
 - the forward and the backward on the oracle's selection, to the parity tolerances
   (per query block and per active chunk for the gradients);
 - hga_forward bit for bit against the separate calls.
+
+HGA_HYPOTHESIS_EXAMPLES sets the number of examples (default 100; 600 have been run).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -43,7 +47,7 @@ def small_layers(draw):
                 chunk_mean_var=draw(st.sampled_from([0.0, 0.5])))
 
 
-@settings(max_examples=100, deadline=None, derandomize=True, database=None,
+@settings(max_examples=int(os.environ.get("HGA_HYPOTHESIS_EXAMPLES", 100)), deadline=None, derandomize=True, database=None,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 @given(kw=small_layers())
 def test_random_small_layer(chk, kw):
