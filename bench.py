@@ -125,6 +125,10 @@ def algorithmic_work(w, gidx):
         "route": {"bytes": route_bytes, "flops": route_flops},
         "attend_fwd": {"bytes": fwd_bytes, "flops": fwd_flops, "gather_bytes": kv_sel},
         # routing and attention in one work-group per unit: Q is read once for both
+        # the same with strictly causal routing: the routing rows are the block before
+        # (read once more), the attention reads the block's own rows
+        "route_attend_causal": {"bytes": route_bytes + fwd_bytes, "flops": route_flops + fwd_flops,
+                                "gather_bytes": kv_sel},
         "route_attend": {"bytes": route_bytes + fwd_bytes - q_bytes, "flops": route_flops + fwd_flops,
                          "gather_bytes": kv_sel},
         "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops, "gather_bytes": kv_sel},
@@ -902,9 +906,6 @@ def main():
         q_prev_np = hi.prev_query_block(seed=1, batch=w.batch, n_q_heads=w.n_q_heads, head_dim=w.head_dim,
                                         dtype=w.dtype)
         q_prev = dev(q_prev_np)
-        route = lambda: L.route_causal(q_prev)   # noqa: E731
-    else:
-        route = L.route
     L.summaries(0, w.t_hist)                                  # history summaries: built once, untimed
     torch.cuda.synchronize()
     # What the box reaches on plain library work; these sustained copies and GEMMs
@@ -917,19 +918,7 @@ def main():
 
     def step(fev=None, bev=None):
         if args.routing == "causal":
-            # three kernels: summaries, causal routing, attention forward (events
-            # between the calls, on the stream the library launches on)
-            if fev:
-                fev[0].record(stream)
-            L.summaries(w.t_hist, w.t_hist + w.seg_len)
-            if fev:
-                fev[1].record(stream)
-            route()
-            if fev:
-                fev[2].record(stream)
-            L.fwd()
-            if fev:
-                fev[3].record(stream)
+            L.forward_causal(q_prev, events=fev)      # summaries, then causal routing + attention
         else:
             L.forward(events=fev)                     # summaries, then routing + attention
         if L.do is not None:
@@ -970,12 +959,8 @@ def main():
         step(fev[i], bev[i])
     torch.cuda.synchronize()
     avg = lambda pairs: statistics.mean(a.elapsed_time(b) for a, b in pairs)   # noqa: E731
-    if args.routing == "causal":
-        kern_ms = {"summaries": avg((e[0], e[1]) for e in fev), "route": avg((e[1], e[2]) for e in fev),
-                   "attend_fwd": avg((e[2], e[3]) for e in fev)}
-    else:
-        kern_ms = {"summaries": avg((e[0], e[1]) for e in fev),
-                   "route_attend": avg((e[2], e[3]) for e in fev)}
+    kern_ms = {"summaries": avg((e[0], e[1]) for e in fev),
+               "route_attend_causal" if args.routing == "causal" else "route_attend": avg((e[2], e[3]) for e in fev)}
     if L.do is not None:
         for k, name in enumerate(("attend_bwd_dq", "attend_bwd_order", "attend_bwd_dkdv", "attend_bwd_finalize")):
             kern_ms[name] = avg((e[2 * k], e[2 * k + 1]) for e in bev)

@@ -198,6 +198,25 @@ int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, cons
                 void* stream);
 
 /*
+ * hga_forward_causal -- hga_forward with strictly causal routing: the summaries of
+ * the active segment, then the routing of every query block by the rows of the block
+ * before it (as hga_route_causal; the side channel of block-level routing is the
+ * subject of the seventnews article's section "一个真正的警告：因果泄露") and the
+ * attention (as hga_attend_fwd).  With bf16 and 4 query heads per KV head a
+ * (sequence, KV head, query block) is routed and attended in one work-group, which
+ * reads the routing rows and then its own rows; other shapes run the two kernels.
+ * Outputs equal those of hga_build_summaries, hga_route_causal and hga_attend_fwd
+ * (bit for bit).
+ *   q_prev  [B, Hq, 64, d] read, as hga_route_causal: required when t_hist > 0
+ *           (HGA_ERR_NULL if NULL), ignored when t_hist == 0.
+ * Other arguments, events, requirements and errors as hga_forward.
+ */
+int hga_forward_causal(const hga_shape* shape, const void* q, const void* q_prev, const void* k_cache,
+                       const void* v_cache, void* chunk_sum, void* group_sum, int64_t t_cap, int64_t t_hist,
+                       int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
+                       void* const* events, void* stream);
+
+/*
  * Host-RAM history tier.  The pages keep older K/V in RAM or on NVMe and bring
  * only what the routing selects (adnankhan.ai note, "Raw Abstract / Excerpt";
  * seventnews, "HGA的不同之处").  With this tier the detached history's K/V live in

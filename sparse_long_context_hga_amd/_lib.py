@@ -98,6 +98,7 @@ SIGNATURES = {
     "hga_route_causal": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "hga_attend_fwd": (ctypes.c_int, [_SHAPE, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "hga_forward": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "hga_forward_causal": (ctypes.c_int, [_SHAPE, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "hga_stage_history": (ctypes.c_int, [_SHAPE, _P, _P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P]),
     "hga_stage_history_min": (ctypes.c_int64, [_SHAPE, _I64, _I64]),
     "hga_attend_bwd_workspace_size": (ctypes.c_size_t, [_SHAPE, _I64, _I64]),
@@ -271,6 +272,24 @@ def hga_forward(shape: HgaShape, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     _check(fn, lib().hga_forward(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum), t_cap, t_hist,
         seg_len, _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), handles, _stream(stream)))
+
+
+def hga_forward_causal(shape: HgaShape, q: torch.Tensor, q_prev: Optional[torch.Tensor], k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, chunk_sum: torch.Tensor, group_sum: torch.Tensor, t_cap: int,
+                       t_hist: int, seg_len: int, chunk_idx: Optional[torch.Tensor], group_idx: Optional[torch.Tensor],
+                       o: torch.Tensor, lse: torch.Tensor, events=None, stream=None) -> None:
+    """hga_forward with strictly causal routing (each block routed by the block before
+    it, q_prev [B, Hq, 64, d] for the first; needed when t_hist > 0)."""
+    fn = "hga_forward_causal"
+    dev = _dev_of(q, k_cache, v_cache)
+    _route_checks(fn, shape, dev, q, chunk_sum, group_sum, t_cap, seg_len, chunk_idx, group_idx, None, None)
+    _attend_checks(fn, shape, dev, q, k_cache, v_cache, t_cap, seg_len, group_idx, o, lse)
+    B, Hq, _, d = _dims(shape)
+    _need(fn, "q_prev", q_prev, _float_dtype(shape), B * Hq * 64 * d, dev, optional=t_hist == 0)
+    handles = None if events is None else _event_handles(events, HGA_FWD_EVENTS, stream)
+    _check(fn, lib().hga_forward_causal(
+        ctypes.byref(shape), _ptr(q), _ptr(q_prev), _ptr(k_cache), _ptr(v_cache), _ptr(chunk_sum), _ptr(group_sum),
+        t_cap, t_hist, seg_len, _ptr(chunk_idx), _ptr(group_idx), _ptr(o), _ptr(lse), handles, _stream(stream)))
 
 
 def hga_stage_history_min(shape: HgaShape, t_hist: int, seg_len: int) -> int:

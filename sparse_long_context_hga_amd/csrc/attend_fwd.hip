@@ -288,8 +288,10 @@ __global__ __launch_bounds__(128 * HPW, 8 / (2 * HPW) > 1 ? 8 / (2 * HPW) : 1) v
 // waves).  The routing waves hold row tiles {w % 4, w % 4 + 4}; wave w attends with
 // row tile w, one of the two, so the query rows are read once for both phases.  The
 // summary batch buffers of the routing are the attention's tile buffer sets 0 and 1;
-// the own chunk's tile is copied into set 2 once the chunk scores are in.
-template <int D>
+// the own chunk's tile is copied into set 2 once the chunk scores are in.  With LAG
+// (strictly causal routing, ra.lag == 1) the block is routed by the rows of the block
+// before it, and the attention then reads the block's own rows.
+template <int D, bool LAG>
 __global__ __launch_bounds__(512, 1) void route_attend_bf16_kernel(RouteArgs ra, FwdArgs a) {
   constexpr int G = 4;
   constexpr int KS = D / 16;
@@ -317,8 +319,18 @@ __global__ __launch_bounds__(512, 1) void route_attend_bf16_kernel(RouteArgs ra,
   for (int i = tid; i < ng; i += 512) sgid[i] = 8 * sm.csel[sm.gsel[i] >> 3] + (sm.gsel[i] & 7);
   __syncthreads();
   bf16x8 qf[KS];
+  if constexpr (LAG) {
+    // row tile w of the block itself: query head w / 2 of the group, rows 32 (w % 2) ..
+    const int l = tid & 63, h = l >> 5, n = l & 31;
+    const int j = unit % a.nb, bh = unit / a.nb, b = bh / a.Hkv, kvh = bh % a.Hkv;
+    const uint16_t* qp = (const uint16_t*)a.q +
+        ((((int64_t)b * a.Hq + kvh * G + (w >> 1)) * a.seg_len) + (int64_t)j * kQBlock + 32 * (w & 1) + n) * D;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = w < 4 ? qr[0][ks] : qr[1][ks];
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = w < 4 ? qr[0][ks] : qr[1][ks];
+  }
   attend_unit_bf16<D, G, G>(a, unit, 0, qf, sgid, __builtin_amdgcn_readfirstlane(ng), KB, VB);
 }
 
@@ -408,21 +420,21 @@ hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void
              : launch_kernel_timed(attend_fwd_f32_kernel<64>, dim3(grid), dim3(64 * d.G), s, start, stop, a, d.G);
 }
 
-hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* k, const void* v, void* chunk_sum,
-                          void* group_sum, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
-                          hipStream_t s, const hipEvent_t* ev) {
+hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* q_prev, bool causal, const void* k,
+                          const void* v, void* chunk_sum, void* group_sum, int32_t* chunk_idx, int32_t* group_idx,
+                          void* o, float* lse, hipStream_t s, const hipEvent_t* ev) {
   const hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   const hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
   hipError_t e = launch_summaries(d, bf16, k, d.t_hist, d.t_hist + d.seg_len, group_sum, chunk_sum, s, e0, e1);
   if (e != hipSuccess) return e;
   if (!(bf16 && d.G == 4)) {
-    e = launch_route(d, bf16, q, nullptr, false, chunk_sum, group_sum, chunk_idx, group_idx, nullptr, nullptr, s,
+    e = launch_route(d, bf16, q, q_prev, causal, chunk_sum, group_sum, chunk_idx, group_idx, nullptr, nullptr, s,
                      e2, nullptr);
     if (e != hipSuccess) return e;
     return launch_attend_fwd(d, bf16, q, k, v, group_idx, o, lse, s, nullptr, e3);
   }
   RouteArgs ra;
-  ra.q = q; ra.q_prev = nullptr; ra.lag = 0;
+  ra.q = q; ra.q_prev = q_prev; ra.lag = causal ? 1 : 0;
   ra.csum = chunk_sum; ra.gsum = group_sum;
   ra.cidx = chunk_idx; ra.gidx = group_idx; ra.cscore = nullptr; ra.gscore = nullptr;
   ra.t_cap = d.t_cap; ra.t_hist = d.t_hist; ra.seg_len = d.seg_len;
@@ -430,8 +442,11 @@ hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* k
   ra.n_units = d.B * d.Hkv * d.nb;
   const FwdArgs a = fwd_args(d, q, k, v, group_idx, o, lse);
   const dim3 grid(xcd_grid(a.n_units));
-  return d.D == 128 ? launch_kernel_timed(route_attend_bf16_kernel<128>, grid, dim3(512), s, e2, e3, ra, a)
-                    : launch_kernel_timed(route_attend_bf16_kernel<64>, grid, dim3(512), s, e2, e3, ra, a);
+  if (causal)
+    return d.D == 128 ? launch_kernel_timed(route_attend_bf16_kernel<128, true>, grid, dim3(512), s, e2, e3, ra, a)
+                      : launch_kernel_timed(route_attend_bf16_kernel<64, true>, grid, dim3(512), s, e2, e3, ra, a);
+  return d.D == 128 ? launch_kernel_timed(route_attend_bf16_kernel<128, false>, grid, dim3(512), s, e2, e3, ra, a)
+                    : launch_kernel_timed(route_attend_bf16_kernel<64, false>, grid, dim3(512), s, e2, e3, ra, a);
 }
 
 }  // namespace hga

@@ -118,9 +118,10 @@ int hga_attend_fwd(const hga_shape* shape, const void* q, const void* k_cache, c
                                            lse, (hipStream_t)stream));
 }
 
-int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache, void* chunk_sum,
-                void* group_sum, int64_t t_cap, int64_t t_hist, int64_t seg_len, int32_t* chunk_idx,
-                int32_t* group_idx, void* o, float* lse, void* const* events, void* stream) {
+static int forward_impl(const hga_shape* shape, const void* q, const void* q_prev, bool causal, const void* k_cache,
+                        const void* v_cache, void* chunk_sum, void* group_sum, int64_t t_cap, int64_t t_hist,
+                        int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
+                        void* const* events, void* stream) {
   hga::Dims d;
   int st = resolve(shape, t_cap, t_hist, seg_len, d);
   if (st != HGA_OK) return st;
@@ -129,13 +130,29 @@ int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, cons
   if (!q || !k_cache || !v_cache || !chunk_sum || !group_sum || !o || !lse || (d.kc > 0 && !chunk_idx) ||
       (d.kg > 0 && !group_idx))
     return HGA_ERR_NULL;
+  if (causal && t_hist > 0 && !q_prev) return HGA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(chunk_sum) ||
       !aligned16(group_sum) || !aligned16(o) || !aligned16(lse) || (chunk_idx && !aligned16(chunk_idx)) ||
-      (group_idx && !aligned16(group_idx)))
+      (group_idx && !aligned16(group_idx)) || (causal && q_prev && !aligned16(q_prev)))
     return HGA_ERR_ALIGN;
-  return hip_status(hga::launch_forward(d, shape->dtype == HGA_BF16, q, k_cache, v_cache, chunk_sum, group_sum,
-                                        chunk_idx, group_idx, o, lse, (hipStream_t)stream,
-                                        (const hipEvent_t*)events));
+  return hip_status(hga::launch_forward(d, shape->dtype == HGA_BF16, q, causal ? q_prev : nullptr, causal, k_cache,
+                                        v_cache, chunk_sum, group_sum, chunk_idx, group_idx, o, lse,
+                                        (hipStream_t)stream, (const hipEvent_t*)events));
+}
+
+int hga_forward(const hga_shape* shape, const void* q, const void* k_cache, const void* v_cache, void* chunk_sum,
+                void* group_sum, int64_t t_cap, int64_t t_hist, int64_t seg_len, int32_t* chunk_idx,
+                int32_t* group_idx, void* o, float* lse, void* const* events, void* stream) {
+  return forward_impl(shape, q, nullptr, false, k_cache, v_cache, chunk_sum, group_sum, t_cap, t_hist, seg_len,
+                      chunk_idx, group_idx, o, lse, events, stream);
+}
+
+int hga_forward_causal(const hga_shape* shape, const void* q, const void* q_prev, const void* k_cache,
+                       const void* v_cache, void* chunk_sum, void* group_sum, int64_t t_cap, int64_t t_hist,
+                       int64_t seg_len, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
+                       void* const* events, void* stream) {
+  return forward_impl(shape, q, q_prev, true, k_cache, v_cache, chunk_sum, group_sum, t_cap, t_hist, seg_len,
+                      chunk_idx, group_idx, o, lse, events, stream);
 }
 
 int64_t hga_stage_history_min(const hga_shape* shape, int64_t t_hist, int64_t seg_len) {

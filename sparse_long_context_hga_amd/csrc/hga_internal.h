@@ -51,13 +51,14 @@ hipError_t launch_attend_fwd(const Dims& d, bool bf16, const void* q, const void
                              hipEvent_t stop = nullptr);
 
 // The forward of a segment: summaries of the active segment [t_hist, t_hist +
-// seg_len), then routing and attention (one kernel that does both per unit for
-// bf16 with 4 query heads per KV head, else the route and attention kernels).
+// seg_len), then routing (by each block's own rows, or with causal by the block
+// before it, q_prev for the first) and attention: one kernel that does both per unit
+// for bf16 with 4 query heads per KV head, else the route and attention kernels.
 // ev: null, or 4 events: [0], [1] around the summaries, [2] at the start of the
 // routing and [3] at the end of the attention.
-hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* k, const void* v, void* chunk_sum,
-                          void* group_sum, int32_t* chunk_idx, int32_t* group_idx, void* o, float* lse,
-                          hipStream_t s, const hipEvent_t* ev);
+hipError_t launch_forward(const Dims& d, bool bf16, const void* q, const void* q_prev, bool causal, const void* k,
+                          const void* v, void* chunk_sum, void* group_sum, int32_t* chunk_idx, int32_t* group_idx,
+                          void* o, float* lse, hipStream_t s, const hipEvent_t* ev);
 
 // Host-RAM history tier: the selected history groups of every (sequence, KV head)
 // copied from host memory into a staging cache, and the selection renumbered for it.

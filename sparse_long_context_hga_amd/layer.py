@@ -99,6 +99,13 @@ class HGALayerBuffers:
         L.hga_forward(self.shape, self.q, self.k, self.v, self.csum, self.gsum, self.t_cap, self.t_hist,
                       self.seg_len, self.cidx, self.gidx, self.o, self.lse, events)
 
+    def forward_causal(self, q_prev: Optional[torch.Tensor], events=None):
+        """hga_forward with strictly causal routing (hga_forward_causal): block j routed
+        by block j-1, the first block by q_prev (needed when t_hist > 0)."""
+        L.hga_forward_causal(self.shape, self.q, q_prev if self.t_hist > 0 else None, self.k, self.v, self.csum,
+                             self.gsum, self.t_cap, self.t_hist, self.seg_len, self.cidx, self.gidx, self.o,
+                             self.lse, events)
+
     def bwd(self, gidx: Optional[torch.Tensor] = None, events=None):
         g = self.gidx if gidx is None else gidx
         if events is None:
@@ -298,10 +305,10 @@ class _HGAAttentionFn(torch.autograd.Function):
             ctx.mark_non_differentiable(lse, gidx)
             return o, lse, gidx
         if causal_routing:
-            t_hist = cache.write(k_seg, v_seg, shape)
-            L.hga_route_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.csum, cache.gsum,
-                               cache.t_cap, t_hist, S, cidx, gidx)
-            L.hga_attend_fwd(shape, q, cache.k, cache.v, cache.t_cap, t_hist, S, gidx, o, lse)
+            # summaries of the segment, causal routing and attention in one call
+            t_hist = cache.write(k_seg, v_seg, shape, summaries=False)
+            L.hga_forward_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.k, cache.v, cache.csum,
+                                 cache.gsum, cache.t_cap, t_hist, S, cidx, gidx, o, lse)
         else:
             # summaries of the segment, routing and attention in one call
             t_hist = cache.write(k_seg, v_seg, shape, summaries=False)

@@ -28,7 +28,8 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert set(names) == {"hga_build_summaries", "hga_forward", "hga_stage_history", "hga_stage_history_min",
+    assert set(names) == {"hga_build_summaries", "hga_forward", "hga_forward_causal", "hga_stage_history",
+                          "hga_stage_history_min",
                           "hga_route", "hga_route_causal", "hga_attend_fwd",
                           "hga_attend_bwd_workspace_size", "hga_attend_bwd", "hga_attend_bwd_timed",
                           "hga_decode_step", "hga_decode_route", "hga_decode_attend", "hga_decode_workspace_size",
@@ -99,6 +100,37 @@ def test_route_causal_validation(L):
     assert call(t_hist=100) == -2
     assert call(shape=_shape(n_q_heads=24)) == -3
     assert f(None, A, A, A, A, 16384, 0, 2048, A, A, None, None, None) == -1
+
+
+def test_forward_validation(L):
+    """hga_forward and hga_forward_causal (the causal one also needs q_prev over history)."""
+    s = _shape()
+
+    def fwd(q=A, k=A, cs=A, t_cap=16384, t_hist=14336, seg=2048, cidx=A, gidx=A, o=A, shape=s):
+        return L.hga_forward(ctypes.byref(shape) if shape is not None else None, q, k, A, cs, A, t_cap, t_hist,
+                             seg, cidx, gidx, o, A, None, None)
+
+    def fwdc(q_prev=A, q=A, k=A, t_hist=14336, seg=2048, gidx=A, shape=s):
+        return L.hga_forward_causal(ctypes.byref(shape), q, q_prev, k, A, A, A, 16384, t_hist, seg, A, gidx, A, A,
+                                    None, None)
+    for f in (fwd, fwdc):
+        assert f(q=None) == -1
+        assert f(k=None) == -1
+        assert f(gidx=None) == -1
+        assert f(q=M) == -5
+        assert f(k=M) == -5
+        assert f(t_hist=100) == -2
+        assert f(seg=0) == -2
+        assert f(shape=_shape(n_q_heads=24)) == -3
+        assert f(shape=_shape(top_groups=129)) == -2
+    assert fwd(shape=None) == -1
+    assert fwd(cs=None) == -1
+    assert fwd(cidx=None) == -1
+    assert fwd(o=None) == -1
+    assert fwd(t_hist=16384) == -4
+    assert fwd(t_cap=1 << 20, t_hist=1 << 19) == -3        # more chunks than the router takes
+    assert fwdc(q_prev=None) == -1                          # history present: the previous block is needed
+    assert fwdc(q_prev=M) == -5
 
 
 def test_summaries_validation(L):

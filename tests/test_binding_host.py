@@ -44,6 +44,12 @@ def test_wrappers_reject_host_tensors_before_the_library():
     q = torch.zeros(1, 4, 128, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="ROCm device"):
         hga.hga_route(s, q, cs, gs, 256, 128, 128, None, None)
+    cidx = torch.zeros(1, 1, 2, 2, dtype=torch.int32)
+    gidx = torch.zeros(1, 1, 2, 8, dtype=torch.int32)
+    o = torch.zeros_like(q)
+    lse = torch.zeros(1, 4, 128, dtype=torch.float32)
+    with pytest.raises(ValueError, match="ROCm device"):
+        hga.hga_forward_causal(s, q, None, k, k, cs, gs, 256, 128, 128, cidx, gidx, o, lse)
 
 
 def test_layer_op_rejects_mismatches_before_any_launch():

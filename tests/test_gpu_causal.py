@@ -10,7 +10,9 @@ segment's first block), everything else as block routing.
     position p of a block changes the outputs at positions <= p under block
     routing, and leaves them bit-identical under causal routing;
   * the 16K-context layer: every unit accepted, forward on sampled units;
-  * two segments through the autograd op with causal routing.
+  * two segments through the autograd op with causal routing;
+  * hga_forward_causal (summaries, causal routing and attention in one call) bit for
+    bit against the separate calls, on every parity layer and the 16K layer.
 Expected values come only from the oracle.
 """
 import numpy as np
@@ -204,3 +206,30 @@ def test_two_segments_causal_through_autograd(chk):
     cache2.length = S
     with pytest.raises(ValueError):
         hga_attention(q1, k1, v1, cache2, w.top_chunks, w.top_groups, causal_routing=True)
+
+
+def _fused_vs_separate(chk, w, q_prev):
+    qp = chk.to_dev(q_prev, w.dtype) if w.t_hist > 0 else None
+    A = chk.DeviceLayer(w)
+    A.summaries(0, w.t_hist + w.seg_len)
+    A.route_causal(qp)
+    A.fwd()
+    B = chk.DeviceLayer(w)
+    B.summaries(0, w.t_hist)
+    B.forward_causal(qp)
+    torch.cuda.synchronize()
+    for field in ("gsum", "csum", "cidx", "gidx", "o", "lse"):
+        assert torch.equal(getattr(A, field), getattr(B, field)), f"hga_forward_causal: {field} differs"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_causal_matches_separate_calls(chk, name):
+    w = hi.random_layer(name=name, **CASES[name])
+    print(f"case {name}", flush=True)
+    _fused_vs_separate(chk, w, _q_prev(w, seed=CASES[name]["seed"]))
+
+
+def test_forward_causal_qwen3_8b_layer_ctx16k(chk):
+    w = hi.qwen_16k()
+    print(f"workload {w.name} (hga_forward_causal)", flush=True)
+    _fused_vs_separate(chk, w, _q_prev(w, seed=33))

@@ -8,7 +8,7 @@ block-structured keys.  Each example checks every step against the oracle:
 - routing on the oracle's summaries, accepted with the near-tie rule;
 - the forward and the backward on the oracle's selection, to the parity tolerances
   (per query block and per active chunk for the gradients);
-- hga_forward bit for bit against the separate calls.
+- hga_forward and hga_forward_causal bit for bit against the separate calls.
 
 HGA_HYPOTHESIS_EXAMPLES sets the number of examples (default 100; 600 have been run).
 """
@@ -95,3 +95,19 @@ def test_random_small_layer(chk, kw):
     torch.cuda.synchronize()
     for field in ("gsum", "csum", "cidx", "gidx", "o", "lse"):
         assert torch.equal(getattr(A, field), getattr(B, field)), f"hga_forward: {field} differs"
+
+    # hga_forward_causal against summaries + hga_route_causal + hga_attend_fwd
+    qp = None
+    if w.t_hist > 0:
+        qp = chk.to_dev(hi.prev_query_block(seed=kw["seed"] + 1, batch=w.batch, n_q_heads=w.n_q_heads,
+                                            head_dim=w.head_dim, dtype=w.dtype), w.dtype)
+    A = chk.DeviceLayer(w)
+    A.summaries(0, T)
+    A.route_causal(qp)
+    A.fwd()
+    B = chk.DeviceLayer(w)
+    B.summaries(0, w.t_hist)
+    B.forward_causal(qp)
+    torch.cuda.synchronize()
+    for field in ("gsum", "csum", "cidx", "gidx", "o", "lse"):
+        assert torch.equal(getattr(A, field), getattr(B, field)), f"hga_forward_causal: {field} differs"
