@@ -134,7 +134,6 @@ def algorithmic_work(w, gidx):
         "attend_bwd_dq": {"bytes": dq_bytes, "flops": dq_flops, "gather_bytes": kv_sel},
         "attend_bwd_dkdv": {"bytes": dkdv_bytes, "flops": dkdv_flops},
         # the work list and the partial sums are not part of the method
-        "attend_bwd_order": {"bytes": 0.0, "flops": 0.0},
         "attend_bwd_finalize": {"bytes": 0.0, "flops": 0.0},
     }
 
@@ -148,7 +147,7 @@ CSRC = os.path.join(ROOT, "sparse_long_context_hga_amd", "csrc")
 # kernel-name prefix -> step kernel (first match wins)
 KERNEL_KEYS = [("summaries_kernel", "summaries"), ("route_attend_", "route_attend"), ("route_", "route"),
                ("attend_fwd_", "attend_fwd"),
-               ("attend_bwd_dq_", "attend_bwd_dq"), ("attend_bwd_order_", "attend_bwd_order"),
+               ("attend_bwd_dq_", "attend_bwd_dq"),
                ("attend_bwd_dkdv_finalize", "attend_bwd_finalize"), ("attend_bwd_dkdv_", "attend_bwd_dkdv"),
                ("decode_route_kernel", "decode_route"), ("decode_attend_kernel", "decode_attend")]
 
@@ -785,6 +784,7 @@ def main_host_tier(args):
     dk = torch.empty(B, Hkv, S, d, dtype=dt, device="cuda")
     dv = torch.empty_like(dk)
     ws = torch.empty(hga.hga_attend_bwd_workspace_size(shape, sh, S), dtype=torch.uint8, device="cuda")
+    ws[:hga.HGA_BWD_WORKSPACE_CLEAR_BYTES].zero_()
     stream = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
 
@@ -962,7 +962,7 @@ def main():
     kern_ms = {"summaries": avg((e[0], e[1]) for e in fev),
                "route_attend_causal" if args.routing == "causal" else "route_attend": avg((e[2], e[3]) for e in fev)}
     if L.do is not None:
-        for k, name in enumerate(("attend_bwd_dq", "attend_bwd_order", "attend_bwd_dkdv", "attend_bwd_finalize")):
+        for k, name in enumerate(("attend_bwd_dq", "attend_bwd_dkdv", "attend_bwd_finalize")):
             kern_ms[name] = avg((e[2 * k], e[2 * k + 1]) for e in bev)
 
     gidx = L.gidx.cpu().numpy()

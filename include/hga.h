@@ -254,6 +254,11 @@ int hga_stage_history(const hga_shape* shape, const void* k_host, const void* v_
 int64_t hga_stage_history_min(const hga_shape* shape, int64_t t_hist, int64_t seg_len);
 
 /* Bytes of device workspace hga_attend_bwd needs (16-byte aligned); 0 on bad shape. */
+/* The workspace's first HGA_BWD_WORKSPACE_CLEAR_BYTES bytes hold counters that must
+ * be zero before the workspace's first use; every call that returns HGA_OK leaves
+ * them zero again, so one workspace serves any number of calls, of any shapes, with
+ * no clearing in between. */
+#define HGA_BWD_WORKSPACE_CLEAR_BYTES 256
 size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int64_t seg_len);
 
 /*
@@ -270,8 +275,13 @@ size_t hga_attend_bwd_workspace_size(const hga_shape* shape, int64_t t_hist, int
  *   dk_active, dv_active [B, Hkv, seg_len, d]  written: gradients of the active
  *              keys/values k_cache[:, :, t_hist + i] (summed over every query
  *              row that attends them, across blocks and query heads)
- *   workspace  device scratch of at least hga_attend_bwd_workspace_size() bytes
- * The result is deterministic (no floating-point atomics).
+ *   workspace  device scratch of at least hga_attend_bwd_workspace_size() bytes, at
+ *              least 16-byte aligned, whose first HGA_BWD_WORKSPACE_CLEAR_BYTES bytes
+ *              are zero (see above).  After HGA_ERR_HIP (a launch rejected once
+ *              earlier kernels of the call were enqueued) clear them again.  Calls
+ *              that share a workspace must not run concurrently.
+ * The result is deterministic (no floating-point atomics; the work items' order
+ * among the dK/dV work-groups varies, but each writes only its own output).
  */
 int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache,
                    const void* v_cache, const void* o, const float* lse, const void* d_o,
@@ -282,14 +292,14 @@ int hga_attend_bwd(const hga_shape* shape, const void* q, const void* k_cache,
 /*
  * hga_attend_bwd_timed -- hga_attend_bwd, plus per-kernel timing marks: for
  * kernel i of the backward (HGA_BWD_KERNELS of them, in launch order: 0 dQ,
- * rowsum(dO*O) and the selection inverse, 1 the dK/dV work list, 2 dK/dV, 3 dK/dV
+ * rowsum(dO*O), the selection inverse and the dK/dV work list, 1 dK/dV, 2 dK/dV
  * partial sums) events[2i] is recorded on `stream` just before its launch and
  * events[2i+1] just after; a kernel that a dtype's path does not launch (the fp32
- * path has no work list and no partial sums) gets its two marks back to back.  events:
+ * path has no partial sums) gets its two marks back to back.  events:
  * 2*HGA_BWD_KERNELS hipEvent_t handles created by the caller (NULL entries are
  * skipped).  Everything else as hga_attend_bwd.
  */
-#define HGA_BWD_KERNELS 4
+#define HGA_BWD_KERNELS 3
 int hga_attend_bwd_timed(const hga_shape* shape, const void* q, const void* k_cache,
                          const void* v_cache, const void* o, const float* lse, const void* d_o,
                          int64_t t_cap, int64_t t_hist, int64_t seg_len, const int32_t* group_idx,

@@ -349,7 +349,8 @@ def hga_attend_bwd(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_cap: int
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-HGA_BWD_KERNELS = 4
+HGA_BWD_KERNELS = 3
+HGA_BWD_WORKSPACE_CLEAR_BYTES = 256   # leading workspace bytes that must be zero before first use
 
 
 def hga_attend_bwd_timed(shape: HgaShape, q, k_cache, v_cache, o, lse, d_o, t_cap: int, t_hist: int,

@@ -9,7 +9,7 @@
 //   dQ = scale sum_t dS k_t;   for active t:  dV_t = sum P dO,  dK_t = scale sum dS q
 // History tokens (< t_hist) receive nothing.
 //
-// bf16 path: four kernels, deterministic (no floating-point atomics):
+// bf16 path: three kernels, deterministic (no floating-point atomics):
 //  * dq (query-major, one work-group per (sequence, KV head, query block) and
 //    query-head slice): the forward's gathered tiles again; recomputes P from
 //    LSE; writes dQ, and D = rowsum(dO * O) and -LSE log2(e) (workspace) for the
@@ -17,15 +17,15 @@
 //    also inverts the selection for the active chunk of its own block -- the
 //    ascending list of query blocks that attend the chunk -- and cuts the
 //    chunk's work into 1..8 items of about 12 or 16 "rounds" (one round = the 64 rows
-//    of one query head of one attending block);
-//  * order (one work-group): lists all items by size, largest first, so that
-//    the dK/dV grid starts with the heaviest items;
-//  * dkdv (one work-group per item): the chunk's 64 keys and values stay in
+//    of one query head of one attending block), filed by size class;
+//  * dkdv (one work-group per item, the largest size class first, so that the
+//    grid starts with the heaviest items): the chunk's 64 keys and values stay in
 //    registers; the item's rounds stream Q / dO rows through swizzled LDS; dK,
 //    dV accumulate in fp32 registers (dV^T += dO^T P, dK^T += Q^T dS, the
 //    transposing LDS reads supplying the k-contiguous operands); a chunk done
 //    by one item writes bf16 dK/dV, otherwise each item writes an fp32 partial;
-//  * finalize: sums a chunk's partials in item order and writes bf16 dK/dV.
+//  * finalize: sums a chunk's partials in item order and writes bf16 dK/dV, and
+//    returns the class counts to zero for the next call.
 // fp32 path: two plain SIMT kernels (dQ, dK/dV), fp32 throughout.
 #include <hip/hip_ext.h>
 
@@ -49,7 +49,7 @@ constexpr int kMaxBlocks = 1024;   // query blocks per segment supported by the 
 constexpr int kTargetRoundsLongHistory = 12;
 constexpr int kTargetRoundsShortHistory = 16;
 constexpr int kMaxParts = 8;       // at most this many items per active chunk
-constexpr int kBuckets = 64;       // work-list size classes (rounds per work item, capped)
+constexpr int kClasses = 16;       // work-list size classes (rounds per work item, capped at 15)
 
 struct BwdArgs {
   const void* q;
@@ -65,12 +65,10 @@ struct BwdArgs {
   float* dvec;      // [B, Hq, S] rowsum(dO * O)            (workspace)
   float* nlse;      // [B, Hq, S] -LSE * log2(e), the exponent offset of P in base 2 (workspace)
   int* flags;       // [B, Hkv, S/64] number of work items of the chunk's dK/dV (workspace)
-  int* nvis;        // [B, Hkv, S/64] number of blocks attending each active chunk (workspace)
   int* vis;         // [B, Hkv, S/64, S/64] attending blocks, ascending: block | group mask << 16
-  int* first;       // [B, Hkv, S/64, kMaxParts] per item: the block of its first round
-  int* order;       // [4 + 4*B*Hkv*S/64*kMaxParts] number of work items (padded to 16 bytes), then the
-                    // items heaviest first, each {unit * kMaxParts + part, parts of the unit, visits of the unit,
-                    // the item's entry of `first`}
+  int* cls_count;   // [kClasses] work items filed per size class; zero between calls (workspace start)
+  int4* cls_items;  // [kClasses, B*Hkv*S/64*kMaxParts] the items of each class, each {unit * kMaxParts +
+                    // part, parts of the unit, visits of the unit, the block of the item's first round}
   float* parts;     // [B, Hkv, S/64, kMaxParts, 2, 64, d] fp32 partials (workspace)
   int64_t t_cap, t_hist, seg_len;
   int Hq, Hkv, kg, nb, n_units;
@@ -97,10 +95,12 @@ __device__ __forceinline__ float dot8_bf16(bf16x8 x, bf16x8 y) {
 // dK/dV is cut.  Runs inside the dQ kernel (one of the work-groups of unit (bh, cc))
 // before its tile pipeline; gv holds this thread's first group ids of the later
 // blocks, loaded early so that their latency overlaps the dQ kernel's own loads.
+// The chunk's work items go to LDS (item_cls[k]: size class of item k, or -1 past
+// the last item; item_entry[k]: its work-list entry) for the caller to file.
 constexpr int kPlanLoads = 8;
 template <int NT, int G>
 __device__ __forceinline__ void plan_chunk(const BwdArgs& a, int bh, int cc, const int32_t (&gv)[kPlanLoads],
-                                           uint32_t* mask) {
+                                           uint32_t* mask, int* item_cls, int4* item_entry) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int64_t g_lo = (a.t_hist / kChunk + cc) * 8;
   const int32_t* g0 = a.gidx + ((int64_t)bh * a.nb + cc + 1) * a.kg;
@@ -139,16 +139,17 @@ __device__ __forceinline__ void plan_chunk(const BwdArgs& a, int bh, int cc, con
     n += __popcll(bal);
   }
   // G rounds (query heads) per attending block (n >= 1: the own block), cut into np
-  // items of about a.target_rounds; item k starts at round k * rounds / np.  The block
-  // of every item's first round goes into the work list, so that the dK/dV kernel can
-  // start its copies before it has read the visit list.
+  // items of about a.target_rounds; item k starts at round k * rounds / np, and its
+  // size class is its number of rounds (capped).  The entry carries the block of the
+  // item's first round, so that the dK/dV kernel can start its copies before it has
+  // read the visit list.
   const int rounds = G * n;
   const int np = min(kMaxParts, (rounds + a.target_rounds - 1) / a.target_rounds);
-  if (l < np) a.first[(int64_t)unit * kMaxParts + l] = (int)mask[cc + (l * rounds / np) / G];
-  if (l == 0) {
-    a.nvis[unit] = n;
-    a.flags[unit] = np;
+  if (l < kMaxParts) {
+    item_cls[l] = l < np ? min(kClasses - 1, (l + 1) * rounds / np - l * rounds / np) : -1;
+    if (l < np) item_entry[l] = make_int4(unit * kMaxParts + l, np, n, (int)mask[cc + (l * rounds / np) / G]);
   }
+  if (l == 0) a.flags[unit] = np;
 }
 
 // ---------------------------------------------------------------- dQ (bf16)
@@ -233,7 +234,9 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 
   const int n_valid = __builtin_amdgcn_readfirstlane(
       count_valid<NT>(a.gidx + (int64_t)unit * a.kg, a.kg, sgid));   // ends with a barrier
-  if (do_plan) plan_chunk<NT, G>(a, bh, j, pgv, pmask);
+  __shared__ int item_cls[kMaxParts];
+  __shared__ int4 item_entry[kMaxParts];
+  if (do_plan) plan_chunk<NT, G>(a, bh, j, pgv, pmask, item_cls, item_entry);
   const int n_sel_tiles = (n_valid + 7) >> 3;
   const int n_tiles = n_sel_tiles + 1;
   // Tile t: 8 selected groups, or the own chunk as the last tile; slots past the
@@ -326,6 +329,18 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 
   pipeline<kStages, 2 * BPW>(n_tiles, issue, compute);
 
+  // File the chunk's work items under their size classes, at the positions an
+  // atomic count of each class gives them (the order within a class is immaterial:
+  // every item writes its own output or partial).  Only the dK/dV kernel reads
+  // them, so this waits until the tiles are done, and the atomics' round trip
+  // overlaps the dQ stores below.
+  int pcls = -1;
+  uint32_t pslot = 0;
+  if (do_plan && w == 0 && l < kMaxParts) {
+    pcls = item_cls[l];
+    if (pcls >= 0)
+      pslot = (uint32_t)__hip_atomic_fetch_add(a.cls_count + pcls, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // dQ leaves through this wave's 32-row LDS region as whole rows; the barrier keeps
   // every region free until all waves have finished their last tile.
   tile_barrier();
@@ -333,6 +348,9 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
     return f32x4_to_bf16x4_bits(dqacc[dt][4 * g] * a.scale, dqacc[dt][4 * g + 1] * a.scale,
                                 dqacc[dt][4 * g + 2] * a.scale, dqacc[dt][4 * g + 3] * a.scale);
   });
+  const uint32_t cap = (uint32_t)a.n_units * kMaxParts;
+  if (pcls >= 0 && pslot < cap)   // (always below cap when the counts started the call at zero)
+    a.cls_items[(int64_t)pcls * cap + pslot] = item_entry[l];
 }
 
 // ---------------------------------------------------------------- dK/dV (bf16)
@@ -349,80 +367,20 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
 // more copies in flight per CU, and those delay the ones the current round waits
 // for).
 
-struct DkdvLayout {   // byte offsets in the workspace after the rowsum(dO*O) vector
+// Workspace layout (byte offsets).  The class counts come first, at the same place
+// for every shape, so that a workspace reused across shapes keeps them at zero.
+struct DkdvLayout {
   static size_t up(size_t x) { return (x + 255) & ~(size_t)255; }
-  static size_t nlse_off(size_t rows) { return up(rows * 4); }
+  static constexpr size_t dvec_off = 256;   // after the kClasses counts
+  static size_t nlse_off(size_t rows) { return up(dvec_off + rows * 4); }
   static size_t flags_off(size_t rows) { return up(nlse_off(rows) + rows * 4); }
-  static size_t nvis_off(size_t rows, size_t units) { return up(flags_off(rows) + units * 4); }
-  static size_t first_off(size_t rows, size_t units) { return up(nvis_off(rows, units) + units * 4); }
-  static size_t vis_off(size_t rows, size_t units) { return up(first_off(rows, units) + units * kMaxParts * 4); }
-  static size_t order_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
+  static size_t vis_off(size_t rows, size_t units) { return up(flags_off(rows) + units * 4); }
+  static size_t items_off(size_t rows, size_t units, size_t nb) { return up(vis_off(rows, units) + units * nb * 4); }
   static size_t part_off(size_t rows, size_t units, size_t nb) {
-    return up(order_off(rows, units, nb) + (4 + 4 * units * kMaxParts) * 4);
+    return up(items_off(rows, units, nb) + kClasses * units * kMaxParts * sizeof(int4));
   }
 };
-
-// The dK/dV work list: every chunk's items (item k of a chunk with R rounds cut
-// into np items has (k+1)R/np - kR/np rounds), heaviest first, so that the long
-// items start early.  One work-group; the order within one size is immaterial
-// (every item writes its own output or partial).
-constexpr int kOrderThreads = 1024;
-template <int G>
-__global__ __launch_bounds__(kOrderThreads) void attend_bwd_order_kernel(BwdArgs a) {
-  __shared__ int cnt[kBuckets];
-  const int tid = threadIdx.x, l = tid & 63;
-  if (tid < kBuckets) cnt[tid] = 0;
-  __syncthreads();
-  auto size_of = [&](int np_u, int r_u, int k) __attribute__((always_inline)) {
-    return min(kBuckets - 1, (k + 1) * r_u / np_u - k * r_u / np_u);
-  };
-  // A thread's first unit (every unit when there are at most kOrderThreads) is read
-  // once, counts and item entries together, and kept for the scatter below.
-  int np0 = 0, nv0 = 0;
-  int fst0[kMaxParts] = {};
-  static_assert(kMaxParts == 8, "two int4 per unit");
-  if (tid < a.n_units) {
-    np0 = a.flags[tid];
-    nv0 = a.nvis[tid];
-    *reinterpret_cast<int4*>(fst0) = reinterpret_cast<const int4*>(a.first)[2 * tid];
-    *reinterpret_cast<int4*>(fst0 + 4) = reinterpret_cast<const int4*>(a.first)[2 * tid + 1];
-  }
-  for (int u = tid; u < a.n_units; u += kOrderThreads) {
-    const int np_u = u == tid ? np0 : a.flags[u], r_u = G * (u == tid ? nv0 : a.nvis[u]);
-    for (int k = 0; k < np_u; ++k) atomicAdd(&cnt[size_of(np_u, r_u, k)], 1);
-  }
-  __syncthreads();
-  if (tid < 64) {   // first position of each size, largest size first
-    const int c = cnt[kBuckets - 1 - l];
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (l >= off) incl += y;
-    }
-    cnt[kBuckets - 1 - l] = incl - c;
-    if (l == 63) a.order[0] = incl;
-  }
-  __syncthreads();
-  for (int u = tid; u < a.n_units; u += kOrderThreads) {
-    int np_u = np0, nv_u = nv0;
-    int fst[kMaxParts];   // loaded whole (entries k >= np_u unused)
-#pragma unroll
-    for (int k = 0; k < kMaxParts; ++k) fst[k] = fst0[k];
-    if (u != tid) {
-      np_u = a.flags[u];
-      nv_u = a.nvis[u];
-      *reinterpret_cast<int4*>(fst) = reinterpret_cast<const int4*>(a.first)[2 * u];
-      *reinterpret_cast<int4*>(fst + 4) = reinterpret_cast<const int4*>(a.first)[2 * u + 1];
-    }
-    const int r_u = G * nv_u;
-#pragma unroll
-    for (int k = 0; k < kMaxParts; ++k)
-      if (k < np_u)
-        reinterpret_cast<int4*>(a.order + 4)[atomicAdd(&cnt[size_of(np_u, r_u, k)], 1)] =
-            make_int4(u * kMaxParts + k, np_u, nv_u, fst[k]);
-  }
-}
+static_assert(kClasses * sizeof(int) <= DkdvLayout::dvec_off, "class counts fit ahead of the row vectors");
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a) {
@@ -446,13 +404,26 @@ __global__ __launch_bounds__(256, 1) void attend_bwd_dkdv_bf16_kernel(BwdArgs a)
   };
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = l & 31;
-  // Work item number blockIdx.x of the list the order kernel wrote (heaviest first),
-  // with its unit's part and visit counts: the count and the entry are loaded
-  // together (the entry lies inside the list's capacity) and the entry is used
-  // only below the count.
-  const int n_items = a.order[0];
-  const int4 entry = reinterpret_cast<const int4*>(a.order + 4)[blockIdx.x];
-  if ((int)blockIdx.x >= n_items) return;
+  // Work item number blockIdx.x in the order of size classes, largest first (items
+  // that finish early leave their compute unit to the next ones, so the long items
+  // go first): the classes' counts locate the item's class and its place in it.
+  const uint32_t cap = (uint32_t)a.n_units * kMaxParts;
+  int4 entry;
+  {
+    const int c = l < kClasses ? a.cls_count[kClasses - 1 - l] : 0;   // lane l: the l-th largest class
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < kClasses; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (l >= off) incl += y;
+    }
+    const uint64_t past = __ballot(l < kClasses && incl > (int)blockIdx.x);
+    if (past == 0) return;                          // beyond the last item
+    const int f = __builtin_ctzll(past);
+    const uint32_t at = (uint32_t)((int)blockIdx.x - __shfl(incl - c, f, 64));
+    if (at >= cap) return;                          // (counts that did not start at zero)
+    entry = a.cls_items[(int64_t)(kClasses - 1 - f) * cap + at];
+  }
   const int item = __builtin_amdgcn_readfirstlane(entry.x);
   const int np = __builtin_amdgcn_readfirstlane(entry.y);
   const int n_visits = __builtin_amdgcn_readfirstlane(entry.z);
@@ -728,6 +699,8 @@ constexpr int kFinalizeSlices = 8;
 
 template <int D>
 __global__ __launch_bounds__(256) void attend_bwd_dkdv_finalize_kernel(BwdArgs a) {
+  // The dK/dV kernel has read the class counts: return them to zero for the next call.
+  if (blockIdx.x == 0 && threadIdx.x < kClasses) a.cls_count[threadIdx.x] = 0;
   const int unit = blockIdx.x / kFinalizeSlices;
   const int slice = blockIdx.x % kFinalizeSlices;
   if (unit >= a.n_units) return;
@@ -869,17 +842,16 @@ struct Launcher {
   }
 };
 
-// The four launches in order; the first one the runtime rejects ends the sequence,
+// The three launches in order; the first one the runtime rejects ends the sequence,
 // so no later kernel reads a workspace that an earlier one did not fill.
 template <int D, int G>
 hipError_t launch_bf16(const BwdArgs& a, const Launcher& run) {
   constexpr int HPW = G >= 8 ? 4 : G;   // query heads per dQ work-group
   hipError_t e = run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))),
                      dim3(128 * HPW), a);
-  if (e == hipSuccess) e = run(1, attend_bwd_order_kernel<G>, dim3(1), dim3(kOrderThreads), a);
-  if (e == hipSuccess) e = run(2, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
+  if (e == hipSuccess) e = run(1, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
   if (e == hipSuccess)
-    e = run(3, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
+    e = run(2, attend_bwd_dkdv_finalize_kernel<D>, dim3(a.n_units * kFinalizeSlices), dim3(256), a);
   return e;
 }
 template <int D>
@@ -910,16 +882,16 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   const Launcher run{events, s};
   BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o; a.lse = lse; a.gidx = group_idx;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dvec = (float*)workspace;
+  a.dq = dq; a.dk = dk; a.dv = dv;
   {
     const size_t rows = (size_t)d.B * d.Hq * (size_t)d.seg_len;
     const size_t units = (size_t)d.B * d.Hkv * (size_t)d.nb;
+    a.cls_count = (int*)workspace;
+    a.dvec = (float*)((char*)workspace + DkdvLayout::dvec_off);
     a.nlse = (float*)((char*)workspace + DkdvLayout::nlse_off(rows));
     a.flags = (int*)((char*)workspace + DkdvLayout::flags_off(rows));
-    a.nvis = (int*)((char*)workspace + DkdvLayout::nvis_off(rows, units));
-    a.first = (int*)((char*)workspace + DkdvLayout::first_off(rows, units));
     a.vis = (int*)((char*)workspace + DkdvLayout::vis_off(rows, units));
-    a.order = (int*)((char*)workspace + DkdvLayout::order_off(rows, units, (size_t)d.nb));
+    a.cls_items = (int4*)((char*)workspace + DkdvLayout::items_off(rows, units, (size_t)d.nb));
     a.parts = (float*)((char*)workspace + DkdvLayout::part_off(rows, units, (size_t)d.nb));
   }
   a.t_cap = d.t_cap; a.t_hist = d.t_hist; a.seg_len = d.seg_len;
@@ -928,14 +900,14 @@ hipError_t launch_attend_bwd(const Dims& d, bool bf16, const void* q, const void
   a.target_rounds = d.t_hist >= 3 * d.seg_len ? kTargetRoundsLongHistory : kTargetRoundsShortHistory;
   const int grid = xcd_grid(a.n_units);
   if (bf16) return d.D == 128 ? launch_bf16_g<128>(a, d.G, run) : launch_bf16_g<64>(a, d.G, run);
-  // fp32: dQ and dK/dV each in one kernel, no work list and no partial sums
+  // fp32: dQ and dK/dV each in one kernel, no work list and no partial sums (the
+  // class counts at the workspace start are not touched)
   hipError_t e = d.D == 128 ? run(0, attend_bwd_dq_f32_kernel<128>, dim3(grid), dim3(64 * d.G), a, d.G)
                             : run(0, attend_bwd_dq_f32_kernel<64>, dim3(grid), dim3(64 * d.G), a, d.G);
-  if (e == hipSuccess) e = run.skip(1);
   if (e == hipSuccess)
-    e = d.D == 128 ? run(2, attend_bwd_dkdv_f32_kernel<128>, dim3(grid), dim3(256), a, d.G)
-                   : run(2, attend_bwd_dkdv_f32_kernel<64>, dim3(grid), dim3(256), a, d.G);
-  if (e == hipSuccess) e = run.skip(3);
+    e = d.D == 128 ? run(1, attend_bwd_dkdv_f32_kernel<128>, dim3(grid), dim3(256), a, d.G)
+                   : run(1, attend_bwd_dkdv_f32_kernel<64>, dim3(grid), dim3(256), a, d.G);
+  if (e == hipSuccess) e = run.skip(2);
   return e;
 }
 

@@ -72,7 +72,8 @@ class HGALayerBuffers:
         self.dk = torch.empty(B, Hkv, S, d, dtype=dt, device=dev)
         self.dv = torch.empty(B, Hkv, S, d, dtype=dt, device=dev)
         ws = L.hga_attend_bwd_workspace_size(shape, t_hist, S)
-        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(ws, L.HGA_BWD_WORKSPACE_CLEAR_BYTES), dtype=torch.uint8, device=dev)
+        self.ws[:L.HGA_BWD_WORKSPACE_CLEAR_BYTES].zero_()     # every backward call leaves them zero
 
     def summaries(self, t_begin: int, t_end: int):
         L.hga_build_summaries(self.shape, self.k, self.t_cap, t_begin, t_end, self.gsum, self.csum)
@@ -330,8 +331,9 @@ class _HGAAttentionFn(torch.autograd.Function):
         dq = torch.empty_like(q)
         dk = torch.empty(B, cache.n_kv_heads, S, d, dtype=q.dtype, device=q.device)
         dv = torch.empty_like(dk)
-        ws = torch.empty(max(L.hga_attend_bwd_workspace_size(shape, t_hist, S), 16), dtype=torch.uint8,
-                         device=q.device)
+        ws = torch.empty(max(L.hga_attend_bwd_workspace_size(shape, t_hist, S), L.HGA_BWD_WORKSPACE_CLEAR_BYTES),
+                         dtype=torch.uint8, device=q.device)
+        ws[:L.HGA_BWD_WORKSPACE_CLEAR_BYTES].zero_()
         L.hga_attend_bwd(shape, q, k, v, o, lse, d_o.contiguous(), t_cap, t_hist, S, gidx, dq, dk, dv, ws)
         return dq, dk, dv, None, None, None, None, None
 

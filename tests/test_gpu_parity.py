@@ -214,7 +214,7 @@ def test_full_chain_and_determinism(chk, cases, name):
 @pytest.mark.parametrize("name", ["bf16_g4_d128_ragged", "f32_g4_d128"])
 def test_timed_backward_matches(chk, cases, name):
     """hga_attend_bwd_timed writes the same bits as hga_attend_bwd and records its
-    events in launch order (dQ, work list, dK/dV, partial sums)."""
+    events in launch order (dQ, dK/dV, partial sums)."""
     import sparse_long_context_hga_amd as hga
     w, _, _, _, gidx = cases[name]
     print(f"case {name}", flush=True)
@@ -239,7 +239,7 @@ def test_timed_backward_matches(chk, cases, name):
     marks = [start] + ev                 # every mark re-recorded after `start`, in launch order
     for e0, e1 in zip(marks, marks[1:]):
         assert e0.elapsed_time(e1) >= 0.0
-    assert ev[0].elapsed_time(ev[1]) > 0.0 and ev[4].elapsed_time(ev[5]) > 0.0
+    assert ev[0].elapsed_time(ev[1]) > 0.0 and ev[2].elapsed_time(ev[3]) > 0.0   # dQ and dK/dV ran
 
 
 def test_backward_workspace_reused_across_shapes(chk, cases):
@@ -260,6 +260,7 @@ def test_backward_workspace_reused_across_shapes(chk, cases):
     torch.cuda.synchronize()
     ref = {n: [chk.to_np(t).copy() for t in (L.dq, L.dk, L.dv)] for n, (L, _) in layers.items()}
     shared = torch.empty(need, dtype=torch.uint8, device="cuda")
+    shared[:hga.HGA_BWD_WORKSPACE_CLEAR_BYTES].zero_()   # cleared once: every call leaves it so
     for name in names:
         print(f"case {name} on the shared workspace", flush=True)
         L, g = layers[name]
