@@ -336,8 +336,8 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   // overlaps the dQ stores below.
   int pcls = -1;
   uint32_t pslot = 0;
-  if (do_plan && w == 0 && l < kMaxParts) {
-    pcls = item_cls[l];
+  if (do_plan && threadIdx.x < kMaxParts) {
+    pcls = item_cls[threadIdx.x];
     if (pcls >= 0)
       pslot = (uint32_t)__hip_atomic_fetch_add(a.cls_count + pcls, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -350,7 +350,7 @@ void attend_bwd_dq_bf16_kernel(BwdArgs a) {
   });
   const uint32_t cap = (uint32_t)a.n_units * kMaxParts;
   if (pcls >= 0 && pslot < cap)   // (always below cap when the counts started the call at zero)
-    a.cls_items[(int64_t)pcls * cap + pslot] = item_entry[l];
+    a.cls_items[(int64_t)pcls * cap + pslot] = item_entry[threadIdx.x];
 }
 
 // ---------------------------------------------------------------- dK/dV (bf16)
