@@ -243,9 +243,10 @@ def test_timed_backward_matches(chk, cases, name):
 
 
 def test_backward_workspace_reused_across_shapes(chk, cases):
-    """One workspace serves backward calls of different shapes in turn (everything in
-    it is written before it is read within a call): the results equal those of a
-    workspace of their own each time."""
+    """One workspace serves backward calls of different shapes in turn (its leading
+    counters are cleared once and every call leaves them at zero; everything else is
+    written before it is read within a call): the results equal those of a workspace
+    of their own each time."""
     import sparse_long_context_hga_amd as hga
     names = ["bf16_g8_full_coverage", "bf16_g4_d128_ragged", "bf16_g8_full_coverage"]
     layers = {}
@@ -271,3 +272,5 @@ def test_backward_workspace_reused_across_shapes(chk, cases):
         torch.cuda.synchronize()
         for a, b_ in zip(ref[name], (L.dq, L.dk, L.dv)):
             assert np.array_equal(a, chk.to_np(b_)), name
+        # the work items' class counts are back at zero for the next call
+        assert not shared[:hga.HGA_BWD_WORKSPACE_CLEAR_BYTES].any().item(), name
