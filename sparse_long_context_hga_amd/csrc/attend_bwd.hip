@@ -846,11 +846,10 @@ struct Launcher {
 // so no later kernel reads a workspace that an earlier one did not fill.
 template <int D, int G>
 hipError_t launch_bf16(const BwdArgs& a, const Launcher& run) {
-  // Query heads per dQ work-group.  With 4 per KV head, two work-groups of two heads
-  // per unit (each gathering the unit's tiles; the second copy mostly hits its XCD's
-  // L2) fit two to a compute unit, so one's start-up overlaps the other's tiles when
-  // there are more units than compute units.
-  constexpr int HPW = G >= 8 ? 4 : (G == 4 ? 2 : G);
+  // Query heads per dQ work-group.  With 4 or more per KV head, work-groups of two
+  // heads (each gathering the unit's tiles; the repeats mostly hit the XCD's L2) fit
+  // two to a compute unit, so one's start-up overlaps the other's tiles.
+  constexpr int HPW = G >= 4 ? 2 : G;
   hipError_t e = run(0, attend_bwd_dq_bf16_kernel<D, G, HPW>, dim3(xcd_grid(a.n_units * (G / HPW))),
                      dim3(128 * HPW), a);
   if (e == hipSuccess) e = run(1, attend_bwd_dkdv_bf16_kernel<D, G>, dim3(a.n_units * kMaxParts), dim3(256), a);
