@@ -9,9 +9,10 @@
 // bf16 path, one work-group per (sequence, KV head, query block), 2G waves of
 // 32 query rows each (the G query heads of the KV head share every gathered
 // tile: GQA-aware, one gather per KV head):
-//   * key tiles of 64 tokens = 8 selected groups (each group is one contiguous
-//     2 KiB run of K and of V in HBM), then the own chunk; two buffer sets in
-//     swizzled LDS, the next tile's copies in flight during the MFMAs;
+//   * key tiles of 64 tokens: the own chunk first (its own buffer set), then 8
+//     selected groups per tile (each group is one contiguous 2 KiB run of K and of
+//     V in HBM) through two buffer sets in swizzled LDS, the next tile's copies in
+//     flight during the MFMAs;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys in rho order, B = the
 //     wave's 32 query rows held in registers): each lane ends with one query row
 //     and 32 of the 64 keys, so the online-softmax statistics live in the lane;
