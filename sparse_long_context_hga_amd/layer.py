@@ -205,7 +205,8 @@ class HGAHostKVCache:
         self._gs_seg = torch.zeros(batch, n_kv_heads, self.stage_cap // 8, head_dim, dtype=dtype, device=device)
         self._cs_seg = torch.zeros(batch, n_kv_heads, self.stage_cap // 64, head_dim, dtype=dtype, device=device)
         self.length = 0
-        self.q_last = None
+        self.q_last: Optional[torch.Tensor] = None      # [B, Hq, 64, d] of the committed history
+        self._q_pending: Optional[torch.Tensor] = None
         self.k = self.k_stage        # the device tensor the segment's checks compare devices with
 
     def write(self, k_seg: torch.Tensor, v_seg: torch.Tensor, shape: L.HgaShape) -> int:
@@ -234,7 +235,8 @@ class HGAHostKVCache:
         return gst
 
     def keep_last_query_block(self, q: torch.Tensor):
-        pass
+        """Remember the written segment's last 64 query rows (taken over by commit)."""
+        self._q_pending = q[:, :, -64:].detach().contiguous().clone()
 
     def commit(self, seg_len: int):
         """The segment becomes history: its K/V go to host memory."""
@@ -242,6 +244,7 @@ class HGAHostKVCache:
         self.k_host[:, :, t0:t0 + seg_len].copy_(self.k_stage[:, :, sh:sh + seg_len])
         self.v_host[:, :, t0:t0 + seg_len].copy_(self.v_stage[:, :, sh:sh + seg_len])
         self.length += seg_len
+        self.q_last, self._q_pending = self._q_pending, None
 
 
 def _check_segment(q: torch.Tensor, k_seg: torch.Tensor, v_seg: torch.Tensor, cache: "HGAKVCache"):
@@ -288,15 +291,18 @@ class _HGAAttentionFn(torch.autograd.Function):
         o = torch.empty_like(q)
         lse = torch.empty(B, Hq, S, dtype=torch.float32, device=q.device)
         if isinstance(cache, HGAHostKVCache):
-            # host-RAM tier: route over the tables in HBM, stage the selected history
-            # groups, attend on the staging cache
-            if causal_routing:
-                raise ValueError("the host-RAM tier routes blocks by their own rows")
+            # host-RAM tier: route over the tables in HBM (block j by its own rows, or
+            # strictly causally by block j-1's), stage the selected history groups,
+            # attend on the staging cache
             if Hq != cache.n_q_heads or top_groups > cache.top_groups:
                 raise ValueError(f"this host-tier cache was sized for {cache.n_q_heads} query heads and at most "
                                  f"{cache.top_groups} groups per block, got {Hq} and {top_groups}")
             t_hist = cache.write(k_seg, v_seg, shape)
-            L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
+            if causal_routing:
+                L.hga_route_causal(shape, q, cache.q_last if t_hist > 0 else None, cache.csum, cache.gsum,
+                                   cache.t_cap, t_hist, S, cidx, gidx)
+            else:
+                L.hga_route(shape, q, cache.csum, cache.gsum, cache.t_cap, t_hist, S, cidx, gidx)
             gst = cache.stage(shape, t_hist, gidx)
             L.hga_attend_fwd(shape, q, cache.k_stage, cache.v_stage, cache.stage_cap, cache.stage_hist, S, gst, o,
                              lse)
@@ -304,6 +310,7 @@ class _HGAAttentionFn(torch.autograd.Function):
             ctx.cache, ctx.shape = cache, shape
             ctx.kv = (cache.k_stage, cache.v_stage, cache.stage_cap, cache.stage_hist)
             ctx.mark_non_differentiable(lse, gidx)
+            cache.keep_last_query_block(q)
             return o, lse, gidx
         if causal_routing:
             # summaries of the segment, causal routing and attention in one call

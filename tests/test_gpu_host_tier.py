@@ -9,7 +9,8 @@ segment a staging cache in HBM holding only the selected history groups.
   * the autograd op over consecutive segments with a host-tier cache gives, bit
     for bit, the outputs, selections and gradients of the same op with the whole
     history in HBM (whose parity with the oracle the other tests establish): one
-    case whose staging area holds the whole history, one where it is far smaller.
+    case whose staging area holds the whole history, one where it is far smaller,
+    each with block and with strictly causal routing.
 """
 import numpy as np
 import pytest
@@ -145,8 +146,11 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["block", "causal"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_host_tier_equals_hbm_history(hga, name):
+def test_host_tier_equals_hbm_history(hga, name, causal):
+    """Every segment's outputs, selection and gradients are bit-identical with the
+    history in host memory and in HBM, with block and with strictly causal routing."""
     from sparse_long_context_hga_amd.layer import HGAHostKVCache, HGAKVCache, hga_attention
     c = CASES[name]
     B, Hq, Hkv, d, S, n_seg = c["batch"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"], c["seg_len"], c["n_seg"]
@@ -154,7 +158,8 @@ def test_host_tier_equals_hbm_history(hga, name):
     T = S * n_seg
     dev_cache = HGAKVCache(B, Hkv, d, T, torch.bfloat16)
     host_cache = HGAHostKVCache(B, Hkv, d, T, S, Hq, kc, kg, torch.bfloat16)
-    print(f"case {name}: staging area {host_cache.stage_hist} tokens for up to {T - S} history tokens", flush=True)
+    print(f"case {name} ({'causal' if causal else 'block'} routing): staging area {host_cache.stage_hist} tokens "
+          f"for up to {T - S} history tokens", flush=True)
     for s in range(n_seg):
         w = hi.random_layer(seed=400 + s, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, t_hist=0, seg_len=S,
                             top_chunks=kc, top_groups=kg, chunk_mean_var=0.5)
@@ -162,7 +167,7 @@ def test_host_tier_equals_hbm_history(hga, name):
         for cache in (dev_cache, host_cache):
             xs = [torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16).requires_grad_(True)
                   for a in (w.q, w.k_cache[:, :, :S], w.v_cache[:, :, :S])]
-            o, lse, gidx = hga_attention(*xs, cache, kc, kg)
+            o, lse, gidx = hga_attention(*xs, cache, kc, kg, causal_routing=causal)
             (o.float() * torch.from_numpy(w.d_o).cuda()).sum().backward()
             cache.commit(S)
             res.append([o.detach(), lse, gidx] + [x.grad for x in xs])
