@@ -377,11 +377,15 @@ class HGAStack:
     loss_fn(h_last).backward(); then every cache commits the segment, whose K/V
     become detached history for the next segment (no gradient ever reaches them).
     budgets: one (top_chunks, top_groups) pair for every layer, or a list of them.
+    host_history: keep every layer's detached history in pinned host memory
+    (HGAHostKVCache; needs seg_len, the fixed segment length, and n_q_heads);
+    results are bit-identical to the all-HBM caches.
     """
 
     def __init__(self, layers, batch: int, n_kv_heads: int, head_dim: int, t_cap: int, budgets=(16, 64),
                  dtype: torch.dtype = torch.bfloat16, device="cuda", softmax_scale: Optional[float] = None,
-                 causal_routing: bool = False):
+                 causal_routing: bool = False, host_history: bool = False, seg_len: Optional[int] = None,
+                 n_q_heads: Optional[int] = None):
         self.layers = list(layers)
         n = len(self.layers)
         if isinstance(budgets[0], (tuple, list)):
@@ -390,7 +394,13 @@ class HGAStack:
             self.budgets = [tuple(b) for b in budgets]
         else:
             self.budgets = [tuple(budgets)] * n
-        self.caches = [HGAKVCache(batch, n_kv_heads, head_dim, t_cap, dtype, device) for _ in range(n)]
+        if host_history:
+            if seg_len is None or n_q_heads is None:
+                raise ValueError("a host-memory history needs seg_len and n_q_heads (they size its staging cache)")
+            self.caches = [HGAHostKVCache(batch, n_kv_heads, head_dim, t_cap, seg_len, n_q_heads, kc, kg, dtype,
+                                          device) for kc, kg in self.budgets]
+        else:
+            self.caches = [HGAKVCache(batch, n_kv_heads, head_dim, t_cap, dtype, device) for _ in range(n)]
         self.softmax_scale = softmax_scale
         self.causal_routing = causal_routing
         self.segments = 0

@@ -12,7 +12,8 @@ o1, and the oracle's fp64 layer 2 is comparable); the loss is sum(o2 * T) with a
 seeded T.  Compared per segment: layer 1's selection (exact) and O / LSE of both
 layers; the gradients of the segment's q, k, v (whole tensors and per 64-row
 block / chunk).  Every earlier segment's tensors must receive no gradient from
-later segments.
+later segments.  The same stack with the history in host memory (both routing
+modes) must match the all-HBM stack bit for bit.
 """
 import numpy as np
 import pytest
@@ -151,3 +152,28 @@ def test_two_layer_stack_over_three_segments(chk):
             e, eb = _rel(got, want), _block_max(got, want)
             print(f"segment {s}: {name} rel-L2 {e:.3e}, worst 64-row block {eb:.3e}", flush=True)
             assert e <= chk.TOL_GRAD_REL_L2 and eb <= chk.TOL_GRAD_REL_L2, (s, name, e, eb)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["block", "causal"])
+def test_stack_with_host_history_equals_hbm(chk, causal):
+    """The same stack with every layer's history in pinned host memory: per segment,
+    both layers' outputs, LSE and selections and the gradients of the segment's
+    inputs are bit-identical to the all-HBM stack, with block and with strictly
+    causal routing."""
+    from sparse_long_context_hga_amd.layer import HGAStack
+    stacks = [HGAStack([_Layer1(), _Layer2()], batch=B, n_kv_heads=HKV, head_dim=D, t_cap=T,
+                       budgets=[BUDGET1, BUDGET2], softmax_scale=SCALE, causal_routing=causal,
+                       host_history=host, seg_len=S, n_q_heads=HQ) for host in (False, True)]
+    for s in range(N_SEG):
+        q, k, v, tgt = _segment_inputs(s)
+        print(f"segment {s} ({'causal' if causal else 'block'} routing)", flush=True)
+        t_dev = chk.to_dev(tgt, "f32")
+        res = []
+        for stack in stacks:
+            x = tuple(chk.to_dev(a, "bf16").requires_grad_(True) for a in (q, k, v))
+            _, outs = stack.run_segment(x, lambda o2: (o2.float() * t_dev).sum())
+            res.append([t for layer in outs for t in layer] + [t.grad for t in x])
+        torch.cuda.synchronize()
+        names = ["o1", "lse1", "gidx1", "o2", "lse2", "gidx2", "dq", "dk", "dv"]
+        for name, a, b_ in zip(names, *res):
+            assert torch.equal(a, b_), f"segment {s}: {name} differs between host and HBM history"
