@@ -178,18 +178,30 @@ struct TopkShared {
   int nsel;
 };
 
-// Lanes n' < n of the calling wave: the candidates fin[0 .. n) (distinct, any order)
-// to out / out_keys (nullable) in ascending index order; a candidate's slot is the
-// number of selected candidates with a lower index.
+// Lanes n' < n of the calling wave: the candidates fin[0 .. n) (distinct chunk
+// indices below kMaxChunks, any order) to out / out_keys (nullable) in ascending
+// index order.  A candidate's slot is the number of candidates with a lower index,
+// counted over the index bits with ballots, most significant first: at each bit, a
+// lane whose bit is set adds the lanes that agree with it on the higher bits and
+// have the bit clear.
+constexpr int kIndexBits = 13;
+static_assert(kMaxChunks <= (1 << kIndexBits), "chunk indices fit the counted bits");
 __device__ __forceinline__ void sort_by_index(const uint64_t* fin, int n, int* out, uint32_t* out_keys) {
   const int lane = threadIdx.x & 63;
-  if (lane < n) {
-    const uint64_t x = fin[lane];
-    const int idx = cand_index(x);
-    int rank = 0;
+  const bool valid = lane < n;
+  const uint64_t x = valid ? fin[lane] : 0ull;
+  const uint32_t idx = valid ? (uint32_t)cand_index(x) : 0u;
+  uint64_t same = __builtin_amdgcn_ballot_w64(valid);   // lanes agreeing with this one on the bits above b
+  int rank = 0;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) rank += j < n && cand_index(fin[j]) < idx;
-    out[rank] = idx;
+  for (int b = kIndexBits - 1; b >= 0; --b) {
+    const bool one = (idx >> b) & 1u;
+    const uint64_t ones = __builtin_amdgcn_ballot_w64(valid && one);
+    if (one) rank += __builtin_popcountll(same & ~ones);
+    same &= one ? ones : ~ones;
+  }
+  if (valid) {
+    out[rank] = (int)idx;
     if (out_keys) out_keys[rank] = (uint32_t)(x >> 32);
   }
 }
